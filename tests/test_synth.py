@@ -1,0 +1,94 @@
+"""Seeded synthetic inputs: determinism, chunk independence, shapes and structure."""
+import math
+
+import numpy as np
+import pytest
+
+from kronecker_factored_transforms_amd import synth as S
+
+
+def test_workload_shapes():
+    shapes = {k: (w.T, w.n1, w.n2, w.dtype) for k, w in S.WORKLOADS.items()}
+    assert shapes["tiny_fp32_n64"] == (16, 8, 8, "fp32")
+    assert shapes["attn_n4096"] == (2048, 64, 64, "bf16")
+    assert shapes["hidden_n8192"] == (16384, 64, 128, "bf16")
+    assert shapes["down_proj_n14336"] == (8192, 112, 128, "bf16")
+    assert shapes["decode_n8192_t64"] == (64, 64, 128, "bf16")
+    assert shapes["prefill_n8192_t65536"] == (65536, 64, 128, "bf16")
+
+
+def test_same_seed_same_bytes_and_token_subsets_agree():
+    a = S.make("attn_n4096", T=300)
+    b = S.make("attn_n4096", T=300)
+    assert S.sha256(a.X) == S.sha256(b.X) and S.sha256(a.P1) == S.sha256(b.P1)
+    ids = np.array([299, 0, 257, 5])
+    sub = S.make("attn_n4096", token_ids=ids)
+    assert np.array_equal(sub.X, a.X[ids])
+    c = S.make("attn_n4096", seed=1, T=300)
+    assert S.sha256(c.X) != S.sha256(a.X)
+
+
+def test_decode_is_a_prefix_of_the_prefill_stream():
+    d = S.make("decode_n8192_t64")
+    p = S.make("prefill_n8192_t65536", token_ids=np.arange(64))
+    assert np.array_equal(d.X, p.X)
+    assert np.array_equal(d.P1, p.P1) and np.array_equal(d.P2, p.P2)
+
+
+def test_tiny_case_structure():
+    inp = S.make("tiny_fp32_n64")
+    assert inp.X.dtype == np.float32 and inp.X.shape == (16, 64)
+    assert inp.c is None and inp.alpha == math.inf
+    sd = inp.X.std(axis=0)
+    assert sd[3] > 5 and sd[40] > 5 and np.median(sd) < 2
+    for P in (inp.P1, inp.P2):
+        P = P.astype(np.float64)
+        assert np.max(np.abs(P.T @ P - np.eye(8))) < 1e-6
+
+
+def test_attention_case_structure():
+    inp = S.make("attn_n4096", T=512)
+    wl = inp.wl
+    x = S.bf16_bits_to_f32(inp.X).astype(np.float64)
+    outl, piv = S.outlier_channels(wl)
+    assert len(outl) == 4 and len(piv) == 2
+    sd = x[1:].std(axis=0)
+    assert np.all(sd[outl] > 20) and np.median(sd) < 1.5
+    assert np.all(np.abs(x[0, piv]) >= 0) and np.max(np.abs(x[0, piv])) > 20
+    assert inp.c.dtype == np.float32 and inp.c.min() >= 0.5 and inp.c.max() <= 2.0
+    assert np.float32(inp.alpha) == inp.alpha and 0 < inp.alpha < 5
+    P1 = S.bf16_bits_to_f32(inp.P1).astype(np.float64)
+    assert np.max(np.abs(P1 - np.eye(64))) < 0.1
+
+
+def test_hidden_case_structure():
+    inp = S.make("hidden_n8192", T=256)
+    x = S.bf16_bits_to_f32(inp.X).astype(np.float64)
+    outl, _ = S.outlier_channels(inp.wl)
+    assert len(outl) == 8
+    assert np.all(np.median(np.abs(x[:, outl]), 0) > 10)
+    P1 = S.bf16_bits_to_f32(inp.P1).astype(np.float64)
+    P2 = S.bf16_bits_to_f32(inp.P2).astype(np.float64)
+    assert np.max(np.abs(P1.T @ P1 - np.eye(64))) < 0.02
+    assert np.max(np.abs(P2.T @ P2 - np.eye(128))) < 0.02
+    assert inp.c is None and inp.alpha == 3.0
+
+
+def test_down_proj_case_structure():
+    inp = S.make("down_proj_n14336", T=256)
+    assert inp.X.shape == (256, 14336)
+    x = S.bf16_bits_to_f32(inp.X).astype(np.float64)
+    assert abs(x.mean()) < 0.05 and 0.3 < x.std() < 1.0
+    assert inp.c.min() >= 0.25 and inp.c.max() <= 4.0
+
+
+def test_bf16_rounding_is_nearest_even():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20])
+    got = S.bf16_bits_to_f32(S.to_bf16_bits(vals))
+    assert got.tolist() == [1.0, 1.0, 1.0 + 2 ** -6, -1.0, 1.0 + 2 ** -7]
+
+
+def test_signed_permutation_helper():
+    P = S.signed_permutation(16, np.random.default_rng(0))
+    assert np.array_equal(np.abs(P).sum(0), np.ones(16)) and np.array_equal(np.abs(P).sum(1), np.ones(16))
+    assert np.allclose(P.T @ P, np.eye(16))
