@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused Kronecker-factored transform + per-token INT4 quantization.
+
+One step = one kq_transform_quant over one batch of synthetic tokens already resident in
+HBM (the whole hot path: load, optional channel scale, both contractions, absmax, clip,
+round, clamp, pack, store). Default workload: hidden size 8192 with factors 64 x 128,
+16384 bf16 tokens (Student-t activations with outlier channels, orthogonal factors,
+clip logit 3).
+
+Prints ONE JSON line on stdout. Algorithmic work per token: 2*n*(n1+n2) FLOP and
+2.5*n bytes (bf16 in + packed int4 out; 4.5*n for fp32 input). The per-launch kernel
+time comes from HIP events recorded on the launch stream around every timed launch.
+Input/output buffer sets are rotated so that consecutive steps never hit data left in
+the 256 MB last-level (Infinity) cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in ("kq_fused.hip", "kq_generic.hip"):
+        with open(os.path.join(ROOT, "kronecker_factored_transforms_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    there is none for this workload/kernel or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_sha and m_b) or m_sha.group(1) != kernel_source_sha256():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(inp, seconds: float):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload's tokens."""
+    import numpy as np
+    from oracle import kq_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:  # pragma: no cover
+        blas = []
+
+    def run(X):
+        Y = O.transform(X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
+        q, s = O.quantize_per_token(Y.astype(np.float32), O.clip_ratio(inp.alpha), inp.wl.scale_dtype)
+        return O.pack_int4(q), s
+
+    T = inp.X.shape[0]
+    k = min(T, 64)
+    run(inp.X[:k])  # warm
+    t0 = time.perf_counter()
+    run(inp.X[:k])
+    dt = max(time.perf_counter() - t0, 1e-6)
+    k = int(min(T, max(k, seconds / dt * k)))
+    w0, c0 = time.perf_counter(), os.times()
+    run(inp.X[:k])
+    w1, c1 = time.perf_counter(), os.times()
+    wall = w1 - w0
+    cpu = (c1.user - c0.user) + (c1.system - c0.system)
+    return {
+        "value": k / wall,
+        "unit": "tokens/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": (f"first {k} of {T} tokens of the same workload; float64 factored transform "
+                   f"(numpy.matmul) + fp32 quantizer + packing, one pass, {wall:.1f} s wall, "
+                   f"{cpu:.1f} s CPU; BLAS {blas}; host cpu_count {os.cpu_count()}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="hidden_n8192")
+    ap.add_argument("--rotate-mib", type=int, default=1536,
+                    help="minimum total size of the rotated input+output buffer sets")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}). Tokens are independent, "
+              f"so N GPUs would each run the same kernel on T/N tokens with no communication.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kronecker_factored_transforms_amd import binding as B
+    from kronecker_factored_transforms_amd import synth as S
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    wl = S.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = S.make(wl)
+    log(f"[bench] generated {wl.name}: T={wl.T} n={wl.n} ({wl.n1}x{wl.n2}) {wl.dtype} "
+        f"in {time.perf_counter() - t_gen:.1f}s")
+
+    def dev_tensor(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    X0 = dev_tensor(inp.X)
+    c = torch.from_numpy(inp.c).to(dev) if inp.c is not None else None
+    plan = B.Plan(dev_tensor(inp.P1), dev_tensor(inp.P2), c, inp.alpha, wl.scale_dtype)
+    T, n = wl.T, wl.n
+    esize = 2 if wl.dtype == "bf16" else 4
+    set_bytes = T * n * esize + T * n // 2 + T * 2
+    nsets = max(2, math.ceil(args.rotate_mib * 2 ** 20 / set_bytes))
+    Xs = [X0] + [X0.clone() for _ in range(nsets - 1)]
+    outs = [(torch.empty((T, n // 2), dtype=torch.uint8, device=dev),
+             torch.empty((T,), dtype=plan.scale_dtype, device=dev)) for _ in range(nsets)]
+    stream = torch.cuda.current_stream()
+    handle, sh = plan.handle, int(stream.cuda_stream)
+    log(f"[bench] kernel={plan.kernel} clip={plan.clip:.6f} buffer sets={nsets} "
+        f"({nsets * set_bytes / 2**20:.0f} MiB)")
+
+    if args.copy_probe:
+        a = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: 3 x 512 MiB device-to-device copies")
+
+    def step(i):
+        X = Xs[i % nsets]
+        codes, scales = outs[i % nsets]
+        B.kq_transform_quant(handle, X, T, n, codes, scales, None, sh)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = (t1 - t0) * 1e3 / K
+    k_avg_s = sum(kernel_ms) / K / 1e3
+    k_med_ms = sorted(kernel_ms)[K // 2]
+
+    flop_tok = 2 * n * (wl.n1 + wl.n2)
+    byte_tok = (esize + 0.5) * n
+    tokens_per_s = T / (ms_per_step / 1e3)
+    achieved_gbs = T * byte_tok / k_avg_s / 1e9
+    achieved_tflops = T * flop_tok / k_avg_s / 1e12
+    traffic = traffic_from_profile(wl.name, plan.kernel)
+    log(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step wall, kernel avg "
+        f"{k_avg_s * 1e6:.2f} us (median {k_med_ms * 1e3:.2f} us): {achieved_gbs:.0f} GB/s, "
+        f"{achieved_tflops:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} cores")
+
+    out = {
+        "metric": "tokens/s + % of roofline (HBM GB/s or MFMA TFLOP/s), n=8192 64x128 transform+INT4",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "T": T, "n": n, "n1": wl.n1, "n2": wl.n2, "x_dtype": wl.dtype,
+            "scale_dtype": wl.scale_dtype, "per_channel_c": inp.c is not None,
+            "alpha": inp.alpha, "kernel": plan.kernel, "buffer_sets": nsets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "kernel_avg_us": k_avg_s * 1e6,
+            "algorithmic_bytes_per_launch": T * byte_tok,
+        },
+        "mfma": {
+            "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved_tflops / PEAK_BF16_TFLOPS,
+            "algorithmic_flop_per_launch": T * flop_tok,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * kq.h -- C ABI of libkq: fused Kronecker-factored activation transform + per-token
+ * symmetric INT4 quantization on AMD Instinct MI355X (gfx950).
+ *
+ * What one call computes, per token t (x_t = row t of X, n = n1*n2):
+ *   1. x^_t = x_t * c                       (optional per-channel scale)
+ *   2. V_t[i][k] = x^_t[i*n2 + k]           (row-major n1 x n2 view)
+ *   3. Y_t = P1^T V_t P2  ==  x^_t (P1 (x) P2)
+ *   4. a_t = max |Y_t|;  s32 = fp32(fp32(clip * a_t) / 7);  s_t = fp16_rne(s32) (or s32)
+ *   5. q = clamp(rint(fp32(y * fp32(1/s_t))), -8, 7); s_t == 0 -> q = 0
+ *   6. codes: element 2m in the low nibble of byte m, 2m+1 in the high nibble,
+ *      4-bit two's complement, row-major Y order (index j*n2 + l).
+ * Sources (web pages): "Kronecker Product" -- Definition (entry formula of A (x) B) and
+ * Why It Matters for LLM Quantization (vec(V)(P1 (x) P2) = vec(P1^T V P2)); "FlatQuant:
+ * Fast Learnable Affine Quantization" -- Symbol Map (X~ as k x n1 x n2, diag(c),
+ * sigmoid-mapped clip alpha_a, Q(.) with step s), Deep Dive: Kronecker factorization
+ * (P1^T x1 X~ x2 P2), Per-channel scaling and learnable clipping (c before the
+ * transform, clip after it), The fused kernel / Figure 8a (P1, P2 resident on chip,
+ * only the quantized tile written), Putting It Together step 3; "High-Rate Quantized
+ * Matrix Multiplication I" -- absmax INT scaling.
+ *
+ * Conventions common to all calls
+ *   - Device pointers are HIP device addresses on the current device. The library
+ *     never frees caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *   - Every entry point returns a kq_status; nothing is thrown or printed across the
+ *     ABI. Argument errors are detected before anything is enqueued.
+ *   - A plan is immutable after kq_create: calls on one plan from several host threads
+ *     or streams are safe.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kq_plan kq_plan;
+
+typedef enum kq_status {
+  KQ_OK = 0,
+  KQ_ERR_INVALID_ARG = 1,   /* bad size, NULL pointer, NaN alpha, ...          */
+  KQ_ERR_UNSUPPORTED = 2,   /* valid, but this build has no kernel for it     */
+  KQ_ERR_ALIGNMENT = 3,     /* a pointer or leading dimension is misaligned   */
+  KQ_ERR_OUT_OF_MEMORY = 4, /* host or device allocation failed (kq_create)   */
+  KQ_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed      */
+} kq_status;
+
+typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
+
+/* Flags for kq_create_ex. */
+#define KQ_FLAG_FORCE_GENERIC 0x1u /* use the fp32 FMA kernel even where the MFMA one applies */
+
+/*
+ * kq_choose_factors -- factor a hidden size for the Kronecker transform.
+ * Picks n1 <= n2 with n1*n2 == n minimising n1 + n2 ("FlatQuant" page, Deep Dive:
+ * Kronecker factorization: the factor sizes minimise n1 + n2, e.g. 8192 -> (64, 128)).
+ * n >= 1; writes *n1, *n2. Returns KQ_ERR_INVALID_ARG for n < 1 or NULL outputs.
+ */
+kq_status kq_choose_factors(int64_t n, int *n1, int *n2);
+
+/*
+ * kq_create -- build an immutable plan for one (P1, P2, c, alpha) set.
+ *   out          receives the plan (set to NULL on error).
+ *   n1, n2       factor sizes, n = n1*n2 must be even. n1, n2 >= 1.
+ *   x_dtype      dtype of X, P1 and P2: KQ_BF16 or KQ_FP32 (P has the dtype of X).
+ *   scale_dtype  KQ_FP16 (default in the bindings) or KQ_FP32 for the per-token scale.
+ *   P1           device, n1 x n1 row-major, x_dtype ("left" factor, enters transposed).
+ *   P2           device, n2 x n2 row-major, x_dtype.
+ *   c            device, n fp32 per-channel scale applied before the transform, or NULL
+ *                (all ones).
+ *   alpha        clip logit; clip = fp32(1 / (1 + exp(-alpha))) in double on the host.
+ *                +INFINITY gives clip 1, -INFINITY gives clip 0. NaN -> INVALID_ARG.
+ *   stream       stream used for the set-up copies. kq_create synchronizes it.
+ * The plan owns device copies of P1, P2 (re-laid-out for the kernels) and c; the caller
+ * may free its buffers when kq_create returns. Not a hot-path call: it allocates.
+ * Errors: INVALID_ARG (sizes, NULLs, dtypes, NaN alpha), OUT_OF_MEMORY, HIP.
+ */
+kq_status kq_create(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype scale_dtype,
+                    const void *P1, const void *P2, const float *c, float alpha,
+                    void *stream);
+
+/* kq_create with flags (KQ_FLAG_*); kq_create(...) == kq_create_ex(..., 0). */
+kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
+                       kq_dtype scale_dtype, const void *P1, const void *P2,
+                       const float *c, float alpha, void *stream, unsigned flags);
+
+/*
+ * kq_transform_quant -- the hot path: transform + quantize T tokens, enqueued on
+ * `stream`, asynchronous. No allocation, no synchronization, no host<->device copy.
+ *   plan     from kq_create.
+ *   X        device, T rows of n elements of the plan's x_dtype; row t starts at
+ *            X + t*ldx elements. 16-byte aligned; ldx >= n and ldx*sizeof(elem) a
+ *            multiple of 16 bytes (else KQ_ERR_ALIGNMENT).
+ *   T        number of tokens, >= 0. T == 0 returns KQ_OK and launches nothing.
+ *   ldx      leading dimension of X in elements.
+ *   codes    device, T x (n/2) bytes, row stride n/2, 4-byte aligned (written).
+ *   scales   device, T scales of the plan's scale_dtype (written).
+ *   y_debug  device, T x n fp32, or NULL. When given, receives the exact fp32 Y that
+ *            was quantized (for verification; adds 4n bytes of writes per token).
+ * Caller owns X, codes, scales and y_debug. Outputs are written in full for every
+ * token; inputs are not modified. Non-finite inputs give unspecified codes.
+ * Errors: INVALID_ARG (NULL plan/pointers with T > 0, T < 0, ldx < n), ALIGNMENT,
+ * HIP (launch failure; checked with hipGetLastError right after the launch).
+ */
+kq_status kq_transform_quant(const kq_plan *plan, const void *X, int64_t T, int64_t ldx,
+                             uint8_t *codes, void *scales, float *y_debug, void *stream);
+
+/* Free a plan and its device buffers. NULL is a no-op (returns KQ_OK). The caller must
+ * make sure no enqueued kq_transform_quant on this plan is still running. */
+kq_status kq_destroy(kq_plan *plan);
+
+/* The exact fp32 clip ratio the kernels use (0 for a NULL plan). */
+float kq_plan_clip_ratio(const kq_plan *plan);
+
+/* Name of the kernel variant the plan dispatches to (static string; "" for NULL). */
+const char *kq_plan_kernel_name(const kq_plan *plan);
+
+/* Static, human-readable description of a status code. */
+const char *kq_status_string(kq_status s);
+
+/* ABI version of this header (major * 10000 + minor * 100 + patch). */
+int kq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

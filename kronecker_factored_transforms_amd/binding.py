@@ -1,0 +1,193 @@
+"""ctypes binding of libkq: the C ABI of include/kq.h under the same names.
+
+Argument marshalling only: tensors are turned into device pointers, sizes and the HIP
+stream handle; every step of the transform and the quantizer runs in the HIP kernels.
+There is no CPU fallback: if libkq.so is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkq.so")
+
+KQ_OK, KQ_ERR_INVALID_ARG, KQ_ERR_UNSUPPORTED, KQ_ERR_ALIGNMENT, KQ_ERR_OUT_OF_MEMORY, KQ_ERR_HIP = range(6)
+KQ_BF16, KQ_FP32, KQ_FP16 = 0, 1, 2
+KQ_FLAG_FORCE_GENERIC = 0x1
+
+# every symbol declared in include/kq.h
+EXPORTS = (
+    "kq_choose_factors", "kq_create", "kq_create_ex", "kq_transform_quant", "kq_destroy",
+    "kq_plan_clip_ratio", "kq_plan_kernel_name", "kq_status_string", "kq_version",
+)
+
+_lib = None
+
+
+class KqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {kq_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkq.so (built in-tree by kronecker_factored_transforms_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m kronecker_factored_transforms_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint
+    L.kq_choose_factors.argtypes = [i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.kq_choose_factors.restype = i32
+    L.kq_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32, i32, vp, vp, vp, ctypes.c_float, vp]
+    L.kq_create.restype = i32
+    L.kq_create_ex.argtypes = [ctypes.POINTER(vp), i32, i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, u32]
+    L.kq_create_ex.restype = i32
+    L.kq_transform_quant.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
+    L.kq_transform_quant.restype = i32
+    L.kq_destroy.argtypes = [vp]
+    L.kq_destroy.restype = i32
+    L.kq_plan_clip_ratio.argtypes = [vp]
+    L.kq_plan_clip_ratio.restype = ctypes.c_float
+    L.kq_plan_kernel_name.argtypes = [vp]
+    L.kq_plan_kernel_name.restype = ctypes.c_char_p
+    L.kq_status_string.argtypes = [i32]
+    L.kq_status_string.restype = ctypes.c_char_p
+    L.kq_version.argtypes = []
+    L.kq_version.restype = i32
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------------------------------
+def _ptr(x) -> int | None:
+    """Device pointer of a tensor, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream) or None
+    if isinstance(stream, int):
+        return stream or None
+    return int(stream.cuda_stream) or None
+
+
+def _dtype_code(d) -> int:
+    if isinstance(d, int):
+        return d
+    s = str(d).replace("torch.", "")
+    return {"bf16": KQ_BF16, "bfloat16": KQ_BF16, "fp32": KQ_FP32, "float32": KQ_FP32,
+            "fp16": KQ_FP16, "float16": KQ_FP16}[s]
+
+
+def _check(st: int, what: str):
+    if st != KQ_OK:
+        raise KqError(st, what)
+
+
+def kq_status_string(status: int) -> str:
+    return lib().kq_status_string(int(status)).decode()
+
+
+def kq_version() -> int:
+    return int(lib().kq_version())
+
+
+def kq_choose_factors(n: int) -> tuple[int, int]:
+    a, b = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().kq_choose_factors(int(n), ctypes.byref(a), ctypes.byref(b)), "kq_choose_factors")
+    return a.value, b.value
+
+
+def kq_create(n1, n2, x_dtype, scale_dtype, P1, P2, c=None, alpha=math.inf, stream=None, flags=0):
+    """Returns an opaque plan handle (int). P1, P2, c are device tensors (or addresses)."""
+    h = ctypes.c_void_p(0)
+    st = lib().kq_create_ex(ctypes.byref(h), int(n1), int(n2), _dtype_code(x_dtype),
+                            _dtype_code(scale_dtype), _ptr(P1), _ptr(P2), _ptr(c),
+                            ctypes.c_float(alpha), _stream(stream), int(flags))
+    _check(st, "kq_create")
+    return h.value
+
+
+def kq_transform_quant(plan, X, T, ldx, codes, scales, y_debug=None, stream=None) -> None:
+    st = lib().kq_transform_quant(plan, _ptr(X), int(T), int(ldx), _ptr(codes), _ptr(scales),
+                                  _ptr(y_debug), _stream(stream))
+    _check(st, "kq_transform_quant")
+
+
+def kq_destroy(plan) -> None:
+    _check(lib().kq_destroy(plan), "kq_destroy")
+
+
+def kq_plan_clip_ratio(plan) -> float:
+    return float(lib().kq_plan_clip_ratio(plan))
+
+
+def kq_plan_kernel_name(plan) -> str:
+    return lib().kq_plan_kernel_name(plan).decode()
+
+
+# ------------------------------------------------------------------------------------
+class Plan:
+    """Convenience wrapper: Plan(P1, P2, c, alpha)(X) -> (codes, scales[, y]).
+
+    X is a [T, n] cuda tensor (bfloat16 or float32, last dim contiguous); P1/P2 have X's
+    dtype; c is float32 [n] or None. Outputs are allocated with torch on X's device.
+    """
+
+    def __init__(self, P1, P2, c=None, alpha=math.inf, scale_dtype="fp16", stream=None, flags=0):
+        import torch
+        if P1.dtype != P2.dtype or P1.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("P1 and P2 must both be bfloat16 or both float32")
+        if not (P1.is_cuda and P2.is_cuda) or (c is not None and not c.is_cuda):
+            raise ValueError("factors must live on the GPU")
+        P1 = P1.contiguous()
+        P2 = P2.contiguous()
+        if c is not None:
+            if c.dtype != torch.float32:
+                raise TypeError("c must be float32")
+            c = c.contiguous()
+        self.n1, self.n2 = int(P1.shape[0]), int(P2.shape[0])
+        self.n = self.n1 * self.n2
+        self.x_dtype = P1.dtype
+        self.scale_dtype = torch.float16 if _dtype_code(scale_dtype) == KQ_FP16 else torch.float32
+        self.handle = kq_create(self.n1, self.n2, P1.dtype, self.scale_dtype, P1, P2, c, alpha,
+                                stream, flags)
+        self.clip = kq_plan_clip_ratio(self.handle)
+        self.kernel = kq_plan_kernel_name(self.handle)
+
+    def __call__(self, X, y_debug=False, out=None, stream=None):
+        import torch
+        if X.dtype != self.x_dtype or X.dim() != 2 or X.shape[1] != self.n or X.stride(1) != 1:
+            raise ValueError("X must be [T, n] of the plan's dtype with unit column stride")
+        T = X.shape[0]
+        if out is None:
+            codes = torch.empty((T, self.n // 2), dtype=torch.uint8, device=X.device)
+            scales = torch.empty((T,), dtype=self.scale_dtype, device=X.device)
+        else:
+            codes, scales = out
+        y = torch.empty((T, self.n), dtype=torch.float32, device=X.device) if y_debug else None
+        kq_transform_quant(self.handle, X, T, X.stride(0) if T else self.n, codes, scales, y, stream)
+        return (codes, scales, y) if y_debug else (codes, scales)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            kq_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

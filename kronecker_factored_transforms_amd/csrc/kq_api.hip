@@ -1,0 +1,253 @@
+// Host side of libkq: argument checks, plan construction (factor re-layout, clip ratio),
+// kernel selection and launch. See include/kq.h for the contract of each entry point.
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "kq_internal.h"
+
+namespace {
+
+bool is_aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(kq_dtype d) {
+  switch (d) {
+    case KQ_BF16: return 2;
+    case KQ_FP16: return 2;
+    case KQ_FP32: return 4;
+  }
+  return 0;
+}
+
+// clip = sigmoid(alpha) in double with the host libm, rounded once to fp32
+// ("FlatQuant: Fast Learnable Affine Quantization", Symbol Map: alpha_a is mapped into
+// (0, 1) by a sigmoid). The two branches avoid overflow of exp for large |alpha|.
+float clip_from_alpha(float alpha) {
+  const double a = (double)alpha;
+  if (isinf(a)) return a > 0 ? 1.0f : 0.0f;
+  double v;
+  if (a >= 0) {
+    v = 1.0 / (1.0 + exp(-a));
+  } else {
+    const double e = exp(a);
+    v = e / (1.0 + e);
+  }
+  return (float)v;
+}
+
+float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+void free_plan_buffers(kq_plan *p) {
+  if (!p) return;
+  if (p->p1op) (void)hipFree(p->p1op);
+  if (p->p2op) (void)hipFree(p->p2op);
+  if (p->p1f) (void)hipFree(p->p1f);
+  if (p->p2f) (void)hipFree(p->p2f);
+  if (p->c) (void)hipFree(p->c);
+}
+
+kq_status upload(void **dst, const void *src, size_t bytes, hipStream_t s) {
+  if (hipMalloc(dst, bytes) != hipSuccess) {
+    *dst = nullptr;
+    return KQ_ERR_OUT_OF_MEMORY;
+  }
+  if (hipMemcpyAsync(*dst, src, bytes, hipMemcpyHostToDevice, s) != hipSuccess) return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kq_version(void) { return 10000; }
+
+const char *kq_status_string(kq_status s) {
+  switch (s) {
+    case KQ_OK: return "ok";
+    case KQ_ERR_INVALID_ARG: return "invalid argument";
+    case KQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KQ_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
+    case KQ_ERR_OUT_OF_MEMORY: return "out of memory";
+    case KQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+kq_status kq_choose_factors(int64_t n, int *n1, int *n2) {
+  if (n < 1 || !n1 || !n2 || n > (int64_t)1 << 40) return KQ_ERR_INVALID_ARG;
+  int64_t d = (int64_t)sqrt((double)n);
+  while (d * d > n) --d;
+  while ((d + 1) * (d + 1) <= n) ++d;
+  for (; d >= 1; --d) {
+    if (n % d == 0) {
+      if (n / d > 0x7fffffff) return KQ_ERR_INVALID_ARG;
+      *n1 = (int)d;
+      *n2 = (int)(n / d);
+      return KQ_OK;
+    }
+  }
+  return KQ_ERR_INVALID_ARG;
+}
+
+kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype scale_dtype,
+                       const void *P1, const void *P2, const float *c, float alpha, void *stream,
+                       unsigned flags) {
+  if (!out) return KQ_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (n1 < 1 || n2 < 1 || (int64_t)n1 * n2 > (1 << 24)) return KQ_ERR_INVALID_ARG;
+  const int n = n1 * n2;
+  if (n % 2) return KQ_ERR_INVALID_ARG;
+  if (x_dtype != KQ_BF16 && x_dtype != KQ_FP32) return KQ_ERR_INVALID_ARG;
+  if (scale_dtype != KQ_FP16 && scale_dtype != KQ_FP32) return KQ_ERR_INVALID_ARG;
+  if (!P1 || !P2) return KQ_ERR_INVALID_ARG;
+  if (isnan(alpha)) return KQ_ERR_INVALID_ARG;
+  if (flags & ~KQ_FLAG_FORCE_GENERIC) return KQ_ERR_INVALID_ARG;
+
+  // kernel choice (pure host logic, before any HIP call)
+  const char *kname = nullptr;
+  const void *ksym = nullptr;
+  kq_launch_fn fn = nullptr;
+  int kind = -1;
+  if (x_dtype == KQ_BF16 && !(flags & KQ_FLAG_FORCE_GENERIC)) {
+    fn = kq_fused_lookup(n1, n2, c != nullptr, &kname, &ksym);
+    if (fn) kind = KQ_KIND_FUSED_MFMA;
+  }
+  if (!fn) {
+    if (n > kq_generic_max_n()) return KQ_ERR_UNSUPPORTED;
+    fn = kq_generic_launcher(&kname, &ksym);
+    kind = KQ_KIND_GENERIC;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kq_plan *p = static_cast<kq_plan *>(calloc(1, sizeof(kq_plan)));
+  if (!p) return KQ_ERR_OUT_OF_MEMORY;
+  p->n1 = n1;
+  p->n2 = n2;
+  p->n = n;
+  p->x_dtype = x_dtype;
+  p->scale_dtype = scale_dtype;
+  p->clip = clip_from_alpha(alpha);
+  p->kind = kind;
+  p->kname = kname;
+  p->launch = fn;
+
+  kq_status st = KQ_OK;
+  const size_t es = elem_size(x_dtype);
+  std::vector<unsigned char> h1((size_t)n1 * n1 * es), h2((size_t)n2 * n2 * es);
+  std::vector<float> hc;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) { st = KQ_ERR_HIP; goto fail; }
+  p->device = dev;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    st = KQ_ERR_HIP;
+    goto fail;
+  }
+  if (hipMemcpyAsync(h1.data(), P1, h1.size(), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(h2.data(), P2, h2.size(), hipMemcpyDeviceToHost, s) != hipSuccess) {
+    st = KQ_ERR_HIP;
+    goto fail;
+  }
+  if (c) {
+    hc.resize(n);
+    if (hipMemcpyAsync(hc.data(), c, (size_t)n * 4, hipMemcpyDeviceToHost, s) != hipSuccess) {
+      st = KQ_ERR_HIP;
+      goto fail;
+    }
+  }
+  if (hipStreamSynchronize(s) != hipSuccess) { st = KQ_ERR_HIP; goto fail; }
+
+  if (kind == KQ_KIND_FUSED_MFMA) {
+    std::vector<uint16_t> a1(kq_fused_p1op_elems(n1)), a2(kq_fused_p2op_elems(n2));
+    kq_fused_arrange_p1(reinterpret_cast<const uint16_t *>(h1.data()), n1, a1.data());
+    kq_fused_arrange_p2(reinterpret_cast<const uint16_t *>(h2.data()), n2, a2.data());
+    if ((st = upload(&p->p1op, a1.data(), a1.size() * 2, s)) != KQ_OK) goto fail;
+    if ((st = upload(&p->p2op, a2.data(), a2.size() * 2, s)) != KQ_OK) goto fail;
+    if (c && (st = upload(reinterpret_cast<void **>(&p->c), hc.data(), hc.size() * 4, s)) != KQ_OK)
+      goto fail;
+    if (hipStreamSynchronize(s) != hipSuccess) { st = KQ_ERR_HIP; goto fail; }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ksym, kq_fused_threads(), 0) !=
+        hipSuccess) {
+      st = KQ_ERR_HIP;
+      goto fail;
+    }
+  } else {
+    std::vector<float> f1((size_t)n1 * n1), f2((size_t)n2 * n2);
+    for (size_t i = 0; i < f1.size(); ++i)
+      f1[i] = es == 2 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(h1.data())[i])
+                      : reinterpret_cast<const float *>(h1.data())[i];
+    for (size_t i = 0; i < f2.size(); ++i)
+      f2[i] = es == 2 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(h2.data())[i])
+                      : reinterpret_cast<const float *>(h2.data())[i];
+    if ((st = upload(reinterpret_cast<void **>(&p->p1f), f1.data(), f1.size() * 4, s)) != KQ_OK)
+      goto fail;
+    if ((st = upload(reinterpret_cast<void **>(&p->p2f), f2.data(), f2.size() * 4, s)) != KQ_OK)
+      goto fail;
+    if (c && (st = upload(reinterpret_cast<void **>(&p->c), hc.data(), hc.size() * 4, s)) != KQ_OK)
+      goto fail;
+    if (hipStreamSynchronize(s) != hipSuccess) { st = KQ_ERR_HIP; goto fail; }
+    const size_t lds = kq_generic_lds_bytes(n);
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(ksym, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+            hipSuccess) {
+      st = KQ_ERR_HIP;
+      goto fail;
+    }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ksym, kq_generic_threads(), lds) !=
+        hipSuccess) {
+      st = KQ_ERR_HIP;
+      goto fail;
+    }
+  }
+  if (per_cu < 1) { st = KQ_ERR_UNSUPPORTED; goto fail; }
+  p->grid_cap = ncu * per_cu;
+  *out = p;
+  return KQ_OK;
+
+fail:
+  free_plan_buffers(p);
+  free(p);
+  return st;
+}
+
+kq_status kq_create(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype scale_dtype,
+                    const void *P1, const void *P2, const float *c, float alpha, void *stream) {
+  return kq_create_ex(out, n1, n2, x_dtype, scale_dtype, P1, P2, c, alpha, stream, 0u);
+}
+
+kq_status kq_transform_quant(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
+                             uint8_t *codes, void *scales, float *y_debug, void *stream) {
+  if (!p || T < 0) return KQ_ERR_INVALID_ARG;
+  if (T == 0) return KQ_OK;
+  if (!X || !codes || !scales) return KQ_ERR_INVALID_ARG;
+  if (ldx < p->n) return KQ_ERR_INVALID_ARG;
+  const size_t es = elem_size(p->x_dtype);
+  if (!is_aligned(X, 16) || ((size_t)ldx * es) % 16 != 0) return KQ_ERR_ALIGNMENT;
+  if (!is_aligned(codes, 4) || !is_aligned(scales, elem_size(p->scale_dtype)))
+    return KQ_ERR_ALIGNMENT;
+  if (y_debug && !is_aligned(y_debug, 16)) return KQ_ERR_ALIGNMENT;
+  if (T > ((int64_t)1 << 40) / p->n) return KQ_ERR_INVALID_ARG;
+  const hipError_t e =
+      p->launch(p, X, T, ldx, codes, scales, y_debug, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
+kq_status kq_destroy(kq_plan *p) {
+  if (!p) return KQ_OK;
+  free_plan_buffers(p);
+  free(p);
+  return KQ_OK;
+}
+
+float kq_plan_clip_ratio(const kq_plan *p) { return p ? p->clip : 0.0f; }
+
+const char *kq_plan_kernel_name(const kq_plan *p) { return p ? p->kname : ""; }
+
+}  // extern "C"

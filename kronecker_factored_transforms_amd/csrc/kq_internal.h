@@ -1,0 +1,60 @@
+// Internal declarations shared by the libkq translation units (host API + kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kq.h"
+
+// Kernel families a plan can dispatch to.
+enum kq_kernel_kind {
+  KQ_KIND_FUSED_MFMA = 0,  // bf16 X/P, two chained bf16 MFMA contractions, fused epilogue
+  KQ_KIND_GENERIC = 1,     // any supported dtype/shape, fp32 FMA contractions
+};
+
+struct kq_plan;
+
+// Launches one kq_transform_quant on a plan of the matching variant. Arguments are
+// already validated by the host API.
+typedef hipError_t (*kq_launch_fn)(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
+                                   uint8_t *codes, void *scales, float *y_debug,
+                                   hipStream_t stream);
+
+struct kq_plan {
+  int n1, n2, n;
+  kq_dtype x_dtype;
+  kq_dtype scale_dtype;
+  float clip;           // exact fp32 clip ratio
+  int device;
+  int kind;             // kq_kernel_kind
+  const char *kname;    // static kernel variant name
+  kq_launch_fn launch;
+  int grid_cap;         // persistent-grid size (workgroups) for this device
+  // fused MFMA variant: operand-ordered bf16 factor copies (see kq_fused.hip)
+  void *p2op;
+  void *p1op;
+  // generic variant: fp32 row-major factor copies
+  float *p1f;
+  float *p2f;
+  // per-channel scale (fp32, n) or nullptr
+  float *c;
+};
+
+// ---- fused MFMA family (kq_fused.hip) ----
+// Returns the launcher for (n1, n2, has_c), or nullptr when no instantiation exists.
+kq_launch_fn kq_fused_lookup(int n1, int n2, bool has_c, const char **name,
+                             const void **kernel_symbol);
+// Bytes of the operand-ordered copies of P1 / P2 for the fused kernel.
+size_t kq_fused_p1op_elems(int n1);
+size_t kq_fused_p2op_elems(int n2);
+// Re-lay a row-major P1 (n1 x n1) / P2 (n2 x n2), given as bf16 bit patterns, into the
+// order in which the fused kernel's lanes consume them as MFMA B operands.
+void kq_fused_arrange_p1(const uint16_t *P1, int n1, uint16_t *out);
+void kq_fused_arrange_p2(const uint16_t *P2, int n2, uint16_t *out);
+int kq_fused_threads();
+
+// ---- generic family (kq_generic.hip) ----
+kq_launch_fn kq_generic_launcher(const char **name, const void **kernel_symbol);
+size_t kq_generic_lds_bytes(int n);
+int kq_generic_threads();
+int kq_generic_max_n();

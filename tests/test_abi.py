@@ -1,0 +1,107 @@
+"""The C-ABI library: it loads, exports every entry point include/kq.h declares, and its
+host-only logic (status strings, factor choice, argument checks that fail before any
+HIP call) behaves as documented. No compute calls: these run without a GPU."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from kronecker_factored_transforms_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libkq.so not built")
+    return B.lib()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(B.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_no_torch_types_in_the_abi():
+    src = open(HEADER).read()
+    assert "torch" not in src.lower() and "at::" not in src and "c10" not in src
+
+
+def test_status_strings_and_version(L):
+    assert B.kq_status_string(0) == "ok"
+    msgs = {B.kq_status_string(s) for s in range(6)}
+    assert len(msgs) == 6
+    assert B.kq_status_string(99) == "unknown status"
+    assert B.kq_version() >= 10000
+
+
+def _brute_factors(n):
+    best = None
+    for a in range(1, n + 1):
+        if n % a == 0 and a <= n // a:
+            if best is None or a + n // a < best[0] + best[1]:
+                best = (a, n // a)
+    return best
+
+
+def test_choose_factors_page_examples_and_brute_force(L):
+    # the FlatQuant page's example: hidden 8192 -> (64, 128)
+    assert B.kq_choose_factors(8192) == (64, 128)
+    assert B.kq_choose_factors(4096) == (64, 64)
+    assert B.kq_choose_factors(14336) == (112, 128)
+    for n in list(range(1, 300)) + [11008, 5120, 6144, 13824, 28672]:
+        assert B.kq_choose_factors(n) == _brute_factors(n), n
+    with pytest.raises(B.KqError) as e:
+        B.kq_choose_factors(0)
+    assert e.value.status == B.KQ_ERR_INVALID_ARG
+
+
+def _create_raw(L, n1, n2, xd=B.KQ_BF16, sd=B.KQ_FP16, p1=0x1000, p2=0x2000, c=None,
+                alpha=math.inf, flags=0):
+    h = ctypes.c_void_p(123)
+    st = L.kq_create_ex(ctypes.byref(h), n1, n2, xd, sd, p1, p2, c, ctypes.c_float(alpha), None, flags)
+    return st, h.value
+
+
+def test_create_rejects_bad_arguments_before_touching_the_gpu(L):
+    bad = [
+        dict(n1=0, n2=8), dict(n1=8, n2=-1), dict(n1=3, n2=5),            # n odd
+        dict(n1=8, n2=8, xd=7), dict(n1=8, n2=8, sd=B.KQ_BF16),
+        dict(n1=8, n2=8, p1=None), dict(n1=8, n2=8, p2=None),
+        dict(n1=8, n2=8, alpha=float("nan")), dict(n1=8, n2=8, flags=0x80),
+        dict(n1=1 << 13, n2=1 << 12),                                        # n too large
+    ]
+    for kw in bad:
+        st, h = _create_raw(L, **kw)
+        assert st == B.KQ_ERR_INVALID_ARG, kw
+        assert h is None, kw
+    assert L.kq_create_ex(None, 8, 8, 0, 2, 0x1000, 0x2000, None, ctypes.c_float(1.0), None, 0) \
+        == B.KQ_ERR_INVALID_ARG
+
+
+def test_create_reports_unsupported_shapes(L):
+    # fp32 beyond the generic kernel's on-chip limit and no MFMA variant for it
+    st, h = _create_raw(L, 256, 128, xd=B.KQ_FP32)
+    assert st == B.KQ_ERR_UNSUPPORTED and h is None
+
+
+def test_null_plan_paths(L):
+    assert L.kq_destroy(None) == B.KQ_OK
+    assert L.kq_plan_clip_ratio(None) == 0.0
+    assert L.kq_plan_kernel_name(None) == b""
+    assert L.kq_transform_quant(None, None, 0, 0, None, None, None, None) == B.KQ_ERR_INVALID_ARG

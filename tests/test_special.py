@@ -1,0 +1,187 @@
+"""GPU edge cases and exact special cases of the HIP path (through the C ABI).
+
+Exact cases: identity and signed-permutation factors have entries 0 / +-1, so every
+product and sum in the bf16 MFMA pipeline is exact; the GPU's Y must then equal the
+(permuted, sign-flipped) input bit for bit, and the codes must match the oracle's whole
+pipeline, not only its quantizer on the GPU's Y ("Kronecker Product", Definition: a
+signed permutation factor pair moves entry (i, k) of V to (s1(i), s2(k)))."""
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import kqtest as K
+from kronecker_factored_transforms_amd import binding as B
+from kronecker_factored_transforms_amd import synth as S
+from oracle import kq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _factor_tensor(P, dtype_name, dev):
+    arr = S.to_bf16_bits(P) if dtype_name == "bf16" else P.astype(np.float32)
+    return K.torch_from(arr, dtype_name).to(dev)
+
+
+@pytest.mark.parametrize("name", ["hidden_n8192", "attn_n4096", "down_proj_n14336"])
+@pytest.mark.parametrize("kind", ["identity", "signed_perm"])
+def test_exact_factors_reproduce_permuted_input(gpu, name, kind):
+    wl = replace(S.WORKLOADS[name], c_kind=None)
+    inp = S.make(wl, T=129)
+    rng = np.random.default_rng(5)
+    if kind == "identity":
+        P1, P2 = np.eye(wl.n1), np.eye(wl.n2)
+    else:
+        P1, P2 = S.signed_permutation(wl.n1, rng), S.signed_permutation(wl.n2, rng)
+    dP1, dP2 = _factor_tensor(P1, wl.dtype, gpu), _factor_tensor(P2, wl.dtype, gpu)
+    plan, X = K.make_plan(inp, P1=dP1, P2=dP2, c=None)
+    codes, scales, y = K.run(plan, X)
+    x = S.bf16_bits_to_f32(inp.X).astype(np.float64)
+    Y = O.transform(x, P1, P2)                       # exact: +-1 times bf16 values
+    assert np.array_equal(y.cpu().numpy(), Y.astype(np.float32))
+    _, oc, os_ = O.transform_quant(x, P1, P2, None, inp.alpha, "fp64")
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(K.np_scales(scales), os_)
+
+
+def test_power_of_two_channel_scale_is_exact(gpu):
+    """c = powers of two: x*c is exact in bf16, the low half of the split is zero, and the
+    identity-factor result is x*c exactly."""
+    wl = S.WORKLOADS["attn_n4096"]
+    inp = S.make(wl, T=70)
+    rng = np.random.default_rng(6)
+    c = (2.0 ** rng.integers(-3, 4, wl.n)).astype(np.float32)
+    import torch
+    dP1 = _factor_tensor(np.eye(wl.n1), "bf16", gpu)
+    dP2 = _factor_tensor(np.eye(wl.n2), "bf16", gpu)
+    plan, X = K.make_plan(inp, P1=dP1, P2=dP2, c=torch.from_numpy(c).to(gpu))
+    codes, scales, y = K.run(plan, X)
+    x = S.bf16_bits_to_f32(inp.X).astype(np.float64) * c.astype(np.float64)
+    assert np.array_equal(y.cpu().numpy(), x.astype(np.float32))
+    K.assert_quant_bit_exact(codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip, "fp16")
+
+
+def test_c_of_ones_equals_no_c(gpu):
+    import torch
+    inp = S.make("hidden_n8192", T=200)
+    p0, X = K.make_plan(inp, c=None)
+    p1, _ = K.make_plan(inp, c=torch.ones(inp.wl.n, dtype=torch.float32, device=gpu))
+    assert p1.kernel.endswith("_c") and not p0.kernel.endswith("_c")
+    a = K.run(p0, X)
+    b = K.run(p1, X)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2].abs(), b[2].abs())
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 63, 65, 127, 1025])
+def test_ragged_token_counts(gpu, T):
+    for name in ("attn_n4096", "hidden_n8192"):
+        inp = S.make(name, T=T)
+        plan, X = K.make_plan(inp)
+        codes, scales, y = K.run(plan, X)
+        assert codes.shape == (T, inp.wl.n // 2) and scales.shape == (T,)
+        K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+def test_zero_tokens_and_zero_rows(gpu):
+    import torch
+    inp = S.make("hidden_n8192", T=9)
+    X0 = inp.X.copy()
+    X0[[0, 4, 8]] = 0
+    inp.X = X0
+    plan, X = K.make_plan(inp)
+    codes, scales, y = K.run(plan, X)
+    s = K.np_scales(scales)
+    assert np.all(s[[0, 4, 8]] == 0) and np.all(codes.cpu().numpy()[[0, 4, 8]] == 0)
+    K.check_against_oracle(inp, codes.cpu().numpy(), s, y.cpu().numpy(), plan.clip)
+    # T == 0 enqueues nothing and succeeds
+    e = torch.empty((0, inp.wl.n), dtype=torch.bfloat16, device=gpu)
+    c0, s0 = plan(e)
+    assert c0.shape == (0, inp.wl.n // 2) and s0.shape == (0,)
+
+
+def test_strided_rows(gpu):
+    import torch
+    inp = S.make("hidden_n8192", T=100)
+    plan, X = K.make_plan(inp)
+    wide = torch.zeros((100, inp.wl.n + 64), dtype=torch.bfloat16, device=gpu)
+    wide[:, 32:32 + inp.wl.n] = X
+    Xs = wide[:, 32:32 + inp.wl.n]
+    assert Xs.stride(0) == inp.wl.n + 64
+    a = K.run(plan, Xs)
+    b = K.run(plan, X)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+@pytest.mark.parametrize("alpha", [-math.inf, -2.0, 0.0, 1.0, 7.0, math.inf])
+def test_clip_logits(gpu, alpha):
+    wl = replace(S.WORKLOADS["hidden_n8192"], alpha=alpha)
+    inp = S.make(wl, T=64)
+    plan, X = K.make_plan(inp)
+    assert plan.clip == float(O.clip_ratio(alpha))
+    codes, scales, y = K.run(plan, X)
+    K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+    if alpha == -math.inf:
+        assert np.all(K.np_scales(scales) == 0) and np.all(codes.cpu().numpy() == 0)
+
+
+def test_fp32_scales(gpu):
+    inp = S.make("attn_n4096", T=100)
+    plan, X = K.make_plan(inp, scale_dtype="fp32")
+    codes, scales, y = K.run(plan, X)
+    import torch
+    assert scales.dtype == torch.float32
+    K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip,
+                           scale_dtype="fp32")
+
+
+@pytest.mark.parametrize("name,T", [("attn_n4096", 50), ("hidden_n8192", 40), ("tiny_fp32_n64", 16)])
+def test_generic_kernel_parity(gpu, name, T):
+    inp = S.make(name, T=T)
+    plan, X = K.make_plan(inp, flags=B.KQ_FLAG_FORCE_GENERIC)
+    assert plan.kernel == "generic_fp32_fma"
+    codes, scales, y = K.run(plan, X)
+    rel = K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+    assert rel <= 1e-5          # fp32 contractions, no bf16 intermediate
+
+
+def test_shapes_without_an_mfma_variant_use_the_generic_kernel(gpu):
+    wl = replace(S.WORKLOADS["attn_n4096"], n1=12, n2=40, c_kind=None)
+    inp = S.make(wl, T=33)
+    plan, X = K.make_plan(inp)
+    assert plan.kernel == "generic_fp32_fma"
+    codes, scales, y = K.run(plan, X)
+    K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+def test_argument_errors(gpu):
+    import torch
+    inp = S.make("hidden_n8192", T=8)
+    plan, X = K.make_plan(inp)
+    n = inp.wl.n
+    codes = torch.empty((8, n // 2), dtype=torch.uint8, device=gpu)
+    scales = torch.empty((8,), dtype=torch.float16, device=gpu)
+    raw = torch.empty((8 * n + 8,), dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(B.KqError) as e:      # X not 16-byte aligned
+        B.kq_transform_quant(plan.handle, raw.data_ptr() + 2, 8, n, codes, scales)
+    assert e.value.status == B.KQ_ERR_ALIGNMENT
+    with pytest.raises(B.KqError) as e:      # ldx < n
+        B.kq_transform_quant(plan.handle, X, 8, n - 8, codes, scales)
+    assert e.value.status == B.KQ_ERR_INVALID_ARG
+    with pytest.raises(B.KqError) as e:      # T < 0
+        B.kq_transform_quant(plan.handle, X, -1, n, codes, scales)
+    assert e.value.status == B.KQ_ERR_INVALID_ARG
+    with pytest.raises(B.KqError) as e:
+        B.Plan(K.torch_from(inp.P1, "bf16").to(gpu), K.torch_from(inp.P2, "bf16").to(gpu),
+               alpha=float("nan"))
+    assert e.value.status == B.KQ_ERR_INVALID_ARG
+
+
+def test_repeated_runs_are_identical(gpu):
+    import torch
+    inp = S.make("down_proj_n14336", T=512)
+    plan, X = K.make_plan(inp)
+    ref = K.run(plan, X)
+    for _ in range(3):
+        out = K.run(plan, X)
+        assert all(torch.equal(a, b) for a, b in zip(ref, out))
