@@ -50,8 +50,17 @@ typedef enum kq_status {
 
 typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
 
-/* Flags for kq_create_ex. */
-#define KQ_FLAG_FORCE_GENERIC 0x1u /* use the fp32 FMA kernel even where the MFMA one applies */
+/* Flags for kq_create_ex. At most one KQ_FLAG_SPLIT_* may be given, only for bf16 plans
+ * (KQ_ERR_UNSUPPORTED when that split is not built for the shape). All variants compute
+ * the same Y up to fp32 accumulation order and quantize it the same way. */
+#define KQ_FLAG_FORCE_GENERIC 0x1u  /* fp32 FMA kernel even where an MFMA one applies   */
+#define KQ_FLAG_SPLIT_REG1 0x10u    /* MFMA: one wave per token, token in registers     */
+#define KQ_FLAG_SPLIT_REG2 0x20u    /* MFMA: two waves per token, token in registers    */
+#define KQ_FLAG_SPLIT_COLS 0x40u    /* MFMA: n2/32 waves per token, token staged in LDS */
+#define KQ_FLAG_SPLIT_DEEP 0x80u    /* MFMA: one wave per token and SIMD, next token     */
+                                    /* prefetched into registers                          */
+#define KQ_FLAG_SPLIT_STREAM 0x100u /* MFMA: one wave per token, next token prefetched   */
+                                    /* into LDS by DMA (no per-channel scale)             */
 
 /*
  * kq_choose_factors -- factor a hidden size for the Kronecker transform.
@@ -96,7 +105,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
  *            multiple of 16 bytes (else KQ_ERR_ALIGNMENT).
  *   T        number of tokens, >= 0. T == 0 returns KQ_OK and launches nothing.
  *   ldx      leading dimension of X in elements.
- *   codes    device, T x (n/2) bytes, row stride n/2, 4-byte aligned (written).
+ *   codes    device, T x (n/2) bytes, row stride n/2, 16-byte aligned (written).
  *   scales   device, T scales of the plan's scale_dtype (written).
  *   y_debug  device, T x n fp32, or NULL. When given, receives the exact fp32 Y that
  *            was quantized (for verification; adds 4n bytes of writes per token).

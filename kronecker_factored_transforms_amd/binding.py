@@ -16,6 +16,11 @@ LIB_PATH = os.path.join(_HERE, "libkq.so")
 KQ_OK, KQ_ERR_INVALID_ARG, KQ_ERR_UNSUPPORTED, KQ_ERR_ALIGNMENT, KQ_ERR_OUT_OF_MEMORY, KQ_ERR_HIP = range(6)
 KQ_BF16, KQ_FP32, KQ_FP16 = 0, 1, 2
 KQ_FLAG_FORCE_GENERIC = 0x1
+KQ_FLAG_SPLIT_REG1 = 0x10
+KQ_FLAG_SPLIT_REG2 = 0x20
+KQ_FLAG_SPLIT_COLS = 0x40
+KQ_FLAG_SPLIT_DEEP = 0x80
+KQ_FLAG_SPLIT_STREAM = 0x100
 
 # every symbol declared in include/kq.h
 EXPORTS = (

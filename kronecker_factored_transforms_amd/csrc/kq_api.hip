@@ -109,19 +109,37 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   if (scale_dtype != KQ_FP16 && scale_dtype != KQ_FP32) return KQ_ERR_INVALID_ARG;
   if (!P1 || !P2) return KQ_ERR_INVALID_ARG;
   if (isnan(alpha)) return KQ_ERR_INVALID_ARG;
-  if (flags & ~KQ_FLAG_FORCE_GENERIC) return KQ_ERR_INVALID_ARG;
+  const unsigned split_flags =
+      flags & (KQ_FLAG_SPLIT_REG1 | KQ_FLAG_SPLIT_REG2 | KQ_FLAG_SPLIT_COLS | KQ_FLAG_SPLIT_DEEP |
+               KQ_FLAG_SPLIT_STREAM);
+  if (flags & ~(KQ_FLAG_FORCE_GENERIC | split_flags)) return KQ_ERR_INVALID_ARG;
+  if ((split_flags & (split_flags - 1)) != 0) return KQ_ERR_INVALID_ARG;  // at most one
+  if (split_flags && ((flags & KQ_FLAG_FORCE_GENERIC) || x_dtype != KQ_BF16))
+    return KQ_ERR_INVALID_ARG;
+  const int split = split_flags == KQ_FLAG_SPLIT_REG1   ? KQ_SPLIT_REG1
+                    : split_flags == KQ_FLAG_SPLIT_REG2 ? KQ_SPLIT_REG2
+                    : split_flags == KQ_FLAG_SPLIT_COLS ? KQ_SPLIT_COLS
+                    : split_flags == KQ_FLAG_SPLIT_DEEP ? KQ_SPLIT_DEEP
+                    : split_flags == KQ_FLAG_SPLIT_STREAM ? KQ_SPLIT_STREAM
+                                                        : 0;
 
   // kernel choice (pure host logic, before any HIP call)
   const char *kname = nullptr;
   const void *ksym = nullptr;
   kq_launch_fn fn = nullptr;
   int kind = -1;
+  const kq_fused_variant *fv = nullptr;
   if (x_dtype == KQ_BF16 && !(flags & KQ_FLAG_FORCE_GENERIC)) {
-    fn = kq_fused_lookup(n1, n2, c != nullptr, &kname, &ksym);
-    if (fn) kind = KQ_KIND_FUSED_MFMA;
+    fv = kq_fused_lookup(n1, n2, c != nullptr, split);
+    if (fv) {
+      fn = fv->launch;
+      kname = fv->name;
+      ksym = fv->kernel_symbol;
+      kind = KQ_KIND_FUSED_MFMA;
+    }
   }
   if (!fn) {
-    if (n > kq_generic_max_n()) return KQ_ERR_UNSUPPORTED;
+    if (split || n > kq_generic_max_n()) return KQ_ERR_UNSUPPORTED;
     fn = kq_generic_launcher(&kname, &ksym);
     kind = KQ_KIND_GENERIC;
   }
@@ -167,13 +185,14 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   if (kind == KQ_KIND_FUSED_MFMA) {
     std::vector<uint16_t> a1(kq_fused_p1op_elems(n1)), a2(kq_fused_p2op_elems(n2));
     kq_fused_arrange_p1(reinterpret_cast<const uint16_t *>(h1.data()), n1, a1.data());
-    kq_fused_arrange_p2(reinterpret_cast<const uint16_t *>(h2.data()), n2, a2.data());
+    kq_fused_arrange_p2(reinterpret_cast<const uint16_t *>(h2.data()), n2, fv->p2_block,
+                        a2.data());
     if ((st = upload(&p->p1op, a1.data(), a1.size() * 2, s)) != KQ_OK) goto fail;
     if ((st = upload(&p->p2op, a2.data(), a2.size() * 2, s)) != KQ_OK) goto fail;
     if (c && (st = upload(reinterpret_cast<void **>(&p->c), hc.data(), hc.size() * 4, s)) != KQ_OK)
       goto fail;
     if (hipStreamSynchronize(s) != hipSuccess) { st = KQ_ERR_HIP; goto fail; }
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ksym, kq_fused_threads(), 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ksym, fv->threads, 0) !=
         hipSuccess) {
       st = KQ_ERR_HIP;
       goto fail;
@@ -230,7 +249,7 @@ kq_status kq_transform_quant(const kq_plan *p, const void *X, int64_t T, int64_t
   if (ldx < p->n) return KQ_ERR_INVALID_ARG;
   const size_t es = elem_size(p->x_dtype);
   if (!is_aligned(X, 16) || ((size_t)ldx * es) % 16 != 0) return KQ_ERR_ALIGNMENT;
-  if (!is_aligned(codes, 4) || !is_aligned(scales, elem_size(p->scale_dtype)))
+  if (!is_aligned(codes, 16) || !is_aligned(scales, elem_size(p->scale_dtype)))
     return KQ_ERR_ALIGNMENT;
   if (y_debug && !is_aligned(y_debug, 16)) return KQ_ERR_ALIGNMENT;
   if (T > ((int64_t)1 << 40) / p->n) return KQ_ERR_INVALID_ARG;

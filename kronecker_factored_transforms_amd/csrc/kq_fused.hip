@@ -13,25 +13,29 @@
 // the intermediate Z is handed from stage 1 to stage 2 in registers (no LDS round trip):
 // the stage-1 accumulator layout (4 consecutive rows of one column per lane) is exactly
 // a stage-2 operand layout once the reduction index is re-ordered, and that re-ordering
-// is absorbed by storing P1 pre-permuted in the plan. Quantization is done on the
-// stage-2 accumulators with a wave reduction for the absmax.
+// is absorbed by storing P1 pre-permuted in the plan. Quantization runs on the stage-2
+// accumulators with a wave reduction for the absmax.
 //
-// Work split: a workgroup has 4 waves; a token is shared by W = n2/32 waves, each of
-// which owns 32 output columns (a column block of Y needs only the same column block
-// of Z, which needs all of V and 32 columns of P2). The token tile V is staged in LDS
-// (XOR-swizzled 16-byte chunks) and read by the W waves as MFMA A operands.
+// Two work splits:
+//  * wave kernel (n1 <= 64): one wave owns a whole token. It loads the token straight
+//    from HBM into MFMA A-operand registers (16 rows x 64 contiguous bytes per load),
+//    reads P1/P2 operands from LDS (shared, read-only, loaded once per workgroup), and
+//    never synchronizes with other waves inside the token loop.
+//  * column kernel (larger n1): a token is shared by W = n2/32 waves of a workgroup,
+//    each owning 32 output columns (a column block of Y needs only the same column block
+//    of Z, which needs all of V and 32 columns of P2). The token tile is staged in LDS
+//    (XOR-swizzled 16-byte chunks) and the absmax is combined across the W waves.
 //
 // MFMA operand layouts used below (wave64, 16x16x32 bf16; lane L, g = L/16):
 //   A (16 x 32):  lane L holds row L%16, 8 reduction slots (g, v), v = 0..7
 //   B (32 x 16):  lane L holds column L%16, the same 8 reduction slots (g, v)
 //   D (16 x 16):  lane L holds rows 4g + r (r = 0..3) of column L%16
-// Only the pairing of A's and B's slots matters for a reduction, so the kernel chooses
-// which reduction index each slot carries and stores the factors in that order.
+// Only the pairing of A's and B's slots matters for a reduction, so the kernels choose
+// which reduction index each slot carries and the plan stores the factors in that order.
 
 #include "kq_internal.h"
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 namespace {
@@ -39,23 +43,592 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// ------------------------------------------------------------------------------------
+// shared helpers
+// ------------------------------------------------------------------------------------
+
+// Workgroup barrier that orders LDS only. __syncthreads() also fences global memory,
+// which makes every wave wait for its in-flight prefetch loads at each barrier; these
+// kernels only exchange data through LDS, so the release/acquire is restricted to it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Max over the wave of a non-negative value, returned wave-uniform: within each row of 16
+// lanes with DPP (quad swaps, half-row and row mirrors), then the four row maxima read
+// into scalars. No LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_step(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(o));
+}
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = dpp_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_step<0x141>(v);  // row_half_mirror
+  v = dpp_step<0x140>(v);  // row_mirror: every lane of a row holds the row max
+  const int i = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(i, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(i, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(i, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(i, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b) {
+  bf16x8 r;
+  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
+  r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
+  return r;
+}
+
+// x (8 bf16) * c (8 fp32) in fp32, split into hi = bf16(x*c) and lo = bf16(x*c - hi):
+// hi + lo carries ~16 significant bits, so one extra MFMA pass over lo keeps the
+// per-channel scale from adding a second bf16 rounding to the transform.
+__device__ __forceinline__ void split_scaled(const uint4 &raw, const float *c, uint4 &hi,
+                                             uint4 &lo) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float s0 = __fmul_rn(__uint_as_float(w[e] << 16), c[2 * e]);
+    const float s1 = __fmul_rn(__uint_as_float(w[e] & 0xFFFF0000u), c[2 * e + 1]);
+    const __bf16 h0 = (__bf16)s0, h1 = (__bf16)s1;
+    const __bf16 l0 = (__bf16)__fsub_rn(s0, (float)h0);
+    const __bf16 l1 = (__bf16)__fsub_rn(s1, (float)h1);
+    h[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    l[e] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Per-token step: s32 = fp32(fp32(clip * a) / 7), stored as fp16 (RNE) or fp32; the
+// codes use the stored step, inv = fp32(1 / s) (0 when s == 0, giving all-zero codes).
+struct TokenScale {
+  float s32;
+  _Float16 s16;
+  float inv;
+};
+
+__device__ __forceinline__ TokenScale token_scale(float amax, float clip, int scale_fp16) {
+  TokenScale t;
+  t.s32 = __fdiv_rn(__fmul_rn(clip, amax), 7.0f);
+  t.s16 = (_Float16)t.s32;
+  const float sf = scale_fp16 ? (float)t.s16 : t.s32;
+  t.inv = (sf == 0.f) ? 0.f : __fdiv_rn(1.0f, sf);
+  return t;
+}
+
+__device__ __forceinline__ void store_scale(void *scales, int64_t tok, const TokenScale &t,
+                                            int scale_fp16) {
+  if (scale_fp16) reinterpret_cast<_Float16 *>(scales)[tok] = t.s16;
+  else reinterpret_cast<float *>(scales)[tok] = t.s32;
+}
+
+// Quantize 8 consecutive values into one dword of 4-bit two's-complement codes (value e
+// in bits 4e..4e+3). Per value: v = fp32(y * inv); adding 1.5*2^23 + 8 in fp32 rounds v
+// to the nearest integer with ties to even (the sum's unit in the last place is 1 and
+// 1.5*2^23 + 8 is even) and leaves q + 8 in the low mantissa bits, for |v| < 2^22; the
+// integer clamp of the bit pattern is the clamp of q to [-8, 7]. The two steps are
+// separate roundings on purpose (no fused multiply-add). Codes are assembled as q + 8
+// and turned into two's complement with one xor per dword. CLAMP = false is only used
+// when every |v| < 7.5 is guaranteed (see clamp_needed), where the clamp is a no-op.
+template <bool CLAMP = true>
+__device__ __forceinline__ uint32_t quant8(const float (&y)[8], float inv) {
+  constexpr float kMagic = 12582920.0f;   // 1.5 * 2^23 + 8, bit pattern 0x4B400008
+  constexpr int kLo = 0x4B400000, kHi = 0x4B40000F;
+  uint32_t u[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = __fadd_rn(__fmul_rn(y[e], inv), kMagic);
+    u[e] = CLAMP ? (uint32_t)min(max(__float_as_int(t), kLo), kHi) : __float_as_uint(t);
+  }
+  // byte k of the result = u[2k] | u[2k+1] << 4 (bits above the low byte are ignored)
+  const uint32_t p0 = (u[1] << 4) | u[0], p1 = (u[3] << 4) | u[2];
+  const uint32_t p2 = (u[5] << 4) | u[4], p3 = (u[7] << 4) | u[6];
+  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);  // [p0.b0, p1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);  // [0, 0, p2.b0, p3.b0]
+  return (lo | hi) ^ 0x88888888u;
+}
+
+// Whether the clamp to [-8, 7] can change a code. With |y| <= a, inv = fp32(1/s) and
+// s the stored step of s32 = fp32(fp32(clip a)/7): for an fp16 step in the normal
+// range (relative rounding error <= 2^-11; an fp32 step is exact) every
+// |fp32(y inv)| <= (7/clip)(1 + 2^-10) < 7.5 once clip >= 0.935 (checked on the host),
+// so rint gives |q| <= 7. A zero or overflowed step gives inv = 0 and q = 0.
+__device__ __forceinline__ bool clamp_needed(int clip_allows_no_clamp, float s32) {
+  return !(clip_allows_no_clamp && (s32 >= 6.103515625e-05f || s32 == 0.f));
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void copy_to_lds(unsigned char *dst, const void *src, int bytes,
+                                            int tid) {
+  const uint4 *s = reinterpret_cast<const uint4 *>(src);
+  uint4 *d = reinterpret_cast<uint4 *>(dst);
+  for (int i = tid; i < bytes / 16; i += kThreads) d[i] = s[i];
+}
+
+// ------------------------------------------------------------------------------------
+// register kernel: WPT (1 or 2) waves per token, the token loaded straight into registers
+// ------------------------------------------------------------------------------------
+template <int N1, int N2, int WPT, bool HAS_C, bool DEEP = false>
+struct RegCfg {
+  static_assert(N1 % 16 == 0 && N1 >= 16 && N1 <= 64, "register kernel: n1 in {16, 32, 48, 64}");
+  static_assert(N2 == 32 || N2 == 64 || N2 == 128, "n2 must be 32, 64 or 128");
+  static_assert(WPT == 1 || WPT == 2, "one or two waves per token");
+  static_assert(N2 / WPT >= 32, "a wave owns at least 32 output columns");
+  static constexpr int MT = N1 / 16;            // row tiles of V/Z = column tiles (j) of Y
+  static constexpr int NT = N2 / 16 / WPT;      // column tiles (l) of this wave's block
+  static constexpr int CB = N2 / WPT;           // output columns owned by a wave
+  static constexpr int KS = N2 / 32;            // stage-1 reduction steps
+  static constexpr int KK = (N1 + 31) / 32;     // stage-2 reduction steps
+  static constexpr bool KHALF = (N1 % 32) != 0;
+  static constexpr int LPL = CB / 4;            // consecutive output columns per lane and row
+  static constexpr int TPI = kWaves / WPT;      // tokens per workgroup iteration
+  // prefetch the next token's tile while this one is computed: always with two waves
+  // per token; with one wave per token only in the deep variant, which runs one wave
+  // per SIMD so that the whole register file (VGPRs + AGPRs) is available
+  static constexpr bool PREFETCH = WPT > 1 || DEEP;
+  static constexpr int P2_BYTES = N2 * N2 * 2;
+  static constexpr int P1_BYTES = KK * MT * 1024;
+};
+
+template <int N1, int N2, int WPT, bool HAS_C, bool DEEP>
+__global__ __launch_bounds__(kThreads, DEEP ? 1 : 2) void kq_reg_kernel(
+    const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
+    const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
+    const float *__restrict__ cvec, float clip, int scale_fp16,
+    uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
+  using C = RegCfg<N1, N2, WPT, HAS_C, DEEP>;
+  constexpr int n = N1 * N2;
+  __shared__ __align__(16) unsigned char s_p2[C::P2_BYTES];
+  __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
+  __shared__ float s_red[2][kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int lr = lane & 15;
+  const int slot = wave / WPT;  // token slot within the iteration
+  const int wb = wave % WPT;    // column block of this wave
+
+  copy_to_lds(s_p2, p2op, C::P2_BYTES, tid);
+  copy_to_lds(s_p1, p1op, C::P1_BYTES, tid);
+  lds_barrier();
+  const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2) + wb * (C::KS * C::NT * 64);
+  const bf16x8 *sp1 = reinterpret_cast<const bf16x8 *>(s_p1);
+
+  // token tile as A operands: lane holds V[16 mt + lr][32 ks + 8 g + v] (raw bf16)
+  uint4 a[C::MT][C::KS];
+  auto load_tile = [&](int64_t tok) {
+    const __bf16 *xt = X + tok * ldx;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        a[mt][ks] = tok < T ? *reinterpret_cast<const uint4 *>(xt + (mt * 16 + lr) * N2 + ks * 32 + g * 8)
+                            : make_uint4(0u, 0u, 0u, 0u);
+  };
+
+  const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
+  int64_t grp = blockIdx.x;
+  if (C::PREFETCH && grp < ngroups) load_tile(grp * C::TPI + slot);
+  for (int it = 0; grp < ngroups; grp += gridDim.x, ++it) {
+    const int64_t tok = grp * C::TPI + slot;
+    if constexpr (!C::PREFETCH) load_tile(tok);
+    // deep variant: the next tile goes to a second register set right away
+    uint4 an[DEEP ? C::MT : 1][DEEP ? C::KS : 1];
+    if constexpr (DEEP) {
+      const int64_t nt_ = (grp + gridDim.x) * C::TPI + slot;
+      const __bf16 *xt = X + nt_ * ldx;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+          an[mt][ks] = nt_ < T ? *reinterpret_cast<const uint4 *>(xt + (mt * 16 + lr) * N2 + ks * 32 + g * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // ---- stage 1: Z[:, block] = V P2[:, block] (columns in the plan's permuted order) ----
+    f32x4 zacc[C::MT][C::NT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) zacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      bf16x8 ahi[C::MT], alo[HAS_C ? C::MT : 1];
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        if constexpr (HAS_C) {
+          const float *cp = cvec + (mt * 16 + lr) * N2 + ks * 32 + g * 8;
+          const float4 c0 = *reinterpret_cast<const float4 *>(cp);
+          const float4 c1 = *reinterpret_cast<const float4 *>(cp + 4);
+          const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          uint4 hi, lo;
+          split_scaled(a[mt][ks], cc, hi, lo);
+          ahi[mt] = __builtin_bit_cast(bf16x8, hi);
+          alo[mt] = __builtin_bit_cast(bf16x8, lo);
+        } else {
+          ahi[mt] = __builtin_bit_cast(bf16x8, a[mt][ks]);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) {
+        const bf16x8 b = sp2[(ks * C::NT + nt) * 64 + lane];
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+          zacc[mt][nt] = mfma(ahi[mt], b, zacc[mt][nt]);
+          if constexpr (HAS_C) zacc[mt][nt] = mfma(alo[mt], b, zacc[mt][nt]);
+        }
+      }
+    }
+    // the tile is consumed: fetch the next one while this token finishes
+    if constexpr (DEEP) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) a[mt][ks] = an[mt][ks];
+    } else if constexpr (C::PREFETCH) {
+      const int64_t nxt = grp + gridDim.x;
+      if (nxt < ngroups) load_tile(nxt * C::TPI + slot);
+    }
+
+    // ---- stage 2: Y^T[block, :] = Z[:, block]^T P1 (M = CB, K = n1, N = n1) ----
+    f32x4 yacc[C::NT][C::MT];
+#pragma unroll
+    for (int m2 = 0; m2 < C::NT; ++m2)
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) yacc[m2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const bool pad = C::KHALF && kk == C::KK - 1;
+      bf16x8 za[C::NT];
+#pragma unroll
+      for (int m2 = 0; m2 < C::NT; ++m2)
+        za[m2] = pack8(zacc[2 * kk][m2], pad ? zero : zacc[(2 * kk + 1) % C::MT][m2]);
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) {
+        const bf16x8 b = sp1[(kk * C::MT + nt) * 64 + lane];
+#pragma unroll
+        for (int m2 = 0; m2 < C::NT; ++m2) yacc[m2][nt] = mfma(za[m2], b, yacc[m2][nt]);
+      }
+    }
+
+    // ---- epilogue: lane holds Y[16 nt + lr][CB wb + LPL g + 4 m2 + r] ----
+    float m = 0.f;
+#pragma unroll
+    for (int m2 = 0; m2 < C::NT; ++m2)
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[m2][nt][r]));
+    m = wave_max(m);
+    if constexpr (WPT > 1) {
+      // combine the partial absmax of the waves sharing the token (slots alternate per
+      // iteration, so one barrier per token is enough)
+      if (lane == 0) s_red[it & 1][wave] = m;
+      lds_barrier();
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) m = fmaxf(m, s_red[it & 1][slot * WPT + w]);
+    }
+    const TokenScale ts = token_scale(m, clip, scale_fp16);
+
+    if (tok < T) {
+      uint8_t *crow = codes + tok * (int64_t)(n / 2);
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) {
+        const int j = nt * 16 + lr;
+        uint32_t w[C::NT / 2];
+#pragma unroll
+        for (int q = 0; q < C::NT / 2; ++q) {
+          const float yv[8] = {yacc[2 * q][nt][0],     yacc[2 * q][nt][1],
+                               yacc[2 * q][nt][2],     yacc[2 * q][nt][3],
+                               yacc[2 * q + 1][nt][0], yacc[2 * q + 1][nt][1],
+                               yacc[2 * q + 1][nt][2], yacc[2 * q + 1][nt][3]};
+          w[q] = quant8(yv, ts.inv);
+        }
+        uint8_t *dst = crow + j * (N2 / 2) + wb * (C::CB / 2) + g * (C::LPL / 2);
+        if constexpr (C::NT == 8) {
+          *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else if constexpr (C::NT == 4) {
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+        } else {
+          *reinterpret_cast<uint32_t *>(dst) = w[0];
+        }
+        if (ydbg != nullptr) {
+          float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wb * C::CB +
+                                                  g * C::LPL);
+#pragma unroll
+          for (int m2 = 0; m2 < C::NT; ++m2)
+            yp[m2] = make_float4(yacc[m2][nt][0], yacc[m2][nt][1], yacc[m2][nt][2], yacc[m2][nt][3]);
+        }
+      }
+      if (wb == 0 && lane == 0) store_scale(scales, tok, ts, scale_fp16);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// stream kernel: one wave per token, next token prefetched into LDS by DMA
+// ------------------------------------------------------------------------------------
+// Eight waves per workgroup (two per SIMD, one workgroup per CU). Each wave owns an LDS
+// slot of one token tile; while it computes token t, a global->LDS DMA
+// (global_load_lds_dwordx4: lane i's 16 bytes land at slot + 16 i) brings its next token
+// into the slot, already in the A-operand lane order, so the load costs no registers and
+// no barrier: a wave only ever waits for its own DMA. The DMA for the next token is
+// issued as soon as stage 1 has read the slot, and is in flight during stage 2, the
+// epilogue and the stores. P2 operands stay in LDS (shared, read-only), P1 operands in
+// registers. The code stores of a token are issued after the wait for the next token's
+// tile, so that wait never covers a just-issued store.
+template <int N1, int N2>
+struct StreamCfg {
+  static_assert(N1 % 16 == 0 && N1 >= 16 && N1 <= 64, "stream kernel: n1 in {16, 32, 48, 64}");
+  static_assert(N2 == 64 || N2 == 128, "stream kernel: n2 in {64, 128}");
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = WAVES * 64;  // the kernel's launch bound
+  static constexpr int MT = N1 / 16;
+  static constexpr int NT = N2 / 16;
+  static constexpr int KS = N2 / 32;
+  static constexpr int KK = (N1 + 31) / 32;
+  static constexpr bool KHALF = (N1 % 32) != 0;
+  static constexpr int LPL = N2 / 4;            // consecutive output columns per lane and row
+  static constexpr int TILE = N1 * N2 * 2;      // bytes of one token
+  static constexpr int P2_BYTES = N2 * N2 * 2;
+  static_assert(P2_BYTES + WAVES * TILE <= 160 * 1024, "LDS budget");
+};
+
+#define KQ_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0)
+
+// Wait, and keep both the compiler and the scheduler from moving memory accesses across.
+template <int IMM>
+__device__ __forceinline__ void wait_and_fence() {
+  __builtin_amdgcn_s_waitcnt(IMM);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Quantize a wave's whole Y tile (lane holds yacc[m2][nt] = 4 consecutive columns of row
+// 16 nt + lr) into packed code words w[nt][q] (8 consecutive columns each).
+template <bool CLAMP, int MT, int NT>
+__device__ __forceinline__ void quant_tile(const f32x4 (&yacc)[NT][MT], float inv,
+                                           uint32_t (&w)[MT][NT / 2]) {
+#pragma unroll
+  for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+    for (int q = 0; q < NT / 2; ++q) {
+      const float yv[8] = {yacc[2 * q][nt][0],     yacc[2 * q][nt][1],     yacc[2 * q][nt][2],
+                           yacc[2 * q][nt][3],     yacc[2 * q + 1][nt][0], yacc[2 * q + 1][nt][1],
+                           yacc[2 * q + 1][nt][2], yacc[2 * q + 1][nt][3]};
+      w[nt][q] = quant8<CLAMP>(yv, inv);
+    }
+}
+
+template <int N1, int N2>
+__device__ __forceinline__ void store_codes(uint8_t *codes, int64_t tok, const uint32_t (*w)[N2 / 32],
+                                            int lr, int g) {
+  uint8_t *crow = codes + tok * (int64_t)(N1 * N2 / 2);
+#pragma unroll
+  for (int nt = 0; nt < N1 / 16; ++nt) {
+    uint8_t *dst = crow + (nt * 16 + lr) * (N2 / 2) + g * (N2 / 8);
+    if constexpr (N2 == 128) *reinterpret_cast<uint4 *>(dst) = make_uint4(w[nt][0], w[nt][1], w[nt][2], w[nt][3]);
+    else *reinterpret_cast<uint2 *>(dst) = make_uint2(w[nt][0], w[nt][1]);
+  }
+}
+
+template <int N1, int N2, bool YDBG>
+__global__ __launch_bounds__(512) void kq_stream_kernel(
+    const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
+    const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
+    float clip, int scale_fp16, int clip_allows_no_clamp,
+    uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
+  using C = StreamCfg<N1, N2>;
+  constexpr int n = N1 * N2;
+  __shared__ __align__(16) unsigned char s_p2[C::P2_BYTES];
+  __shared__ __align__(16) unsigned char s_tile[C::WAVES][C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int g = lane >> 4;
+  const int lr = lane & 15;
+
+  {
+    const uint4 *src = reinterpret_cast<const uint4 *>(p2op);
+    uint4 *dst = reinterpret_cast<uint4 *>(s_p2);
+    for (int i = tid; i < C::P2_BYTES / 16; i += C::THREADS) dst[i] = src[i];
+  }
+  bf16x8 p1r[C::KK][C::MT];  // stage-2 B operands, resident
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+    for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
+  __syncthreads();
+  const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
+  unsigned char *slot = s_tile[wave];
+
+  // DMA token `tok` into this wave's slot: chunk (mt, ks) of lane L lands at
+  // slot + ((mt KS + ks) 64 + L) 16, exactly where the A-operand read expects it
+  auto dma_tile = [&](int64_t tok) {
+    const __bf16 *xt = X + tok * ldx + lr * N2 + g * 8;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        __builtin_amdgcn_global_load_lds(xt + mt * 16 * N2 + ks * 32,
+                                         KQ_LDS_PTR(slot + (mt * C::KS + ks) * 1024), 16, 0, 0);
+  };
+
+  const int64_t stride = (int64_t)gridDim.x * C::WAVES;
+  int64_t tok = (int64_t)blockIdx.x * C::WAVES + wave;
+  if (tok < T) dma_tile(tok);
+
+  uint32_t pend[C::MT][C::NT / 2];  // codes of the previous token, stored one step late
+  TokenScale pend_s{0.f, (_Float16)0.f, 0.f};
+  int64_t pend_tok = -1;
+
+  for (; tok < T; tok += stride) {
+    wait_and_fence<kWaitVm0>();  // this token's tile (and older stores) have landed
+    if (pend_tok >= 0) {
+      store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
+      if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
+    }
+    // ---- stage 1: Z = V P2, A operands read from the slot one reduction step at a time ----
+    // Operands are fetched one MFMA group ahead: B (P2, from LDS) for the next column
+    // tile, and A (the token, from the slot) for the next reduction step.
+    f32x4 zacc[C::MT][C::NT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) zacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a_cur[C::MT], a_nxt[C::MT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+      a_cur[mt] = *reinterpret_cast<const bf16x8 *>(slot + (mt * C::KS * 64 + lane) * 16);
+    bf16x8 b_cur = sp2[lane];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) {
+        const int nx = ks * C::NT + nt + 1;  // next (step, tile) in order
+        bf16x8 b_nxt = b_cur;
+        if (nx < C::KS * C::NT) b_nxt = sp2[nx * 64 + lane];
+        if (nt == 0 && ks + 1 < C::KS) {
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt)
+            a_nxt[mt] = *reinterpret_cast<const bf16x8 *>(slot + ((mt * C::KS + ks + 1) * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) zacc[mt][nt] = mfma(a_cur[mt], b_cur, zacc[mt][nt]);
+        b_cur = b_nxt;
+      }
+      if (ks + 1 < C::KS) {
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) a_cur[mt] = a_nxt[mt];
+      }
+    }
+    wait_and_fence<kWaitLgkm0>();  // every slot read has returned: the slot is free again
+    if (tok + stride < T) dma_tile(tok + stride);
+
+    // ---- stage 2: Y^T = Z^T P1 ----
+    // all of Z is converted to bf16 operands first, so that the fp32 stage-1
+    // accumulators are dead before the stage-2 accumulators come to life
+    bf16x8 za[C::KK][C::NT];
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const bool pad = C::KHALF && kk == C::KK - 1;
+#pragma unroll
+      for (int m2 = 0; m2 < C::NT; ++m2)
+        za[kk][m2] = pack8(zacc[2 * kk][m2], pad ? zero : zacc[(2 * kk + 1) % C::MT][m2]);
+    }
+    f32x4 yacc[C::NT][C::MT];
+#pragma unroll
+    for (int m2 = 0; m2 < C::NT; ++m2)
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) yacc[m2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+        for (int m2 = 0; m2 < C::NT; ++m2) yacc[m2][nt] = mfma(za[kk][m2], p1r[kk][nt], yacc[m2][nt]);
+
+    // ---- epilogue: lane holds Y[16 nt + lr][LPL g + 4 m2 + r] ----
+    float m = 0.f;
+#pragma unroll
+    for (int m2 = 0; m2 < C::NT; ++m2)
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[m2][nt][r]));
+    // the absmax and the clamp decision are wave-uniform: broadcast them so that the
+    // choice below is one scalar branch, not a per-lane select
+    const float amax = wave_max_uniform(m);
+    const TokenScale ts = token_scale(amax, clip, scale_fp16);
+    if (__builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, ts.s32) ? 1 : 0)) {
+      quant_tile<true, C::MT, C::NT>(yacc, ts.inv, pend);
+    } else {
+      quant_tile<false, C::MT, C::NT>(yacc, ts.inv, pend);
+    }
+    pend_s = ts;
+    pend_tok = tok;
+    if constexpr (YDBG) {
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) {
+        float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + (nt * 16 + lr) * N2 + g * C::LPL);
+#pragma unroll
+        for (int m2 = 0; m2 < C::NT; ++m2)
+          yp[m2] = make_float4(yacc[m2][nt][0], yacc[m2][nt][1], yacc[m2][nt][2], yacc[m2][nt][3]);
+      }
+    }
+  }
+  if (pend_tok >= 0) {
+    store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
+    if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// column kernel: W = n2/32 waves per token
+// ------------------------------------------------------------------------------------
 template <int N1, int N2, bool HAS_C>
-struct Cfg {
+struct ColsCfg {
   static_assert(N1 % 16 == 0 && N1 >= 16 && N1 <= 128, "n1 must be a multiple of 16 up to 128");
   static_assert(N2 == 32 || N2 == 64 || N2 == 128, "n2 must be 32, 64 or 128");
   static constexpr int W = N2 / 32;                 // waves per token
   static constexpr int TPI = kWaves / W;            // tokens per workgroup iteration
   static constexpr int MT = N1 / 16;                // 16-row tiles of V / Z
   static constexpr int KS = N2 / 32;                // stage-1 reduction steps
-  static constexpr int KK = N1 / 32;                // stage-2 full reduction steps
-  static constexpr bool KHALF = (N1 % 32) != 0;     // one trailing 16-wide stage-2 step
+  static constexpr int KK = (N1 + 31) / 32;         // stage-2 reduction steps of 32
+  static constexpr bool KHALF = (N1 % 32) != 0;     // last step holds 16 rows + 16 zeros
   static constexpr int CH = N2 / 8;                 // 16-byte chunks per V row
   static constexpr int TOK_CHUNKS = N1 * CH;
   static constexpr int CPT = TPI * TOK_CHUNKS / kThreads;  // chunks per thread per iter
   static_assert(CPT * kThreads == TPI * TOK_CHUNKS, "token tile must split evenly");
   static constexpr int V_BYTES = N1 * N2 * 2;
   static constexpr int P2_BYTES = N2 * N2 * 2;
-  static constexpr int P1_BYTES = N1 * N1 * 2;
+  static constexpr int P1_BYTES = KK * MT * 1024;   // n1 x n1 bf16, zero-padded to 32-steps
   static constexpr int VPLANES = HAS_C ? 2 : 1;     // hi (+ lo) bf16 planes of x*c
   static constexpr int VBUF = TPI * V_BYTES * VPLANES;
 };
@@ -67,40 +640,14 @@ __device__ __forceinline__ int vchunk_off(int r, int cc) {
   return (r * CH + (cc ^ (r & (CH - 1)))) * 16;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b) {
-  bf16x8 r;
-  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
-  r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
-  return r;
-}
-
-__device__ __forceinline__ bf16x4 pack4(const f32x4 &a) {
-  bf16x4 r;
-  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
-  return r;
-}
-
-// q = clamp(rint(fp32(y * inv)), -8, 7) as a 4-bit two's-complement nibble
-__device__ __forceinline__ uint32_t quant_nibble(float y, float inv) {
-  float v = __fmul_rn(y, inv);
-  v = rintf(v);
-  v = fminf(fmaxf(v, -8.0f), 7.0f);
-  return (uint32_t)((int)v) & 0xFu;
-}
-
 template <int N1, int N2, bool HAS_C>
-__global__ __launch_bounds__(kThreads) void kq_fused_kernel(
+__global__ __launch_bounds__(kThreads) void kq_cols_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
     const float *__restrict__ cvec, float clip, int scale_fp16,
     uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
-  using C = Cfg<N1, N2, HAS_C>;
+  using C = ColsCfg<N1, N2, HAS_C>;
+  constexpr int n = N1 * N2;
   __shared__ __align__(16) unsigned char s_p2[C::P2_BYTES];
   __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
   __shared__ __align__(16) unsigned char s_v[C::VBUF];
@@ -108,23 +655,15 @@ __global__ __launch_bounds__(kThreads) void kq_fused_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4;
   const int lr = lane & 15;
   const int ts = wave / C::W;  // token slot within the iteration
   const int wt = wave % C::W;  // column block of this wave
-  constexpr int n = N1 * N2;
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
 
-  // ---- factors -> LDS, once per workgroup (operand order, 16 B per lane) ----
-  {
-    const uint4 *src2 = reinterpret_cast<const uint4 *>(p2op);
-    uint4 *dst2 = reinterpret_cast<uint4 *>(s_p2);
-    for (int i = tid; i < C::P2_BYTES / 16; i += kThreads) dst2[i] = src2[i];
-    const uint4 *src1 = reinterpret_cast<const uint4 *>(p1op);
-    uint4 *dst1 = reinterpret_cast<uint4 *>(s_p1);
-    for (int i = tid; i < C::P1_BYTES / 16; i += kThreads) dst1[i] = src1[i];
-  }
+  copy_to_lds(s_p2, p2op, C::P2_BYTES, tid);
+  copy_to_lds(s_p1, p1op, C::P1_BYTES, tid);
 
   // per-thread chunk coordinates (fixed for the whole kernel)
   int c_ts[C::CPT], c_row[C::CPT], c_cc[C::CPT];
@@ -152,9 +691,9 @@ __global__ __launch_bounds__(kThreads) void kq_fused_kernel(
   auto issue_loads = [&](int64_t grp) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int64_t tok = grp * C::TPI + c_ts[i];
-      if (tok < T) {
-        pre[i] = *reinterpret_cast<const uint4 *>(X + tok * ldx + c_row[i] * N2 + c_cc[i] * 8);
+      const int64_t t = grp * C::TPI + c_ts[i];
+      if (t < T) {
+        pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + c_row[i] * N2 + c_cc[i] * 8);
       } else {
         pre[i] = make_uint4(0u, 0u, 0u, 0u);
       }
@@ -165,25 +704,10 @@ __global__ __launch_bounds__(kThreads) void kq_fused_kernel(
     for (int i = 0; i < C::CPT; ++i) {
       const int off = c_ts[i] * C::V_BYTES + vchunk_off<C::CH>(c_row[i], c_cc[i]);
       if constexpr (HAS_C) {
-        const uint32_t w[4] = {pre[i].x, pre[i].y, pre[i].z, pre[i].w};
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = __uint_as_float(w[e] << 16);
-          const float x1 = __uint_as_float(w[e] & 0xFFFF0000u);
-          const float s0 = __fmul_rn(x0, creg[i][2 * e]);
-          const float s1 = __fmul_rn(x1, creg[i][2 * e + 1]);
-          const __bf16 h0 = (__bf16)s0, h1 = (__bf16)s1;
-          const __bf16 l0 = (__bf16)__fsub_rn(s0, (float)h0);
-          const __bf16 l1 = (__bf16)__fsub_rn(s1, (float)h1);
-          hi[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-          lo[e] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-        }
-        *reinterpret_cast<uint4 *>(s_v + off) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        *reinterpret_cast<uint4 *>(s_v + C::TPI * C::V_BYTES + off) =
-            make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        uint4 hi, lo;
+        split_scaled(pre[i], creg[i], hi, lo);
+        *reinterpret_cast<uint4 *>(s_v + off) = hi;
+        *reinterpret_cast<uint4 *>(s_v + C::TPI * C::V_BYTES + off) = lo;
       } else {
         *reinterpret_cast<uint4 *>(s_v + off) = pre[i];
       }
@@ -192,14 +716,14 @@ __global__ __launch_bounds__(kThreads) void kq_fused_kernel(
 
   int64_t grp = blockIdx.x;
   if (grp < ngroups) issue_loads(grp);
-  __syncthreads();  // factors visible
+  lds_barrier();  // factors visible
 
   const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
   const bf16x8 *sp1 = reinterpret_cast<const bf16x8 *>(s_p1);
 
   for (; grp < ngroups; grp += gridDim.x) {
     store_lds();
-    __syncthreads();
+    lds_barrier();
     {
       const int64_t nxt = grp + gridDim.x;
       if (nxt < ngroups) issue_loads(nxt);  // in flight while this group computes
@@ -217,45 +741,36 @@ __global__ __launch_bounds__(kThreads) void kq_fused_kernel(
       const bf16x8 b1 = sp2[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
-        const int r = mt * 16 + lr;
-        const int off = vchunk_off<C::CH>(r, ks * 4 + g);
+        const int off = vchunk_off<C::CH>(mt * 16 + lr, ks * 4 + g);
         const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vt + off);
-        zacc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, zacc[mt][0], 0, 0, 0);
-        zacc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, zacc[mt][1], 0, 0, 0);
+        zacc[mt][0] = mfma(a, b0, zacc[mt][0]);
+        zacc[mt][1] = mfma(a, b1, zacc[mt][1]);
         if constexpr (HAS_C) {
           const bf16x8 al = *reinterpret_cast<const bf16x8 *>(vt + C::TPI * C::V_BYTES + off);
-          zacc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b0, zacc[mt][0], 0, 0, 0);
-          zacc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b1, zacc[mt][1], 0, 0, 0);
+          zacc[mt][0] = mfma(al, b0, zacc[mt][0]);
+          zacc[mt][1] = mfma(al, b1, zacc[mt][1]);
         }
       }
     }
 
     // ---- stage 2: Y^T[block, :] = Z[:, block]^T P1  (M = 32, K = n1, N = n1) ----
-    // The stage-1 accumulators of row tiles (2kk, 2kk+1) form the A operand of
-    // reduction step kk; P1 is stored in the matching reduction order.
+    // The stage-1 accumulators of row tiles (2kk, 2kk+1) form the A operand of step kk;
+    // an odd number of row tiles pads the last step with zeros (and P1 with zero rows),
+    // so that every accumulator chain uses the same MFMA opcode.
     f32x4 yacc[2][C::MT];
 #pragma unroll
     for (int nt = 0; nt < C::MT; ++nt) yacc[0][nt] = yacc[1][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
-      const bf16x8 za0 = pack8(zacc[2 * kk][0], zacc[2 * kk + 1][0]);
-      const bf16x8 za1 = pack8(zacc[2 * kk][1], zacc[2 * kk + 1][1]);
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const bool pad = C::KHALF && kk == C::KK - 1;
+      const bf16x8 za0 = pack8(zacc[2 * kk][0], pad ? zero : zacc[(2 * kk + 1) % C::MT][0]);
+      const bf16x8 za1 = pack8(zacc[2 * kk][1], pad ? zero : zacc[(2 * kk + 1) % C::MT][1]);
 #pragma unroll
       for (int nt = 0; nt < C::MT; ++nt) {
         const bf16x8 b = sp1[(kk * C::MT + nt) * 64 + lane];
-        yacc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za0, b, yacc[0][nt], 0, 0, 0);
-        yacc[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za1, b, yacc[1][nt], 0, 0, 0);
-      }
-    }
-    if constexpr (C::KHALF) {
-      const bf16x4 za0 = pack4(zacc[2 * C::KK][0]);
-      const bf16x4 za1 = pack4(zacc[2 * C::KK][1]);
-      const bf16x4 *sp1h = reinterpret_cast<const bf16x4 *>(s_p1 + C::KK * C::MT * 1024);
-#pragma unroll
-      for (int nt = 0; nt < C::MT; ++nt) {
-        const bf16x4 b = sp1h[nt * 64 + lane];
-        yacc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(za0, b, yacc[0][nt], 0, 0, 0);
-        yacc[1][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(za1, b, yacc[1][nt], 0, 0, 0);
+        yacc[0][nt] = mfma(za0, b, yacc[0][nt]);
+        yacc[1][nt] = mfma(za1, b, yacc[1][nt]);
       }
     }
 
@@ -269,17 +784,11 @@ __global__ __launch_bounds__(kThreads) void kq_fused_kernel(
         for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[h][nt][r]));
     m = wave_max(m);
     if (lane == 0) s_red[wave] = m;
-    __syncthreads();
+    lds_barrier();
     float amax = 0.f;
 #pragma unroll
     for (int w = 0; w < C::W; ++w) amax = fmaxf(amax, s_red[ts * C::W + w]);
-
-    // step s = fp16(fp32(fp32(clip * a) / 7)); codes use the stored step
-    const float s32 = __fdiv_rn(__fmul_rn(clip, amax), 7.0f);
-    float sf;
-    _Float16 s16 = (_Float16)s32;
-    if (scale_fp16) sf = (float)s16; else sf = s32;
-    const float inv = (sf == 0.f) ? 0.f : __fdiv_rn(1.0f, sf);
+    const TokenScale sc = token_scale(amax, clip, scale_fp16);
 
     if (tok < T) {
       // lane holds Y[j = nt*16 + lr][wt*32 + 8g + 4h + r]: 8 consecutive codes -> 1 dword
@@ -287,109 +796,154 @@ __global__ __launch_bounds__(kThreads) void kq_fused_kernel(
 #pragma unroll
       for (int nt = 0; nt < C::MT; ++nt) {
         const int j = nt * 16 + lr;
-        uint32_t word = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) word |= quant_nibble(yacc[h][nt][r], inv) << (4 * (4 * h + r));
-        *reinterpret_cast<uint32_t *>(crow + j * (N2 / 2) + wt * 16 + g * 4) = word;
+        const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
+                             yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
+        *reinterpret_cast<uint32_t *>(crow + j * (N2 / 2) + wt * 16 + g * 4) = quant8(yv, sc.inv);
         if (ydbg != nullptr) {
           float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wt * 32 + g * 8);
           yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
           yp[1] = make_float4(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]);
         }
       }
-      if (wt == 0 && lane == 0) {
-        if (scale_fp16) reinterpret_cast<_Float16 *>(scales)[tok] = s16;
-        else reinterpret_cast<float *>(scales)[tok] = s32;
-      }
+      if (wt == 0 && lane == 0) store_scale(scales, tok, sc, scale_fp16);
     }
-    __syncthreads();  // V tile and s_red are reused by the next iteration
+    lds_barrier();  // V tile and s_red are reused by the next iteration
   }
 }
 
-template <int N1, int N2, bool HAS_C>
-hipError_t launch_fused(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
-                        void *scales, float *y_debug, hipStream_t stream) {
-  using C = Cfg<N1, N2, HAS_C>;
+// ------------------------------------------------------------------------------------
+// launchers and the variant table
+// ------------------------------------------------------------------------------------
+template <int N1, int N2, int WPT, bool HAS_C, bool DEEP>
+hipError_t launch_reg(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
+                      void *scales, float *y_debug, hipStream_t stream) {
+  using C = RegCfg<N1, N2, WPT, HAS_C, DEEP>;
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
-  hipLaunchKernelGGL((kq_fused_kernel<N1, N2, HAS_C>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((kq_reg_kernel<N1, N2, WPT, HAS_C, DEEP>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
                      p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
   return hipGetLastError();
 }
 
-struct Entry {
-  int n1, n2;
-  bool has_c;
-  kq_launch_fn fn;
-  const void *sym;
-  const char *name;
-};
+template <int N1, int N2, bool HAS_C>
+hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
+                       void *scales, float *y_debug, hipStream_t stream) {
+  using C = ColsCfg<N1, N2, HAS_C>;
+  const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
+  const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
+  hipLaunchKernelGGL((kq_cols_kernel<N1, N2, HAS_C>), dim3(grid), dim3(kThreads), 0, stream,
+                     static_cast<const __bf16 *>(X), T, ldx,
+                     static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
+                     p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
+  return hipGetLastError();
+}
 
-#define KQ_FUSED_ENTRY(A, B)                                                           \
-  {A, B, false, &launch_fused<A, B, false>,                                            \
-   reinterpret_cast<const void *>(&kq_fused_kernel<A, B, false>),                      \
-   "fused_mfma_bf16_" #A "x" #B},                                                      \
-  {A, B, true, &launch_fused<A, B, true>,                                              \
-   reinterpret_cast<const void *>(&kq_fused_kernel<A, B, true>),                       \
-   "fused_mfma_bf16_" #A "x" #B "_c"}
+template <int N1, int N2>
+hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
+                         void *scales, float *y_debug, hipStream_t stream) {
+  using C = StreamCfg<N1, N2>;
+  const int64_t ngroups = (T + C::WAVES - 1) / C::WAVES;
+  const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
+  // the debug output has its own instantiation so that the timed kernel keeps its
+  // registers; both compute Y with the same per-accumulator MFMA order
+  auto k = y_debug ? &kq_stream_kernel<N1, N2, true> : &kq_stream_kernel<N1, N2, false>;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
+                     static_cast<const __bf16 *>(X), T, ldx,
+                     static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
+                     p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes,
+                     scales, y_debug);
+  return hipGetLastError();
+}
 
-const Entry kEntries[] = {
-    KQ_FUSED_ENTRY(16, 32),  KQ_FUSED_ENTRY(32, 32),
-    KQ_FUSED_ENTRY(16, 64),  KQ_FUSED_ENTRY(32, 64),  KQ_FUSED_ENTRY(48, 64),
-    KQ_FUSED_ENTRY(64, 64),
-    KQ_FUSED_ENTRY(16, 128), KQ_FUSED_ENTRY(32, 128), KQ_FUSED_ENTRY(48, 128),
-    KQ_FUSED_ENTRY(64, 128), KQ_FUSED_ENTRY(80, 128), KQ_FUSED_ENTRY(96, 128),
-    KQ_FUSED_ENTRY(112, 128), KQ_FUSED_ENTRY(128, 128),
+#define KQ_STREAM(A, B)                                                                \
+  kq_fused_variant{A, B, false, KQ_SPLIT_STREAM, (B), StreamCfg<A, B>::THREADS,          \
+                   &launch_stream<A, B>,                                               \
+                   reinterpret_cast<const void *>(&kq_stream_kernel<A, B, false>),     \
+                   "fused_mfma_bf16_stream_" #A "x" #B}
+#define KQ_REG(A, B, WPT, HC, SUF)                                                     \
+  kq_fused_variant{A, B, HC, WPT, (B) / (WPT), kThreads, &launch_reg<A, B, WPT, HC, false>, \
+                   reinterpret_cast<const void *>(&kq_reg_kernel<A, B, WPT, HC, false>), \
+                   "fused_mfma_bf16_reg" #WPT "_" #A "x" #B SUF}
+#define KQ_DEEP(A, B, HC, SUF)                                                         \
+  kq_fused_variant{A, B, HC, KQ_SPLIT_DEEP, (B), kThreads, &launch_reg<A, B, 1, HC, true>, \
+                   reinterpret_cast<const void *>(&kq_reg_kernel<A, B, 1, HC, true>),   \
+                   "fused_mfma_bf16_deep_" #A "x" #B SUF}
+#define KQ_COLS(A, B, HC, SUF)                                                         \
+  kq_fused_variant{A, B, HC, KQ_SPLIT_COLS, 32, kThreads, &launch_cols<A, B, HC>,       \
+                   reinterpret_cast<const void *>(&kq_cols_kernel<A, B, HC>),          \
+                   "fused_mfma_bf16_cols_" #A "x" #B SUF}
+#define KQ_ALL1(A, B)                                                                  \
+  KQ_REG(A, B, 1, false, ""), KQ_REG(A, B, 1, true, "_c"), KQ_COLS(A, B, false, ""),    \
+      KQ_COLS(A, B, true, "_c")
+#define KQ_ALL(A, B)                                                                   \
+  KQ_ALL1(A, B), KQ_REG(A, B, 2, false, ""), KQ_REG(A, B, 2, true, "_c")
+
+// Every work split that is built. The first match for a shape is its default: the
+// register kernels where their registers fit without spilling (two waves per token
+// where n2 >= 64, which leaves room to prefetch the next token), else the column kernel.
+const kq_fused_variant kVariants[] = {
+    // defaults
+    KQ_REG(16, 32, 1, false, ""),  KQ_REG(16, 32, 1, true, "_c"),
+    KQ_REG(32, 32, 1, false, ""),  KQ_REG(32, 32, 1, true, "_c"),
+    KQ_REG(16, 64, 2, false, ""),  KQ_REG(16, 64, 2, true, "_c"),
+    KQ_REG(32, 64, 2, false, ""),  KQ_REG(32, 64, 2, true, "_c"),
+    KQ_REG(48, 64, 2, false, ""),  KQ_REG(48, 64, 2, true, "_c"),
+    KQ_REG(64, 64, 2, false, ""),  KQ_REG(64, 64, 2, true, "_c"),
+    KQ_REG(16, 128, 2, false, ""), KQ_COLS(16, 128, true, "_c"),
+    KQ_REG(32, 128, 2, false, ""), KQ_COLS(32, 128, true, "_c"),
+    KQ_REG(48, 128, 2, false, ""), KQ_COLS(48, 128, true, "_c"),
+    KQ_STREAM(64, 128), KQ_COLS(64, 128, true, "_c"),
+    KQ_COLS(80, 128, false, ""),   KQ_COLS(80, 128, true, "_c"),
+    KQ_COLS(96, 128, false, ""),   KQ_COLS(96, 128, true, "_c"),
+    KQ_COLS(112, 128, false, ""),  KQ_COLS(112, 128, true, "_c"),
+    KQ_COLS(128, 128, false, ""),  KQ_COLS(128, 128, true, "_c"),
+    // the other splits, selectable with KQ_FLAG_SPLIT_*
+    KQ_ALL1(16, 32), KQ_ALL1(32, 32), KQ_ALL(16, 64), KQ_ALL(32, 64), KQ_ALL(48, 64),
+    KQ_ALL(64, 64), KQ_ALL(16, 128), KQ_ALL(32, 128), KQ_ALL(48, 128), KQ_ALL(64, 128),
+    KQ_DEEP(64, 128, false, ""), KQ_DEEP(64, 64, false, ""), KQ_DEEP(64, 64, true, "_c"),
+    KQ_STREAM(16, 64), KQ_STREAM(32, 64), KQ_STREAM(48, 64), KQ_STREAM(64, 64),
+    KQ_STREAM(16, 128), KQ_STREAM(32, 128), KQ_STREAM(48, 128),
 };
 
 }  // namespace
 
-kq_launch_fn kq_fused_lookup(int n1, int n2, bool has_c, const char **name,
-                             const void **kernel_symbol) {
-  for (const Entry &e : kEntries) {
-    if (e.n1 == n1 && e.n2 == n2 && e.has_c == has_c) {
-      if (name) *name = e.name;
-      if (kernel_symbol) *kernel_symbol = e.sym;
-      return e.fn;
-    }
-  }
+const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split) {
+  for (const kq_fused_variant &e : kVariants)
+    if (e.n1 == n1 && e.n2 == n2 && e.has_c == has_c && (split == 0 || e.split == split))
+      return &e;
   return nullptr;
 }
 
-int kq_fused_threads() { return kThreads; }
 
-size_t kq_fused_p1op_elems(int n1) { return (size_t)n1 * (size_t)n1; }
+size_t kq_fused_p1op_elems(int n1) { return (size_t)((n1 + 31) / 32) * (n1 / 16) * 512; }
 size_t kq_fused_p2op_elems(int n2) { return (size_t)n2 * (size_t)n2; }
 
-// P2 as stage-1 B operands: [wave block wb][step ks][tile a][lane L][slot v] =
-//   P2[32 ks + 8 g + v][32 wb + sigma(16 a + L%16)],  g = L/16,
-// with sigma(16a + 4b + r) = 8b + 4a + r, so that after stage 2 every lane holds 8
-// consecutive output columns (one packed dword of codes).
-void kq_fused_arrange_p2(const uint16_t *P2, int n2, uint16_t *out) {
-  const int W = n2 / 32, KS = n2 / 32;
+// P2 as stage-1 B operands, in blocks of `cb` output columns (one block per wave that
+// shares a token): [block wb][step ks][tile a][lane L][slot v] =
+//   P2[32 ks + 8 g + v][cb wb + (cb/4) b + 4 a + r],   g = L/16, b = (L%16)/4, r = L%4.
+// Reduction slot (g, v) of step ks carries row 32 ks + 8 g + v. The 16 columns of tile a
+// are spread so that, after stage 2, lane group g holds the cb/4 consecutive output
+// columns cb wb + (cb/4) g + [0, cb/4) of a row of Y, i.e. cb/8 packed code bytes.
+void kq_fused_arrange_p2(const uint16_t *P2, int n2, int cb, uint16_t *out) {
+  const int KS = n2 / 32, NB = n2 / cb, NT = cb / 16;
   size_t o = 0;
-  for (int wb = 0; wb < W; ++wb)
+  for (int wb = 0; wb < NB; ++wb)
     for (int ks = 0; ks < KS; ++ks)
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < NT; ++a)
         for (int L = 0; L < 64; ++L)
           for (int v = 0; v < 8; ++v) {
             const int g = L / 16, x = L % 16, b = x / 4, r = x % 4;
-            const int k = 32 * ks + 8 * g + v;
-            const int col = 32 * wb + 8 * b + 4 * a + r;
-            out[o++] = P2[(size_t)k * n2 + col];
+            out[o++] = P2[(size_t)(32 * ks + 8 * g + v) * n2 + cb * wb + (cb / 4) * b + 4 * a + r];
           }
 }
 
-// P1 as stage-2 B operands: full steps [kk][tile t][lane L][slot v] =
-//   P1[32 kk + 16 (v/4) + 4 g + (v%4)][16 t + L%16]
-// (slot order of the stage-1 accumulators of row tiles 2kk and 2kk+1), then, when n1 is
-// an odd multiple of 16, one half step [t][L][v<4] = P1[32 KK + 4 g + v][16 t + L%16].
+// P1 as stage-2 B operands: [kk][tile t][lane L][slot v] =
+//   P1[32 kk + 16 (v/4) + 4 g + (v%4)][16 t + L%16]   (zero where that row is >= n1)
+// i.e. the slot order of the stage-1 accumulators of row tiles 2kk and 2kk+1.
 void kq_fused_arrange_p1(const uint16_t *P1, int n1, uint16_t *out) {
-  const int MT = n1 / 16, KK = n1 / 32;
+  const int MT = n1 / 16, KK = (n1 + 31) / 32;
   size_t o = 0;
   for (int kk = 0; kk < KK; ++kk)
     for (int t = 0; t < MT; ++t)
@@ -397,15 +951,6 @@ void kq_fused_arrange_p1(const uint16_t *P1, int n1, uint16_t *out) {
         for (int v = 0; v < 8; ++v) {
           const int g = L / 16;
           const int i = 32 * kk + 16 * (v / 4) + 4 * g + (v % 4);
-          out[o++] = P1[(size_t)i * n1 + 16 * t + L % 16];
+          out[o++] = i < n1 ? P1[(size_t)i * n1 + 16 * t + L % 16] : (uint16_t)0;
         }
-  if (n1 % 32) {
-    for (int t = 0; t < MT; ++t)
-      for (int L = 0; L < 64; ++L)
-        for (int v = 0; v < 4; ++v) {
-          const int g = L / 16;
-          const int i = 32 * KK + 4 * g + v;
-          out[o++] = P1[(size_t)i * n1 + 16 * t + L % 16];
-        }
-  }
 }

@@ -23,6 +23,13 @@ __device__ __forceinline__ float load_elem(const void *X, int is_bf16, int64_t i
   return static_cast<const float *>(X)[idx];
 }
 
+// Workgroup barrier ordering LDS only (no wait for in-flight global loads).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint32_t quant_nibble(float y, float inv) {
   float v = __fmul_rn(y, inv);
   v = rintf(v);
@@ -48,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void kq_generic_kernel(
       if (cvec != nullptr) x = __fmul_rn(x, cvec[e]);
       V[e] = x;
     }
-    __syncthreads();
+    lds_barrier();
     // Z[i][l] = sum_k V[i][k] P2[k][l]
     for (int e = tid; e < n; e += kThreads) {
       const int i = e / n2, l = e % n2;
@@ -56,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void kq_generic_kernel(
       for (int k = 0; k < n2; ++k) acc = fmaf(V[i * n2 + k], P2[(size_t)k * n2 + l], acc);
       Z[e] = acc;
     }
-    __syncthreads();
+    lds_barrier();
     // Y[j][l] = sum_i P1[i][j] Z[i][l]
     float m = 0.f;
     for (int e = tid; e < n; e += kThreads) {
@@ -69,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void kq_generic_kernel(
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     if ((tid & 63) == 0) s_red[tid >> 6] = m;
-    __syncthreads();
+    lds_barrier();
     float amax = 0.f;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) amax = fmaxf(amax, s_red[w]);
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void kq_generic_kernel(
       if (scale_fp16) static_cast<_Float16 *>(scales)[tok] = s16;
       else static_cast<float *>(scales)[tok] = s32;
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

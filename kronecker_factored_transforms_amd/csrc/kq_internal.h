@@ -41,17 +41,33 @@ struct kq_plan {
 };
 
 // ---- fused MFMA family (kq_fused.hip) ----
-// Returns the launcher for (n1, n2, has_c), or nullptr when no instantiation exists.
-kq_launch_fn kq_fused_lookup(int n1, int n2, bool has_c, const char **name,
-                             const void **kernel_symbol);
-// Bytes of the operand-ordered copies of P1 / P2 for the fused kernel.
+// Work splits of the fused family: 1 or 2 waves per token with the token in registers
+// ("deep": one wave per token and per SIMD, next token prefetched into registers), the
+// column kernel (n2/32 waves per token, token staged in LDS), or the stream kernel (one
+// wave per token, next token prefetched into an LDS slot by DMA).
+enum { KQ_SPLIT_REG1 = 1, KQ_SPLIT_REG2 = 2, KQ_SPLIT_COLS = 3, KQ_SPLIT_DEEP = 4,
+       KQ_SPLIT_STREAM = 5 };
+
+struct kq_fused_variant {
+  int n1, n2;
+  bool has_c;
+  int split;      // KQ_SPLIT_*
+  int p2_block;   // output columns per P2 operand block (kq_fused_arrange_p2)
+  int threads;    // workgroup size
+  kq_launch_fn launch;
+  const void *kernel_symbol;
+  const char *name;
+};
+
+// The variant for (n1, n2, has_c) with the given split (0: the default one), or nullptr.
+const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split);
+// Element counts of the operand-ordered bf16 copies of P1 / P2.
 size_t kq_fused_p1op_elems(int n1);
 size_t kq_fused_p2op_elems(int n2);
 // Re-lay a row-major P1 (n1 x n1) / P2 (n2 x n2), given as bf16 bit patterns, into the
-// order in which the fused kernel's lanes consume them as MFMA B operands.
+// order in which the fused kernels' lanes consume them as MFMA B operands.
 void kq_fused_arrange_p1(const uint16_t *P1, int n1, uint16_t *out);
-void kq_fused_arrange_p2(const uint16_t *P2, int n2, uint16_t *out);
-int kq_fused_threads();
+void kq_fused_arrange_p2(const uint16_t *P2, int n2, int cb, uint16_t *out);
 
 // ---- generic family (kq_generic.hip) ----
 kq_launch_fn kq_generic_launcher(const char **name, const void **kernel_symbol);

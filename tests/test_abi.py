@@ -94,6 +94,17 @@ def test_create_rejects_bad_arguments_before_touching_the_gpu(L):
         == B.KQ_ERR_INVALID_ARG
 
 
+def test_split_flags_are_validated_on_the_host(L):
+    two = B.KQ_FLAG_SPLIT_REG1 | B.KQ_FLAG_SPLIT_COLS
+    for kw in (dict(flags=two), dict(flags=B.KQ_FLAG_SPLIT_REG2 | B.KQ_FLAG_FORCE_GENERIC),
+               dict(flags=B.KQ_FLAG_SPLIT_REG1, xd=B.KQ_FP32)):
+        st, h = _create_raw(L, 64, 128, **kw)
+        assert st == B.KQ_ERR_INVALID_ARG and h is None, kw
+    # a split that is not built for the shape
+    st, h = _create_raw(L, 112, 128, flags=B.KQ_FLAG_SPLIT_REG2)
+    assert st == B.KQ_ERR_UNSUPPORTED and h is None
+
+
 def test_create_reports_unsupported_shapes(L):
     # fp32 beyond the generic kernel's on-chip limit and no MFMA variant for it
     st, h = _create_raw(L, 256, 128, xd=B.KQ_FP32)

@@ -1,0 +1,51 @@
+"""Every fused work split (one or two waves per token with the token in registers, or the
+column kernel with the token in LDS) against the oracle, on shapes around the workloads:
+square and non-square factors, with and without the per-channel scale, ragged T."""
+from dataclasses import replace
+
+import pytest
+
+import kqtest as K
+from kronecker_factored_transforms_amd import binding as B
+from kronecker_factored_transforms_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+
+SPLITS = {"reg1": B.KQ_FLAG_SPLIT_REG1, "reg2": B.KQ_FLAG_SPLIT_REG2, "cols": B.KQ_FLAG_SPLIT_COLS,
+          "deep": B.KQ_FLAG_SPLIT_DEEP, "stream": B.KQ_FLAG_SPLIT_STREAM}
+DEEP_SHAPES = {(64, 128, False), (64, 64, False), (64, 64, True)}
+SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (32, 128, False),
+          (48, 128, True), (16, 64, True), (48, 64, False), (32, 32, True), (16, 32, False),
+          (112, 128, False), (112, 128, True), (96, 128, False), (128, 128, True), (80, 128, False)]
+
+
+def _available(n1, n2, split, with_c=False):
+    if split == "deep":
+        return (n1, n2, with_c) in DEEP_SHAPES
+    if split == "stream":
+        return n1 <= 64 and n2 >= 64 and not with_c
+    if split == "reg1":
+        return n1 <= 64
+    if split == "reg2":
+        return n1 <= 64 and n2 >= 64
+    return True
+
+
+@pytest.mark.parametrize("n1,n2,with_c", SHAPES)
+@pytest.mark.parametrize("split", sorted(SPLITS))
+def test_split_parity(gpu, n1, n2, with_c, split):
+    base = S.WORKLOADS["attn_n4096"] if with_c else S.WORKLOADS["hidden_n8192"]
+    wl = replace(base, n1=n1, n2=n2, n_outliers=4, pivot_channels=0)
+    inp = S.make(wl, T=203)
+    if not _available(n1, n2, split, with_c):
+        with pytest.raises(B.KqError) as e:
+            K.make_plan(inp, flags=SPLITS[split])
+        assert e.value.status == B.KQ_ERR_UNSUPPORTED
+        return
+    plan, X = K.make_plan(inp, flags=SPLITS[split])
+    assert plan.kernel.startswith(f"fused_mfma_bf16_{split}_"), plan.kernel
+    codes, scales, y = K.run(plan, X)
+    codes2, scales2 = K.run(plan, X, y_debug=False)
+    import torch
+    assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
+    K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
