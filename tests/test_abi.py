@@ -83,7 +83,7 @@ def test_create_rejects_bad_arguments_before_touching_the_gpu(L):
         dict(n1=0, n2=8), dict(n1=8, n2=-1), dict(n1=3, n2=5),            # n odd
         dict(n1=8, n2=8, xd=7), dict(n1=8, n2=8, sd=B.KQ_BF16),
         dict(n1=8, n2=8, p1=None), dict(n1=8, n2=8, p2=None),
-        dict(n1=8, n2=8, alpha=float("nan")), dict(n1=8, n2=8, flags=0x80),
+        dict(n1=8, n2=8, alpha=float("nan")), dict(n1=8, n2=8, flags=0x8000),
         dict(n1=1 << 13, n2=1 << 12),                                        # n too large
     ]
     for kw in bad:
