@@ -392,9 +392,8 @@ __global__ __launch_bounds__(kThreads, DEEP ? 1 : 2) void kq_reg_kernel(
 // slot of one token tile; while it computes token t, a global->LDS DMA
 // (global_load_lds_dwordx4: lane i's 16 bytes land at slot + 16 i) brings its next token
 // into the slot, already in the A-operand lane order, so the load costs no registers and
-// no barrier: a wave only ever waits for its own DMA. The DMA for the next token is
-// issued as soon as stage 1 has read the slot, and is in flight during stage 2, the
-// epilogue and the stores. P2 operands stay in LDS (shared, read-only), P1 operands in
+// no barrier: a wave only ever waits for its own DMA. The next token's DMA is issued
+// once the last slot read of the current token has returned. P2 operands stay in LDS (shared, read-only), P1 operands in
 // registers. The code stores of a token are issued after the wait for the next token's
 // tile, so that wait never covers a just-issued store.
 template <int N1, int N2>
@@ -415,6 +414,14 @@ struct StreamCfg {
 };
 
 #define KQ_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Cache policy of the streaming accesses: every input byte is read once and every code
+// byte written once, so both go non-temporal ("nt"), which keeps them from displacing
+// each other in the caches (measured on MI355X: read 16 KiB + write 4 KiB per token
+// streams about 12% faster than with the default policy).
+constexpr int kCpolNT = 2;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0)
@@ -451,8 +458,13 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t tok, const u
 #pragma unroll
   for (int nt = 0; nt < N1 / 16; ++nt) {
     uint8_t *dst = crow + (nt * 16 + lr) * (N2 / 2) + g * (N2 / 8);
-    if constexpr (N2 == 128) *reinterpret_cast<uint4 *>(dst) = make_uint4(w[nt][0], w[nt][1], w[nt][2], w[nt][3]);
-    else *reinterpret_cast<uint2 *>(dst) = make_uint2(w[nt][0], w[nt][1]);
+    if constexpr (N2 == 128) {
+      const u32x4_t v = {w[nt][0], w[nt][1], w[nt][2], w[nt][3]};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
+    } else {
+      const u32x2_t v = {w[nt][0], w[nt][1]};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(dst));
+    }
   }
 }
 
@@ -489,14 +501,15 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 
   // DMA token `tok` into this wave's slot: chunk (mt, ks) of lane L lands at
   // slot + ((mt KS + ks) 64 + L) 16, exactly where the A-operand read expects it
+  const uint32_t lane_off = (uint32_t)(lr * N2 + g * 8);  // elements, fixed per lane
   auto dma_tile = [&](int64_t tok) {
-    const __bf16 *xt = X + tok * ldx + lr * N2 + g * 8;
+    const __bf16 *xt = X + tok * ldx;  // wave-uniform base
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        __builtin_amdgcn_global_load_lds(xt + mt * 16 * N2 + ks * 32,
-                                         KQ_LDS_PTR(slot + (mt * C::KS + ks) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(xt + (lane_off + (uint32_t)(mt * 16 * N2 + ks * 32)),
+                                         KQ_LDS_PTR(slot + (mt * C::KS + ks) * 1024), 16, 0, kCpolNT);
   };
 
   const int64_t stride = (int64_t)gridDim.x * C::WAVES;
@@ -513,75 +526,75 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
       store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
       if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
     }
-    // ---- stage 1: Z = V P2, A operands read from the slot one reduction step at a time ----
-    // Operands are fetched one MFMA group ahead: B (P2, from LDS) for the next column
-    // tile, and A (the token, from the slot) for the next reduction step.
-    f32x4 zacc[C::MT][C::NT];
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) zacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 a_cur[C::MT], a_nxt[C::MT];
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-      a_cur[mt] = *reinterpret_cast<const bf16x8 *>(slot + (mt * C::KS * 64 + lane) * 16);
-    bf16x8 b_cur = sp2[lane];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) {
-        const int nx = ks * C::NT + nt + 1;  // next (step, tile) in order
-        bf16x8 b_nxt = b_cur;
-        if (nx < C::KS * C::NT) b_nxt = sp2[nx * 64 + lane];
-        if (nt == 0 && ks + 1 < C::KS) {
-#pragma unroll
-          for (int mt = 0; mt < C::MT; ++mt)
-            a_nxt[mt] = *reinterpret_cast<const bf16x8 *>(slot + ((mt * C::KS + ks + 1) * 64 + lane) * 16);
-        }
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) zacc[mt][nt] = mfma(a_cur[mt], b_cur, zacc[mt][nt]);
-        b_cur = b_nxt;
-      }
-      if (ks + 1 < C::KS) {
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) a_cur[mt] = a_nxt[mt];
-      }
-    }
-    wait_and_fence<kWaitLgkm0>();  // every slot read has returned: the slot is free again
-    if (tok + stride < T) dma_tile(tok + stride);
-
-    // ---- stage 2: Y^T = Z^T P1 ----
-    // all of Z is converted to bf16 operands first, so that the fp32 stage-1
-    // accumulators are dead before the stage-2 accumulators come to life
-    bf16x8 za[C::KK][C::NT];
-#pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const bool pad = C::KHALF && kk == C::KK - 1;
-#pragma unroll
-      for (int m2 = 0; m2 < C::NT; ++m2)
-        za[kk][m2] = pack8(zacc[2 * kk][m2], pad ? zero : zacc[(2 * kk + 1) % C::MT][m2]);
-    }
+    // ---- stages 1 and 2 per half of the output columns ----
+    // A column tile of Y needs only the same column tile of Z, so each half runs stage 1
+    // (Z = V P2 for its columns) and stage 2 (Y^T = Z^T P1) on its own: only half of
+    // the stage-1 accumulators are ever live, which leaves registers to fetch operands
+    // ahead, and the first half's absmax overlaps the second half's MFMAs.
+    constexpr int NH = C::NT / 2;  // column tiles per half
     f32x4 yacc[C::NT][C::MT];
+    float pm[C::NT];
 #pragma unroll
-    for (int m2 = 0; m2 < C::NT; ++m2)
+    for (int h = 0; h < 2; ++h) {
+      f32x4 zacc[C::MT][NH];
 #pragma unroll
-      for (int nt = 0; nt < C::MT; ++nt) yacc[m2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk)
+        for (int nt = 0; nt < NH; ++nt) zacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < C::MT; ++nt)
+      for (int ks = 0; ks < C::KS; ++ks) {
+        bf16x8 av[C::MT], bv[NH];
 #pragma unroll
-        for (int m2 = 0; m2 < C::NT; ++m2) yacc[m2][nt] = mfma(za[kk][m2], p1r[kk][nt], yacc[m2][nt]);
+        for (int mt = 0; mt < C::MT; ++mt)
+          av[mt] = *reinterpret_cast<const bf16x8 *>(slot + ((mt * C::KS + ks) * 64 + lane) * 16);
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt) bv[nt] = sp2[(ks * C::NT + h * NH + nt) * 64 + lane];
+#pragma unroll
+        for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt) zacc[mt][nt] = mfma(av[mt], bv[nt], zacc[mt][nt]);
+      }
+      if (h == 1) {
+        wait_and_fence<kWaitLgkm0>();  // every slot read has returned: the slot is free again
+        if (tok + stride < T) dma_tile(tok + stride);
+      }
+      bf16x8 za[C::KK][NH];
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const bool pad = C::KHALF && kk == C::KK - 1;
+#pragma unroll
+        for (int m2 = 0; m2 < NH; ++m2)
+          za[kk][m2] = pack8(zacc[2 * kk][m2], pad ? zero : zacc[(2 * kk + 1) % C::MT][m2]);
+      }
+#pragma unroll
+      for (int m2 = 0; m2 < NH; ++m2)
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt) yacc[h * NH + m2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+          for (int m2 = 0; m2 < NH; ++m2)
+            yacc[h * NH + m2][nt] = mfma(za[kk][m2], p1r[kk][nt], yacc[h * NH + m2][nt]);
+      // partial absmax of this half (independent chains, one per column tile)
+#pragma unroll
+      for (int m2 = h * NH; m2 < (h + 1) * NH; ++m2) {
+        pm[m2] = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pm[m2] = fmaxf(pm[m2], fabsf(yacc[m2][nt][r]));
+      }
+    }
 
     // ---- epilogue: lane holds Y[16 nt + lr][LPL g + 4 m2 + r] ----
-    float m = 0.f;
 #pragma unroll
-    for (int m2 = 0; m2 < C::NT; ++m2)
+    for (int w = C::NT / 2; w >= 1; w /= 2)
 #pragma unroll
-      for (int nt = 0; nt < C::MT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[m2][nt][r]));
+      for (int i = 0; i < w; ++i) pm[i] = fmaxf(pm[i], pm[i + w]);
+    const float m = pm[0];
     // the absmax and the clamp decision are wave-uniform: broadcast them so that the
     // choice below is one scalar branch, not a per-lane select
     const float amax = wave_max_uniform(m);
