@@ -108,7 +108,7 @@ def main():
                     help="minimum total size of the rotated input+output buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--split", choices=["default", "reg1", "reg2", "cols", "deep", "stream", "generic"],
+    ap.add_argument("--split", choices=["default", "reg1", "reg2", "cols", "deep", "stream", "pair", "generic"],
                     default="default", help="work split of the fused kernel (default: the plan's)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
@@ -147,7 +147,7 @@ def main():
     c = torch.from_numpy(inp.c).to(dev) if inp.c is not None else None
     flags = {"default": 0, "reg1": B.KQ_FLAG_SPLIT_REG1, "reg2": B.KQ_FLAG_SPLIT_REG2,
              "cols": B.KQ_FLAG_SPLIT_COLS, "deep": B.KQ_FLAG_SPLIT_DEEP,
-             "stream": B.KQ_FLAG_SPLIT_STREAM,
+             "stream": B.KQ_FLAG_SPLIT_STREAM, "pair": B.KQ_FLAG_SPLIT_PAIR,
              "generic": B.KQ_FLAG_FORCE_GENERIC}[args.split]
     plan = B.Plan(dev_tensor(inp.P1), dev_tensor(inp.P2), c, inp.alpha, wl.scale_dtype, flags=flags)
     T, n = wl.T, wl.n

@@ -61,6 +61,9 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
                                     /* prefetched into registers                          */
 #define KQ_FLAG_SPLIT_STREAM 0x100u /* MFMA: one wave per token, next token prefetched   */
                                     /* into LDS by DMA (no per-channel scale)             */
+#define KQ_FLAG_SPLIT_PAIR 0x200u   /* MFMA: two waves per token (one column half each),  */
+                                    /* operands in registers, tokens double-buffered in   */
+                                    /* LDS by DMA (no per-channel scale)                  */
 
 /*
  * kq_choose_factors -- factor a hidden size for the Kronecker transform.

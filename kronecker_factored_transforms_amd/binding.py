@@ -21,6 +21,7 @@ KQ_FLAG_SPLIT_REG2 = 0x20
 KQ_FLAG_SPLIT_COLS = 0x40
 KQ_FLAG_SPLIT_DEEP = 0x80
 KQ_FLAG_SPLIT_STREAM = 0x100
+KQ_FLAG_SPLIT_PAIR = 0x200
 
 # every symbol declared in include/kq.h
 EXPORTS = (

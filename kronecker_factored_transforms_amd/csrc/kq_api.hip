@@ -111,7 +111,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   if (isnan(alpha)) return KQ_ERR_INVALID_ARG;
   const unsigned split_flags =
       flags & (KQ_FLAG_SPLIT_REG1 | KQ_FLAG_SPLIT_REG2 | KQ_FLAG_SPLIT_COLS | KQ_FLAG_SPLIT_DEEP |
-               KQ_FLAG_SPLIT_STREAM);
+               KQ_FLAG_SPLIT_STREAM | KQ_FLAG_SPLIT_PAIR);
   if (flags & ~(KQ_FLAG_FORCE_GENERIC | split_flags)) return KQ_ERR_INVALID_ARG;
   if ((split_flags & (split_flags - 1)) != 0) return KQ_ERR_INVALID_ARG;  // at most one
   if (split_flags && ((flags & KQ_FLAG_FORCE_GENERIC) || x_dtype != KQ_BF16))
@@ -121,6 +121,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
                     : split_flags == KQ_FLAG_SPLIT_COLS ? KQ_SPLIT_COLS
                     : split_flags == KQ_FLAG_SPLIT_DEEP ? KQ_SPLIT_DEEP
                     : split_flags == KQ_FLAG_SPLIT_STREAM ? KQ_SPLIT_STREAM
+                    : split_flags == KQ_FLAG_SPLIT_PAIR ? KQ_SPLIT_PAIR
                                                         : 0;
 
   // kernel choice (pure host logic, before any HIP call)

@@ -391,11 +391,14 @@ __global__ __launch_bounds__(kThreads, DEEP ? 1 : 2) void kq_reg_kernel(
 // Eight waves per workgroup (two per SIMD, one workgroup per CU). Each wave owns an LDS
 // slot of one token tile; while it computes token t, a global->LDS DMA
 // (global_load_lds_dwordx4: lane i's 16 bytes land at slot + 16 i) brings its next token
-// into the slot, already in the A-operand lane order, so the load costs no registers and
-// no barrier: a wave only ever waits for its own DMA. The next token's DMA is issued
-// once the last slot read of the current token has returned. P2 operands stay in LDS (shared, read-only), P1 operands in
-// registers. The code stores of a token are issued after the wait for the next token's
-// tile, so that wait never covers a just-issued store.
+// into the slot, so the load costs no registers and no barrier: a wave only ever waits
+// for its own DMA. Every DMA instruction reads 1 KiB of contiguous global memory (whole
+// rows of V); the 16-byte pieces of row R are permuted within the row (piece P stored
+// at position P ^ swz(R)), which makes the A-operand reads of a 16-row tile hit 16
+// different bank groups. The next token's DMA is issued as soon as stage 1 has read the
+// slot. P2 operands stay in LDS (shared, read-only), P1 operands in registers. The code
+// stores of a token are issued after the wait for the next token's tile, so that wait
+// never covers a just-issued store.
 template <int N1, int N2>
 struct StreamCfg {
   static_assert(N1 % 16 == 0 && N1 >= 16 && N1 <= 64, "stream kernel: n1 in {16, 32, 48, 64}");
@@ -411,6 +414,13 @@ struct StreamCfg {
   static constexpr int TILE = N1 * N2 * 2;      // bytes of one token
   static constexpr int P2_BYTES = N2 * N2 * 2;
   static_assert(P2_BYTES + WAVES * TILE <= 160 * 1024, "LDS budget");
+  static constexpr int RB = N2 * 2;             // bytes per row of V
+  static constexpr int PPR = RB / 16;           // 16-byte pieces per row
+  static constexpr int RPB = 256 / RB;          // rows per 256-byte bank row
+  static constexpr int RPI = 1024 / RB;         // rows per DMA instruction
+  static constexpr int LOADS = TILE / 1024;     // DMA instructions per token
+  // position permutation of row R's pieces (an xor, so its own inverse)
+  __device__ static constexpr int swz(int R) { return (R / RPB) % PPR; }
 };
 
 #define KQ_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
@@ -419,7 +429,6 @@ struct StreamCfg {
 // byte written once, so both go non-temporal ("nt"), which keeps them from displacing
 // each other in the caches (measured on MI355X: read 16 KiB + write 4 KiB per token
 // streams about 12% faster than with the default policy).
-constexpr int kCpolNT = 2;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -433,6 +442,32 @@ __device__ __forceinline__ void wait_and_fence() {
   __builtin_amdgcn_s_waitcnt(IMM);
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
+}
+
+// One global -> LDS DMA of 16 bytes per lane (global_load_lds_dwordx4, non-temporal):
+// lane i reads base + voff_i and its bytes land at lds_base + 16 i; base and lds_base
+// must be wave-uniform. Issued from inline asm on purpose: the compiler's wait insertion
+// cannot tell which LDS bytes a DMA writes, so for a builtin DMA it makes every later
+// LDS read wait for it, and with code stores in flight it turns that into a wait for all
+// vector-memory traffic (stores included). The kernels order their DMAs with explicit
+// s_waitcnt instead. m0 is saved and restored so that no value the compiler keeps there
+// is lost; the s_nop gives the m0 write and a VALU write of the base (readfirstlane)
+// the wait states a vector-memory read of them needs.
+__device__ __forceinline__ void dma16_nt(const void *base, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)KQ_LDS_PTR(p);
 }
 
 // Quantize a wave's whole Y tile (lane holds yacc[m2][nt] = 4 consecutive columns of row
@@ -499,17 +534,27 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
   const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
   unsigned char *slot = s_tile[wave];
 
-  // DMA token `tok` into this wave's slot: chunk (mt, ks) of lane L lands at
-  // slot + ((mt KS + ks) 64 + L) 16, exactly where the A-operand read expects it
-  const uint32_t lane_off = (uint32_t)(lr * N2 + g * 8);  // elements, fixed per lane
+  // DMA token `tok` into this wave's slot: instruction j fills slot bytes [1024 j, 1024 j
+  // + 1024) = rows [RPI j, RPI j + RPI); lane i lands at row R = RPI j + i / PPR, position
+  // i % PPR, so it reads piece (i % PPR) ^ swz(R) of that row.
+  // The lane's byte offset within instruction j's 1 KiB depends on j only through
+  // swz(R), which repeats every SWP instructions: SWP offsets per lane.
+  constexpr int SWP = C::PPR * C::RPB / C::RPI;  // swz period in instructions
+  static_assert(SWP >= 1 && C::LOADS % SWP == 0, "swizzle period");
+  uint32_t voff[SWP];
+  {
+    const int r0 = lane / C::PPR, pos0 = lane % C::PPR;
+#pragma unroll
+    for (int j = 0; j < SWP; ++j) {
+      const int R = j * C::RPI + r0;
+      voff[j] = (uint32_t)((r0 * N2 + ((pos0 ^ C::swz(R)) * 8)) * 2);
+    }
+  }
   auto dma_tile = [&](int64_t tok) {
-    const __bf16 *xt = X + tok * ldx;  // wave-uniform base
+    const unsigned char *xt = reinterpret_cast<const unsigned char *>(X + tok * ldx);
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        __builtin_amdgcn_global_load_lds(xt + (lane_off + (uint32_t)(mt * 16 * N2 + ks * 32)),
-                                         KQ_LDS_PTR(slot + (mt * C::KS + ks) * 1024), 16, 0, kCpolNT);
+    for (int j = 0; j < C::LOADS; ++j)  // swz(R + SWP RPI) == swz(R)
+      dma16_nt(xt + j * 1024, voff[j % SWP], lds_addr(slot + j * 1024));
   };
 
   const int64_t stride = (int64_t)gridDim.x * C::WAVES;
@@ -531,6 +576,8 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
     // (Z = V P2 for its columns) and stage 2 (Y^T = Z^T P1) on its own: only half of
     // the stage-1 accumulators are ever live, which leaves registers to fetch operands
     // ahead, and the first half's absmax overlaps the second half's MFMAs.
+    // A operand (mt, ks) of lane L: V[16 mt + lr][32 ks + 8 g + v], i.e. piece 4 ks + g
+    // of row 16 mt + lr.
     constexpr int NH = C::NT / 2;  // column tiles per half
     f32x4 yacc[C::NT][C::MT];
     float pm[C::NT];
@@ -543,10 +590,11 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
         for (int nt = 0; nt < NH; ++nt) zacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
+        const unsigned char *arow = slot + lr * C::RB + (((ks * 4 + g) ^ C::swz(lr)) * 16);
         bf16x8 av[C::MT], bv[NH];
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
-          av[mt] = *reinterpret_cast<const bf16x8 *>(slot + ((mt * C::KS + ks) * 64 + lane) * 16);
+        for (int mt = 0; mt < C::MT; ++mt)  // swz(16 mt + lr) == swz(lr)
+          av[mt] = *reinterpret_cast<const bf16x8 *>(arow + mt * 16 * C::RB);
 #pragma unroll
         for (int nt = 0; nt < NH; ++nt) bv[nt] = sp2[(ks * C::NT + h * NH + nt) * 64 + lane];
 #pragma unroll
@@ -619,6 +667,202 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
   if (pend_tok >= 0) {
     store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
     if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// pair kernel: a workgroup of two waves per token, each wave one half of the columns
+// ------------------------------------------------------------------------------------
+// A column half of Y needs only the same column half of Z (stage 2 mixes rows, not
+// columns), so wave h computes Z[:, half h] = V P2[:, half h] and Y[:, half h] = P1^T of
+// it with both operand sets resident in registers: P2's half (its stage-1 B operands)
+// and P1 (stage-2 B operands). Only V comes from LDS, read by both waves. The token tile
+// is double-buffered: each wave DMAs one half of a tile (whole 128-byte row pieces, in
+// the A-operand lane order) two tokens ahead. Two barriers per token, between the two
+// waves of the pair only: "tile landed" and "tile read + absmax half exchanged"; the
+// buffer is refilled right after the second one. Four pairs share a CU, one wave of two
+// pairs per SIMD, so the MFMA work of one pair overlaps the waits of another.
+template <int N1, int N2>
+struct PairCfg {
+  static_assert(N1 % 16 == 0 && N1 >= 16 && N1 <= 64, "pair kernel: n1 in {16, 32, 48, 64}");
+  static_assert(N2 == 64 || N2 == 128, "pair kernel: n2 in {64, 128}");
+  static constexpr int THREADS = 128;
+  static constexpr int MT = N1 / 16;            // row tiles of V / Z
+  static constexpr int CB = N2 / 2;             // output columns per wave
+  static constexpr int NH = CB / 16;            // column tiles per wave
+  static constexpr int KS = N2 / 32;            // stage-1 reduction steps
+  static constexpr int KK = (N1 + 31) / 32;     // stage-2 reduction steps
+  static constexpr bool KHALF = (N1 % 32) != 0;
+  static constexpr int LPL = CB / 4;            // consecutive output columns per lane and row
+  static constexpr int TILE = N1 * N2 * 2;      // bytes of one token
+  static constexpr int CHUNKS = MT * KS;        // 1 KiB DMA chunks per tile
+  static constexpr int HALF_LOADS = CHUNKS / 2; // DMA instructions per wave and tile
+  static_assert(CHUNKS % 2 == 0 && HALF_LOADS < 64, "vmcnt range");
+  static constexpr int kWaitHalf = 0x0F70 | (HALF_LOADS & 15) | ((HALF_LOADS >> 4) << 14);
+};
+
+template <int N1, int N2>
+__device__ __forceinline__ void store_codes_half(uint8_t *codes, int64_t tok, int wave,
+                                                 const uint32_t (*w)[N2 / 64], int lr, int g) {
+  using C = PairCfg<N1, N2>;
+  uint8_t *crow = codes + tok * (int64_t)(N1 * N2 / 2) + wave * (C::CB / 2) + g * (C::LPL / 2);
+#pragma unroll
+  for (int nt = 0; nt < C::MT; ++nt) {
+    uint8_t *dst = crow + (nt * 16 + lr) * (N2 / 2);
+    if constexpr (N2 == 128) {
+      const u32x2_t v = {w[nt][0], w[nt][1]};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(dst));
+    } else {
+      __builtin_nontemporal_store(w[nt][0], reinterpret_cast<uint32_t *>(dst));
+    }
+  }
+}
+
+template <int N1, int N2, bool YDBG>
+__global__ __launch_bounds__(128, 2) void kq_pair_kernel(
+    const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
+    const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
+    float clip, int scale_fp16, int clip_allows_no_clamp,
+    uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
+  using C = PairCfg<N1, N2>;
+  constexpr int n = N1 * N2;
+  __shared__ __align__(16) unsigned char s_tile[2][C::TILE];
+  __shared__ float s_max[2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // column half
+  const int g = lane >> 4;
+  const int lr = lane & 15;
+
+  bf16x8 p2r[C::KS][C::NH];  // stage-1 B operands of this wave's column half
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int a = 0; a < C::NH; ++a) p2r[ks][a] = p2op[((wave * C::KS + ks) * C::NH + a) * 64 + lane];
+  bf16x8 p1r[C::KK][C::MT];  // stage-2 B operands
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+    for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
+  wait_and_fence<kWaitVm0>();  // operands resident before the first DMA is counted
+
+  // this wave's half of token tok's tile into buffer b: chunk c = mt KS + ks (lane L's 16
+  // bytes of it at buffer + (c 64 + L) 16), for c in [wave HALF_LOADS, (wave+1) HALF_LOADS)
+  const uint32_t lane_off = (uint32_t)(lr * N2 + g * 8);  // elements, fixed per lane
+  auto dma_half = [&](int64_t tok, int b) {
+    const __bf16 *xt = X + tok * ldx;  // wave-uniform base
+#pragma unroll
+    for (int i = 0; i < C::HALF_LOADS; ++i) {
+      const int c = wave * C::HALF_LOADS + i;
+      const int mt = c / C::KS, ks = c % C::KS;
+      dma16_nt(xt + (mt * 16 * N2 + ks * 32), lane_off * 2, lds_addr(s_tile[b] + c * 1024));
+    }
+  };
+
+  const int64_t G = gridDim.x;
+  int64_t tok = blockIdx.x;
+  if (tok < T) dma_half(tok, 0);
+  if (tok + G < T) dma_half(tok + G, 1);
+
+  uint32_t pend[C::MT][C::NH / 2];  // codes of the previous token, stored one step late
+  TokenScale pend_s{0.f, (_Float16)0.f, 0.f};
+  int64_t pend_tok = -1;
+
+  for (int it = 0; tok < T; tok += G, ++it) {
+    const int b = it & 1;
+    // this wave's half of the tile has landed once at most the next tile's loads are in
+    // flight (loads complete in issue order); the barrier adds the partner's half
+    if (tok + G < T) wait_and_fence<C::kWaitHalf>();
+    else wait_and_fence<kWaitVm0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    if (pend_tok >= 0) {
+      store_codes_half<N1, N2>(codes, pend_tok, wave, pend, lr, g);
+      if (wave == 0 && lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
+    }
+    const unsigned char *tile = s_tile[b];
+
+    // ---- stage 1: Z[:, half] = V P2[:, half] ----
+    f32x4 zacc[C::MT][C::NH];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int a = 0; a < C::NH; ++a) zacc[mt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      bf16x8 av[C::MT];
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+        av[mt] = *reinterpret_cast<const bf16x8 *>(tile + ((mt * C::KS + ks) * 64 + lane) * 16);
+#pragma unroll
+      for (int a = 0; a < C::NH; ++a)
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) zacc[mt][a] = mfma(av[mt], p2r[ks][a], zacc[mt][a]);
+    }
+    // ---- stage 2: Y[:, half]^T = Z[:, half]^T P1 (Z rounded to bf16 as the A operand) ----
+    bf16x8 za[C::KK][C::NH];
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const bool pad = C::KHALF && kk == C::KK - 1;
+#pragma unroll
+      for (int m2 = 0; m2 < C::NH; ++m2)
+        za[kk][m2] = pack8(zacc[2 * kk][m2], pad ? zero : zacc[(2 * kk + 1) % C::MT][m2]);
+    }
+    f32x4 yacc[C::NH][C::MT];
+    float pm[C::NH];
+#pragma unroll
+    for (int m2 = 0; m2 < C::NH; ++m2) {
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) yacc[m2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt) yacc[m2][nt] = mfma(za[kk][m2], p1r[kk][nt], yacc[m2][nt]);
+      pm[m2] = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pm[m2] = fmaxf(pm[m2], fabsf(yacc[m2][nt][r]));
+    }
+
+    // ---- absmax over both halves; lane holds Y[16 nt + lr][CB wave + LPL g + 4 m2 + r] ----
+#pragma unroll
+    for (int w = C::NH / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) pm[i] = fmaxf(pm[i], pm[i + w]);
+    const float m = wave_max_uniform(pm[0]);
+    if (lane == 0) s_max[wave] = m;
+    wait_and_fence<kWaitLgkm0>();  // tile reads returned, own maximum written
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    const float amax = fmaxf(m, s_max[wave ^ 1]);
+    if (tok + 2 * G < T) dma_half(tok + 2 * G, b);  // both waves are done with buffer b
+
+    const TokenScale ts = token_scale(amax, clip, scale_fp16);
+    if (__builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, ts.s32) ? 1 : 0)) {
+      quant_tile<true, C::MT, C::NH>(yacc, ts.inv, pend);
+    } else {
+      quant_tile<false, C::MT, C::NH>(yacc, ts.inv, pend);
+    }
+    pend_s = ts;
+    pend_tok = tok;
+    if constexpr (YDBG) {
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) {
+        float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + (nt * 16 + lr) * N2 +
+                                                wave * C::CB + g * C::LPL);
+#pragma unroll
+        for (int m2 = 0; m2 < C::NH; ++m2)
+          yp[m2] = make_float4(yacc[m2][nt][0], yacc[m2][nt][1], yacc[m2][nt][2], yacc[m2][nt][3]);
+      }
+    }
+  }
+  if (pend_tok >= 0) {
+    store_codes_half<N1, N2>(codes, pend_tok, wave, pend, lr, g);
+    if (wave == 0 && lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
   }
 }
 
@@ -870,6 +1114,25 @@ hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx
   return hipGetLastError();
 }
 
+template <int N1, int N2>
+hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
+                       void *scales, float *y_debug, hipStream_t stream) {
+  using C = PairCfg<N1, N2>;
+  const int grid = (int)(T < (int64_t)p->grid_cap ? T : (int64_t)p->grid_cap);
+  auto k = y_debug ? &kq_pair_kernel<N1, N2, true> : &kq_pair_kernel<N1, N2, false>;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
+                     static_cast<const __bf16 *>(X), T, ldx,
+                     static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
+                     p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes,
+                     scales, y_debug);
+  return hipGetLastError();
+}
+
+#define KQ_PAIR(A, B)                                                                  \
+  kq_fused_variant{A, B, false, KQ_SPLIT_PAIR, (B) / 2, PairCfg<A, B>::THREADS,          \
+                   &launch_pair<A, B>,                                                 \
+                   reinterpret_cast<const void *>(&kq_pair_kernel<A, B, false>),       \
+                   "fused_mfma_bf16_pair_" #A "x" #B}
 #define KQ_STREAM(A, B)                                                                \
   kq_fused_variant{A, B, false, KQ_SPLIT_STREAM, (B), StreamCfg<A, B>::THREADS,          \
                    &launch_stream<A, B>,                                               \
@@ -918,6 +1181,8 @@ const kq_fused_variant kVariants[] = {
     KQ_DEEP(64, 128, false, ""), KQ_DEEP(64, 64, false, ""), KQ_DEEP(64, 64, true, "_c"),
     KQ_STREAM(16, 64), KQ_STREAM(32, 64), KQ_STREAM(48, 64), KQ_STREAM(64, 64),
     KQ_STREAM(16, 128), KQ_STREAM(32, 128), KQ_STREAM(48, 128),
+    KQ_PAIR(16, 64), KQ_PAIR(32, 64), KQ_PAIR(48, 64), KQ_PAIR(64, 64),
+    KQ_PAIR(16, 128), KQ_PAIR(32, 128), KQ_PAIR(48, 128), KQ_PAIR(64, 128),
 };
 
 }  // namespace

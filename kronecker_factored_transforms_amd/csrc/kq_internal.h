@@ -46,7 +46,7 @@ struct kq_plan {
 // column kernel (n2/32 waves per token, token staged in LDS), or the stream kernel (one
 // wave per token, next token prefetched into an LDS slot by DMA).
 enum { KQ_SPLIT_REG1 = 1, KQ_SPLIT_REG2 = 2, KQ_SPLIT_COLS = 3, KQ_SPLIT_DEEP = 4,
-       KQ_SPLIT_STREAM = 5 };
+       KQ_SPLIT_STREAM = 5, KQ_SPLIT_PAIR = 6 };
 
 struct kq_fused_variant {
   int n1, n2;

@@ -1,5 +1,6 @@
-"""Every fused work split (one or two waves per token with the token in registers, or the
-column kernel with the token in LDS) against the oracle, on shapes around the workloads:
+"""Every fused work split (one or two waves per token with the token in registers, the
+column kernel with the token in LDS, the DMA-fed stream and pair kernels) against the
+oracle, on shapes around the workloads:
 square and non-square factors, with and without the per-channel scale, ragged T."""
 from dataclasses import replace
 
@@ -12,7 +13,8 @@ from kronecker_factored_transforms_amd import synth as S
 pytestmark = pytest.mark.gpu
 
 SPLITS = {"reg1": B.KQ_FLAG_SPLIT_REG1, "reg2": B.KQ_FLAG_SPLIT_REG2, "cols": B.KQ_FLAG_SPLIT_COLS,
-          "deep": B.KQ_FLAG_SPLIT_DEEP, "stream": B.KQ_FLAG_SPLIT_STREAM}
+          "deep": B.KQ_FLAG_SPLIT_DEEP, "stream": B.KQ_FLAG_SPLIT_STREAM,
+          "pair": B.KQ_FLAG_SPLIT_PAIR}
 DEEP_SHAPES = {(64, 128, False), (64, 64, False), (64, 64, True)}
 SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (32, 128, False),
           (48, 128, True), (16, 64, True), (48, 64, False), (32, 32, True), (16, 32, False),
@@ -22,7 +24,7 @@ SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (3
 def _available(n1, n2, split, with_c=False):
     if split == "deep":
         return (n1, n2, with_c) in DEEP_SHAPES
-    if split == "stream":
+    if split in ("stream", "pair"):
         return n1 <= 64 and n2 >= 64 and not with_c
     if split == "reg1":
         return n1 <= 64
