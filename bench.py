@@ -3,14 +3,15 @@
 
 One step = one kq_transform_quant over one batch of synthetic tokens already resident in
 HBM (the whole hot path: load, optional channel scale, both contractions, absmax, clip,
-round, clamp, pack, store). Default workload: hidden size 8192 with factors 64 x 128,
+round, clamp, pack, store). The throughput (`value`, tokens/s) is timed over K
+back-to-back steps bracketed by device synchronizations; the kernel's average duration
+(for the roofline) is the span of HIP events recorded on the launch stream around the
+same K launches, divided by K. Default workload: hidden size 8192 with factors 64 x 128,
 16384 bf16 tokens (Student-t activations with outlier channels, orthogonal factors,
 clip logit 3).
 
 Prints ONE JSON line on stdout. Algorithmic work per token: 2*n*(n1+n2) FLOP and
-2.5*n bytes (bf16 in + packed int4 out; 4.5*n for fp32 input). The per-launch kernel
-time comes from HIP events recorded on the launch stream around every timed launch.
-Input/output buffer sets are rotated so that consecutive steps never hit data left in
+2.5*n bytes (bf16 in + packed int4 out; 4.5*n for fp32 input). Input/output buffer sets are rotated so that consecutive steps never hit data left in
 the 256 MB last-level (Infinity) cache.
 """
 from __future__ import annotations
@@ -82,19 +83,26 @@ def cpu_baseline(inp, seconds: float):
     run(inp.X[:k])
     dt = max(time.perf_counter() - t0, 1e-6)
     k = int(min(T, max(k, seconds / dt * k)))
+    # whole passes over the first k tokens until about `seconds` of wall time
+    passes, done = 0, 0
     w0, c0 = time.perf_counter(), os.times()
-    run(inp.X[:k])
+    while True:
+        run(inp.X[:k])
+        passes += 1
+        done += k
+        if time.perf_counter() - w0 >= seconds:
+            break
     w1, c1 = time.perf_counter(), os.times()
     wall = w1 - w0
     cpu = (c1.user - c0.user) + (c1.system - c0.system)
     return {
-        "value": k / wall,
+        "value": done / wall,
         "unit": "tokens/s",
         "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
-        "sample": (f"first {k} of {T} tokens of the same workload; float64 factored transform "
-                   f"(numpy.matmul) + fp32 quantizer + packing, one pass, {wall:.1f} s wall, "
-                   f"{cpu:.1f} s CPU; BLAS {blas}; host cpu_count {os.cpu_count()}"),
+        "sample": (f"first {k} of {T} tokens of the same workload, {passes} pass(es); float64 "
+                   f"factored transform (numpy.matmul) + fp32 quantizer + packing, {wall:.1f} s "
+                   f"wall, {cpu:.1f} s CPU; BLAS {blas}; host cpu_count {os.cpu_count()}"),
     }
 
 
@@ -102,7 +110,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="hidden_n8192")
     ap.add_argument("--rotate-mib", type=int, default=1536,
                     help="minimum total size of the rotated input+output buffer sets")
@@ -110,6 +118,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", choices=["default", "reg1", "reg2", "cols", "deep", "stream", "pair", "generic"],
                     default="default", help="work split of the fused kernel (default: the plan's)")
+    ap.add_argument("--per-launch-events", action="store_true",
+                    help="also time every launch with its own event pair (diagnostic)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -175,24 +185,42 @@ def main():
         codes, scales = outs[i % nsets]
         B.kq_transform_quant(handle, X, T, n, codes, scales, None, sh)
 
+    K = args.steps
+    # events are created before the warmup: creating them between the warmup and the
+    # timed region would leave the GPU idle for milliseconds, and the launches right
+    # after such a pause run measurably slower while the clocks ramp back up
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K if args.per_launch_events else 0)]
+    span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
+    # timed region 1: K back-to-back steps, bracketed by synchronizations (the throughput)
     t0 = time.perf_counter()
+    span[0].record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         step(i)
-        ev[i][1].record(stream)
+    span[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kernel_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = (t1 - t0) * 1e3 / K
-    k_avg_s = sum(kernel_ms) / K / 1e3
-    k_med_ms = sorted(kernel_ms)[K // 2]
+    gpu_span_ms = span[0].elapsed_time(span[1]) / K
+    # average launch duration: the HIP event span of the timed region on the launch stream
+    # over K back-to-back launches (each launch waits for the previous one)
+    k_avg_s = gpu_span_ms / 1e3
+    per_launch = None
+    if args.per_launch_events:
+        # diagnostic only: an event pair around every launch; the event packets add a few
+        # microseconds to each measured interval and space the launches apart
+        for i in range(K):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        kernel_ms = sorted(a.elapsed_time(b) for a, b in ev)
+        per_launch = {"mean_us": sum(kernel_ms) / K * 1e3, "median_us": kernel_ms[K // 2] * 1e3,
+                      "min_us": kernel_ms[0] * 1e3, "max_us": kernel_ms[-1] * 1e3}
 
     flop_tok = 2 * n * (wl.n1 + wl.n2)
     byte_tok = (esize + 0.5) * n
@@ -200,9 +228,9 @@ def main():
     achieved_gbs = T * byte_tok / k_avg_s / 1e9
     achieved_tflops = T * flop_tok / k_avg_s / 1e12
     traffic = traffic_from_profile(wl.name, plan.kernel)
-    log(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step wall, kernel avg "
-        f"{k_avg_s * 1e6:.2f} us (median {k_med_ms * 1e3:.2f} us): {achieved_gbs:.0f} GB/s, "
-        f"{achieved_tflops:.1f} TFLOP/s")
+    log(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step wall, {gpu_span_ms * 1e3:.2f} us/launch "
+        f"on the stream: {achieved_gbs:.0f} GB/s, {achieved_tflops:.1f} TFLOP/s"
+        + (f"; per-launch events: {per_launch}" if per_launch else ""))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -235,6 +263,7 @@ def main():
             "frac": achieved_gbs / PEAK_HBM_GBS,
             "traffic": traffic,
             "kernel_avg_us": k_avg_s * 1e6,
+            "kernel_avg_source": "HIP event span of the timed region on the launch stream / steps",
             "algorithmic_bytes_per_launch": T * byte_tok,
         },
         "mfma": {
