@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="hidden_n8192")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's token count (sweeps; the JSON names it)")
     ap.add_argument("--rotate-mib", type=int, default=1536,
                     help="minimum total size of the rotated input+output buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -144,7 +146,9 @@ def main():
     dev = torch.device("cuda:0")
     wl = S.WORKLOADS[args.workload]
     t_gen = time.perf_counter()
-    inp = S.make(wl)
+    inp = S.make(wl, T=args.tokens)
+    if args.tokens is not None:
+        wl = S.with_tokens(wl, args.tokens)
     log(f"[bench] generated {wl.name}: T={wl.T} n={wl.n} ({wl.n1}x{wl.n2}) {wl.dtype} "
         f"in {time.perf_counter() - t_gen:.1f}s")
 
@@ -169,7 +173,8 @@ def main():
              torch.empty((T,), dtype=plan.scale_dtype, device=dev)) for _ in range(nsets)]
     stream = torch.cuda.current_stream()
     handle, sh = plan.handle, int(stream.cuda_stream)
-    log(f"[bench] kernel={plan.kernel} clip={plan.clip:.6f} buffer sets={nsets} "
+    kname = plan.kernel_for(T)
+    log(f"[bench] kernel={kname} clip={plan.clip:.6f} buffer sets={nsets} "
         f"({nsets * set_bytes / 2**20:.0f} MiB)")
 
     if args.copy_probe:
@@ -227,7 +232,7 @@ def main():
     tokens_per_s = T / (ms_per_step / 1e3)
     achieved_gbs = T * byte_tok / k_avg_s / 1e9
     achieved_tflops = T * flop_tok / k_avg_s / 1e12
-    traffic = traffic_from_profile(wl.name, plan.kernel)
+    traffic = traffic_from_profile(wl.name, kname)
     log(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step wall, {gpu_span_ms * 1e3:.2f} us/launch "
         f"on the stream: {achieved_gbs:.0f} GB/s, {achieved_tflops:.1f} TFLOP/s"
         + (f"; per-launch events: {per_launch}" if per_launch else ""))
@@ -253,7 +258,7 @@ def main():
         "config": {
             "workload": wl.name, "T": T, "n": n, "n1": wl.n1, "n2": wl.n2, "x_dtype": wl.dtype,
             "scale_dtype": wl.scale_dtype, "per_channel_c": inp.c is not None,
-            "alpha": inp.alpha, "kernel": plan.kernel, "buffer_sets": nsets,
+            "alpha": inp.alpha, "kernel": kname, "buffer_sets": nsets,
         },
         "roofline": {
             "bound": "hbm",

@@ -127,8 +127,15 @@ kq_status kq_destroy(kq_plan *plan);
 /* The exact fp32 clip ratio the kernels use (0 for a NULL plan). */
 float kq_plan_clip_ratio(const kq_plan *plan);
 
-/* Name of the kernel variant the plan dispatches to (static string; "" for NULL). */
+/* Name of the kernel variant the plan dispatches to for large batches (static string;
+ * "" for NULL). */
 const char *kq_plan_kernel_name(const kq_plan *plan);
+
+/* Name of the kernel variant a kq_transform_quant of T tokens runs on this plan. A plan
+ * created without a KQ_FLAG_SPLIT_* flag may use a second work split for small batches
+ * (fewer than about four tokens per compute unit), which spreads each token over more
+ * waves; both compute the same Y and codes. "" for NULL. */
+const char *kq_plan_kernel_name_for(const kq_plan *plan, int64_t T);
 
 /* Static, human-readable description of a status code. */
 const char *kq_status_string(kq_status s);

@@ -26,7 +26,8 @@ KQ_FLAG_SPLIT_PAIR = 0x200
 # every symbol declared in include/kq.h
 EXPORTS = (
     "kq_choose_factors", "kq_create", "kq_create_ex", "kq_transform_quant", "kq_destroy",
-    "kq_plan_clip_ratio", "kq_plan_kernel_name", "kq_status_string", "kq_version",
+    "kq_plan_clip_ratio", "kq_plan_kernel_name", "kq_plan_kernel_name_for", "kq_status_string",
+    "kq_version",
 )
 
 _lib = None
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.kq_plan_clip_ratio.restype = ctypes.c_float
     L.kq_plan_kernel_name.argtypes = [vp]
     L.kq_plan_kernel_name.restype = ctypes.c_char_p
+    L.kq_plan_kernel_name_for.argtypes = [vp, i64]
+    L.kq_plan_kernel_name_for.restype = ctypes.c_char_p
     L.kq_status_string.argtypes = [i32]
     L.kq_status_string.restype = ctypes.c_char_p
     L.kq_version.argtypes = []
@@ -144,6 +147,10 @@ def kq_plan_kernel_name(plan) -> str:
     return lib().kq_plan_kernel_name(plan).decode()
 
 
+def kq_plan_kernel_name_for(plan, T: int) -> str:
+    return lib().kq_plan_kernel_name_for(plan, int(T)).decode()
+
+
 # ------------------------------------------------------------------------------------
 class Plan:
     """Convenience wrapper: Plan(P1, P2, c, alpha)(X) -> (codes, scales[, y]).
@@ -186,6 +193,10 @@ class Plan:
         y = torch.empty((T, self.n), dtype=torch.float32, device=X.device) if y_debug else None
         kq_transform_quant(self.handle, X, T, X.stride(0) if T else self.n, codes, scales, y, stream)
         return (codes, scales, y) if y_debug else (codes, scales)
+
+    def kernel_for(self, T: int) -> str:
+        """Name of the kernel a call with T tokens runs."""
+        return kq_plan_kernel_name_for(self.handle, T)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -520,18 +520,6 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
   const int g = lane >> 4;
   const int lr = lane & 15;
 
-  {
-    const uint4 *src = reinterpret_cast<const uint4 *>(p2op);
-    uint4 *dst = reinterpret_cast<uint4 *>(s_p2);
-    for (int i = tid; i < C::P2_BYTES / 16; i += C::THREADS) dst[i] = src[i];
-  }
-  bf16x8 p1r[C::KK][C::MT];  // stage-2 B operands, resident
-#pragma unroll
-  for (int kk = 0; kk < C::KK; ++kk)
-#pragma unroll
-    for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
-  __syncthreads();
-  const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
   unsigned char *slot = s_tile[wave];
 
   // DMA token `tok` into this wave's slot: instruction j fills slot bytes [1024 j, 1024 j
@@ -559,7 +547,20 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 
   const int64_t stride = (int64_t)gridDim.x * C::WAVES;
   int64_t tok = (int64_t)blockIdx.x * C::WAVES + wave;
-  if (tok < T) dma_tile(tok);
+  if (tok < T) dma_tile(tok);  // first, so that it overlaps the factor loads below
+
+  {
+    const uint4 *src = reinterpret_cast<const uint4 *>(p2op);
+    uint4 *dst = reinterpret_cast<uint4 *>(s_p2);
+    for (int i = tid; i < C::P2_BYTES / 16; i += C::THREADS) dst[i] = src[i];
+  }
+  bf16x8 p1r[C::KK][C::MT];  // stage-2 B operands, resident
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+    for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
+  __syncthreads();  // P2 visible (this also waits for every load issued so far)
+  const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
 
   uint32_t pend[C::MT][C::NT / 2];  // codes of the previous token, stored one step late
   TokenScale pend_s{0.f, (_Float16)0.f, 0.f};
@@ -734,17 +735,6 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
   const int g = lane >> 4;
   const int lr = lane & 15;
 
-  bf16x8 p2r[C::KS][C::NH];  // stage-1 B operands of this wave's column half
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-    for (int a = 0; a < C::NH; ++a) p2r[ks][a] = p2op[((wave * C::KS + ks) * C::NH + a) * 64 + lane];
-  bf16x8 p1r[C::KK][C::MT];  // stage-2 B operands
-#pragma unroll
-  for (int kk = 0; kk < C::KK; ++kk)
-#pragma unroll
-    for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
-  wait_and_fence<kWaitVm0>();  // operands resident before the first DMA is counted
 
   // this wave's half of token tok's tile into buffer b: chunk c = mt KS + ks (lane L's 16
   // bytes of it at buffer + (c 64 + L) 16), for c in [wave HALF_LOADS, (wave+1) HALF_LOADS)
@@ -761,7 +751,21 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
 
   const int64_t G = gridDim.x;
   int64_t tok = blockIdx.x;
-  if (tok < T) dma_half(tok, 0);
+  if (tok < T) dma_half(tok, 0);  // first, so that it overlaps the operand loads below
+
+  bf16x8 p2r[C::KS][C::NH];  // stage-1 B operands of this wave's column half
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int a = 0; a < C::NH; ++a) p2r[ks][a] = p2op[((wave * C::KS + ks) * C::NH + a) * 64 + lane];
+  bf16x8 p1r[C::KK][C::MT];  // stage-2 B operands
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+    for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
+  // operands resident (and the first tile landed) before any later DMA is counted: the
+  // compiler's own waits for these loads know nothing of the DMAs
+  wait_and_fence<kWaitVm0>();
   if (tok + G < T) dma_half(tok + G, 1);
 
   uint32_t pend[C::MT][C::NH / 2];  // codes of the previous token, stored one step late

@@ -38,6 +38,13 @@ struct kq_plan {
   float *p2f;
   // per-channel scale (fp32, n) or nullptr
   float *c;
+  // small-batch variant of the fused family, used when T < small_max_T: it spreads each
+  // token over more waves (a different P2 operand layout, hence its own copy)
+  kq_launch_fn small_launch;
+  const char *small_kname;
+  void *small_p2op;
+  int small_grid_cap;
+  int64_t small_max_T;
 };
 
 // ---- fused MFMA family (kq_fused.hip) ----

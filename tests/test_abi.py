@@ -115,4 +115,5 @@ def test_null_plan_paths(L):
     assert L.kq_destroy(None) == B.KQ_OK
     assert L.kq_plan_clip_ratio(None) == 0.0
     assert L.kq_plan_kernel_name(None) == b""
+    assert L.kq_plan_kernel_name_for(None, 5) == b""
     assert L.kq_transform_quant(None, None, 0, 0, None, None, None, None) == B.KQ_ERR_INVALID_ARG

@@ -185,3 +185,31 @@ def test_repeated_runs_are_identical(gpu):
     for _ in range(3):
         out = K.run(plan, X)
         assert all(torch.equal(a, b) for a, b in zip(ref, out))
+
+
+def test_small_batches_switch_to_the_pair_split(gpu):
+    """A default 64x128 plan runs the pair split (two waves per token) below a token
+    count and the stream split (one wave per token) from there on; both sides of the
+    switch match the oracle and the debug-free launch."""
+    inp = S.make("hidden_n8192", T=8)
+    plan, _ = K.make_plan(inp)
+    assert plan.kernel.startswith("fused_mfma_bf16_stream_"), plan.kernel
+    assert plan.kernel_for(1).startswith("fused_mfma_bf16_pair_")
+    assert plan.kernel_for(1 << 20) == plan.kernel
+    lo, hi = 1, 1 << 20  # smallest T that runs the stream split
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if plan.kernel_for(mid) == plan.kernel:
+            hi = mid
+        else:
+            lo = mid + 1
+    print(f"[switch] stream from T={lo}", flush=True)
+    for T in (lo - 1, lo):
+        inp = S.make("hidden_n8192", T=T)
+        plan, X = K.make_plan(inp)
+        import torch
+        codes, scales, y = K.run(plan, X, y_debug=True)
+        codes2, scales2 = K.run(plan, X, y_debug=False)
+        assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
+        K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(),
+                               plan.clip)
