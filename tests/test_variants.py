@@ -24,7 +24,9 @@ SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (3
 def _available(n1, n2, split, with_c=False):
     if split == "deep":
         return (n1, n2, with_c) in DEEP_SHAPES
-    if split in ("stream", "pair"):
+    if split == "stream":
+        return n1 <= 64 and n2 >= 64 and (not with_c or n2 == 64)
+    if split == "pair":
         return n1 <= 64 and n2 >= 64 and not with_c
     if split == "reg1":
         return n1 <= 64
