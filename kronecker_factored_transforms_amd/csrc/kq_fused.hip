@@ -176,10 +176,10 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
 }
 
 __device__ __forceinline__ void copy_to_lds(unsigned char *dst, const void *src, int bytes,
-                                            int tid) {
+                                            int tid, int nthreads = kThreads) {
   const uint4 *s = reinterpret_cast<const uint4 *>(src);
   uint4 *d = reinterpret_cast<uint4 *>(dst);
-  for (int i = tid; i < bytes / 16; i += kThreads) d[i] = s[i];
+  for (int i = tid; i < bytes / 16; i += nthreads) d[i] = s[i];
 }
 
 // ------------------------------------------------------------------------------------
@@ -905,36 +905,51 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
 // ------------------------------------------------------------------------------------
 // column kernel: W = n2/32 waves per token
 // ------------------------------------------------------------------------------------
+// Waves per workgroup of the column kernel: one per 32 output columns of a token, at
+// least four (then several tokens share a workgroup).
+constexpr int cols_waves(int n2) { return n2 / 32 > kWaves ? n2 / 32 : kWaves; }
+
 template <int N1, int N2, bool HAS_C>
 struct ColsCfg {
   static_assert(N1 % 16 == 0 && N1 >= 16 && N1 <= 128, "n1 must be a multiple of 16 up to 128");
-  static_assert(N2 == 32 || N2 == 64 || N2 == 128, "n2 must be 32, 64 or 128");
+  static_assert(N2 % 32 == 0 && N2 >= 32 && N2 <= 256, "n2 must be a multiple of 32 up to 256");
   static constexpr int W = N2 / 32;                 // waves per token
-  static constexpr int TPI = kWaves / W;            // tokens per workgroup iteration
+  static constexpr int WAVES = cols_waves(N2);      // waves per workgroup
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int TPI = WAVES / W;             // tokens per workgroup iteration
   static constexpr int MT = N1 / 16;                // 16-row tiles of V / Z
   static constexpr int KS = N2 / 32;                // stage-1 reduction steps
   static constexpr int KK = (N1 + 31) / 32;         // stage-2 reduction steps of 32
   static constexpr bool KHALF = (N1 % 32) != 0;     // last step holds 16 rows + 16 zeros
   static constexpr int CH = N2 / 8;                 // 16-byte chunks per V row
+  // row layout in LDS: an XOR swizzle of the chunks when CH is a power of two, else rows
+  // padded by one chunk; either way the 16 rows of one A-operand read hit 16 different
+  // bank groups
+  static constexpr bool POW2 = (CH & (CH - 1)) == 0;
+  static constexpr int ROW_CHUNKS = POW2 ? CH : CH + 1;
   static constexpr int TOK_CHUNKS = N1 * CH;
-  static constexpr int CPT = TPI * TOK_CHUNKS / kThreads;  // chunks per thread per iter
-  static_assert(CPT * kThreads == TPI * TOK_CHUNKS, "token tile must split evenly");
-  static constexpr int V_BYTES = N1 * N2 * 2;
-  static constexpr int P2_BYTES = N2 * N2 * 2;
+  static constexpr int CPT = TPI * TOK_CHUNKS / THREADS;  // chunks per thread per iter
+  static_assert(CPT * THREADS == TPI * TOK_CHUNKS, "token tile must split evenly");
+  static constexpr int V_BYTES = N1 * ROW_CHUNKS * 16;
+  // P2 operands: shared in LDS while they fit, else read from the plan's copy in global
+  // memory, which stays in the L2 caches
+  static constexpr bool P2_LDS = N2 <= 128;
+  static constexpr int P2_BYTES = P2_LDS ? N2 * N2 * 2 : 16;
   static constexpr int P1_BYTES = KK * MT * 1024;   // n1 x n1 bf16, zero-padded to 32-steps
   static constexpr int VPLANES = HAS_C ? 2 : 1;     // hi (+ lo) bf16 planes of x*c
+  static_assert(!HAS_C || P2_LDS, "column kernel with c: n2 <= 128");
   static constexpr int VBUF = TPI * V_BYTES * VPLANES;
 };
 
-// byte offset of 16-byte chunk `cc` of row `r` of a token tile in LDS (XOR swizzle so
-// that the 16 rows read by one A-operand load land in distinct banks)
+// byte offset of 16-byte chunk `cc` of row `r` of a token tile in LDS
 template <int CH>
 __device__ __forceinline__ int vchunk_off(int r, int cc) {
-  return (r * CH + (cc ^ (r & (CH - 1)))) * 16;
+  if constexpr ((CH & (CH - 1)) == 0) return (r * CH + (cc ^ (r & (CH - 1)))) * 16;
+  else return (r * (CH + 1) + cc) * 16;
 }
 
 template <int N1, int N2, bool HAS_C>
-__global__ __launch_bounds__(kThreads) void kq_cols_kernel(
+__global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
     const float *__restrict__ cvec, float clip, int scale_fp16,
@@ -944,7 +959,7 @@ __global__ __launch_bounds__(kThreads) void kq_cols_kernel(
   __shared__ __align__(16) unsigned char s_p2[C::P2_BYTES];
   __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
   __shared__ __align__(16) unsigned char s_v[C::VBUF];
-  __shared__ float s_red[kWaves];
+  __shared__ float s_red[C::WAVES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -955,14 +970,14 @@ __global__ __launch_bounds__(kThreads) void kq_cols_kernel(
   const int wt = wave % C::W;  // column block of this wave
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
 
-  copy_to_lds(s_p2, p2op, C::P2_BYTES, tid);
-  copy_to_lds(s_p1, p1op, C::P1_BYTES, tid);
+  if constexpr (C::P2_LDS) copy_to_lds(s_p2, p2op, C::P2_BYTES, tid, C::THREADS);
+  copy_to_lds(s_p1, p1op, C::P1_BYTES, tid, C::THREADS);
 
   // per-thread chunk coordinates (fixed for the whole kernel)
   int c_ts[C::CPT], c_row[C::CPT], c_cc[C::CPT];
 #pragma unroll
   for (int i = 0; i < C::CPT; ++i) {
-    const int q = tid + kThreads * i;
+    const int q = tid + C::THREADS * i;
     c_ts[i] = q / C::TOK_CHUNKS;
     const int qq = q % C::TOK_CHUNKS;
     c_row[i] = qq / C::CH;
@@ -1028,10 +1043,17 @@ __global__ __launch_bounds__(kThreads) void kq_cols_kernel(
     f32x4 zacc[C::MT][2];
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) zacc[mt][0] = zacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+    // (large n2: a rolled loop, so that only one step's operands are in registers)
+#pragma unroll(C::P2_LDS ? C::KS : 1)
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 b0 = sp2[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
-      const bf16x8 b1 = sp2[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
+      bf16x8 b0, b1;
+      if constexpr (C::P2_LDS) {
+        b0 = sp2[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
+        b1 = sp2[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
+      } else {  // from the plan's copy in global memory (L2-resident, shared by all CUs)
+        b0 = p2op[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
+        b1 = p2op[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
+      }
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
         const int off = vchunk_off<C::CH>(mt * 16 + lr, ks * 4 + g);
@@ -1126,7 +1148,7 @@ hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
   using C = ColsCfg<N1, N2, HAS_C>;
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
-  hipLaunchKernelGGL((kq_cols_kernel<N1, N2, HAS_C>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((kq_cols_kernel<N1, N2, HAS_C>), dim3(grid), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
                      p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
@@ -1188,7 +1210,7 @@ hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
                    reinterpret_cast<const void *>(&kq_reg_kernel<A, B, 1, HC, true>),   \
                    "fused_mfma_bf16_deep_" #A "x" #B SUF}
 #define KQ_COLS(A, B, HC, SUF)                                                         \
-  kq_fused_variant{A, B, HC, KQ_SPLIT_COLS, 32, kThreads, &launch_cols<A, B, HC>,       \
+  kq_fused_variant{A, B, HC, KQ_SPLIT_COLS, 32, ColsCfg<A, B, HC>::THREADS, &launch_cols<A, B, HC>, \
                    reinterpret_cast<const void *>(&kq_cols_kernel<A, B, HC>),          \
                    "fused_mfma_bf16_cols_" #A "x" #B SUF}
 #define KQ_ALL1(A, B)                                                                  \
@@ -1219,6 +1241,9 @@ const kq_fused_variant kVariants[] = {
     KQ_COLS(96, 128, false, ""),   KQ_COLS(96, 128, true, "_c"),
     KQ_COLS(112, 128, false, ""),  KQ_COLS(112, 128, true, "_c"),
     KQ_COLS(128, 128, false, ""),  KQ_COLS(128, 128, true, "_c"),
+    // hidden sizes whose larger factor exceeds 128 (e.g. 28672 -> 128 x 224)
+    KQ_COLS(128, 160, false, ""),  KQ_COLS(128, 192, false, ""),
+    KQ_COLS(128, 224, false, ""),  KQ_COLS(128, 256, false, ""),
     // the other splits, selectable with KQ_FLAG_SPLIT_*
     KQ_ALL1(16, 32), KQ_ALL1(32, 32), KQ_ALL(16, 64), KQ_ALL(32, 64), KQ_ALL(48, 64),
     KQ_ALL(64, 64), KQ_ALL(16, 128), KQ_ALL(32, 128), KQ_ALL(48, 128), KQ_ALL(64, 128),

@@ -88,6 +88,10 @@ WORKLOADS = {
         "prefill_n8192_t65536", 5, T=65536, n1=64, n2=128, dtype="bf16",
         x_kind="student_t3", n_outliers=8, outlier_scale=30.0, p_kind="orthogonal",
         alpha=3.0),
+    # a larger factor than 128: the 70B-class FFN down-projection input, 28672 = 128 x 224
+    "down_proj_n28672": Workload(
+        "down_proj_n28672", 6, T=4096, n1=128, n2=224, dtype="bf16", x_kind="silu_gate",
+        p_kind="orthogonal", alpha=3.0),
 }
 
 

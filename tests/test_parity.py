@@ -32,6 +32,7 @@ SMALL = [
     ("down_proj_n14336", 301),
     ("decode_n8192_t64", 64),
     ("prefill_n8192_t65536", 777),
+    ("down_proj_n28672", 203),
 ]
 
 
@@ -49,7 +50,7 @@ def test_parity_against_full_oracle(gpu, name, T):
 
 
 FULL = ["attn_n4096", "hidden_n8192", "down_proj_n14336", "decode_n8192_t64",
-        "prefill_n8192_t65536"]
+        "prefill_n8192_t65536", "down_proj_n28672"]
 
 
 @pytest.mark.parametrize("name", FULL)

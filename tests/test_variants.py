@@ -18,10 +18,13 @@ SPLITS = {"reg1": B.KQ_FLAG_SPLIT_REG1, "reg2": B.KQ_FLAG_SPLIT_REG2, "cols": B.
 DEEP_SHAPES = {(64, 128, False), (64, 64, False), (64, 64, True)}
 SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (32, 128, False),
           (48, 128, True), (16, 64, True), (48, 64, False), (32, 32, True), (16, 32, False),
-          (112, 128, False), (112, 128, True), (96, 128, False), (128, 128, True), (80, 128, False)]
+          (112, 128, False), (112, 128, True), (96, 128, False), (128, 128, True), (80, 128, False),
+          (128, 160, False), (128, 224, False), (128, 256, False), (128, 224, True)]
 
 
 def _available(n1, n2, split, with_c=False):
+    if n2 > 128:  # only the column kernel, without c (P2 operands read from L2)
+        return split == "cols" and not with_c
     if split == "deep":
         return (n1, n2, with_c) in DEEP_SHAPES
     if split == "stream":
