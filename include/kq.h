@@ -94,6 +94,14 @@ kq_status kq_create(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype sc
                     const void *P1, const void *P2, const float *c, float alpha,
                     void *stream);
 
+/* Shapes with a kernel (anything else: KQ_ERR_UNSUPPORTED from kq_create):
+ *   bf16, bf16 MFMA kernels, with or without c: n2 = 32 with n1 in {16, 32}; n2 = 64
+ *     with n1 in {16, 32, 48, 64}; n2 = 128 with n1 in {16, 32, ..., 128}. Without c
+ *     also n1 = 128 with n2 in {160, 192, 224, 256} (hidden sizes 20480 ... 32768, e.g.
+ *     28672 = 128 x 224).
+ *   fp32 (and bf16 shapes not listed above): the generic fp32 kernel, n <= 16384.
+ */
+
 /* kq_create with flags (KQ_FLAG_*); kq_create(...) == kq_create_ex(..., 0). */
 kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
                        kq_dtype scale_dtype, const void *P1, const void *P2,
