@@ -68,6 +68,8 @@ __all__ = [
     "inverse_transform",
     "clip_ratio",
     "quantize_per_token",
+    "weight_factors",
+    "int4_gemm",
     "pack_int4",
     "unpack_int4",
     "dequantize",
@@ -325,3 +327,52 @@ def transform_quant(X, P1, P2, c, alpha, dtype, scale_dtype="fp16"):
     Y = transform(X, P1, P2, c, dtype)
     q, s = quantize_per_token(Y.astype(np.float32), clip_ratio(alpha), scale_dtype)
     return Y, pack_int4(q), s
+
+
+# ----------------------------------------------------------------------------------------
+# Weight side and the INT4 consumer
+def weight_factors(P1, P2):
+    """Factors that transform the rows of a weight matrix W [N x n] so that the INT4 product
+    of the two transformed sides reproduces X W^T.
+
+    [FQ Learning the affine transformation]: the layer computes (X P)(P^-1 W^T); with
+    [FQ Kronecker factorization] P = P1 (x) P2 and P^-1 = P1^-1 (x) P2^-1. Row j of
+    (P^-1 W^T)^T = W P^-T is w_j (P1^-T (x) P2^-T) ([KP] Definition: (A (x) B)^T =
+    A^T (x) B^T), i.e. the same transform as a token with factors P1^-T and P2^-T.
+    float64 inputs and outputs.
+    """
+    P1 = np.asarray(P1, dtype=np.float64)
+    P2 = np.asarray(P2, dtype=np.float64)
+    return np.linalg.inv(P1).T, np.linalg.inv(P2).T
+
+
+def _f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def int4_gemm(codes_x, scales_x, codes_w, scales_w, out_dtype: str = "fp32"):
+    """The INT4 x INT4 product of two quantized operands with their per-row steps.
+
+    acc[t, j] = sum_k qx[t, k] qw[j, k] exactly (integers), then in fp32, one rounding per
+    step: out = fp32(fp32(acc) * sx[t]) * sw[j]; stored as fp32, or rounded to nearest
+    even into bf16 (bit patterns, uint16) or fp16. [FQ Putting It Together]: the codes and
+    steps of both sides feed an INT4 GEMM; [HR Technical Summary]: the product of two
+    absmax-quantized matrices is the integer product times the two scale vectors.
+    """
+    qx = unpack_int4(codes_x).astype(np.int64)
+    qw = unpack_int4(codes_w).astype(np.int64)
+    acc = qx @ qw.T
+    sx = np.asarray(scales_x).astype(np.float32)
+    sw = np.asarray(scales_w).astype(np.float32)
+    out = (acc.astype(np.float32) * sx[:, None]).astype(np.float32)
+    out = (out * sw[None, :]).astype(np.float32)
+    if out_dtype == "fp32":
+        return out
+    if out_dtype == "bf16":
+        return _f32_to_bf16_bits(out)
+    if out_dtype == "fp16":
+        return out.astype(np.float16)
+    raise ValueError(out_dtype)

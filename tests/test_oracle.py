@@ -341,3 +341,100 @@ def test_full_path_identity_factors_match_library_quantizer():
     assert np.array_equal(Y, X.astype(np.float64))
     for t in range(T):
         assert np.array_equal(codes[t], _torch_quint4x2_bytes(X[t], 2.0 ** t) ^ np.uint8(0x88))
+
+
+# ---- weight side and the INT4 consumer ------------------------------------------------
+def _rand_codes(rng, rows, k):
+    return O.pack_int4(rng.integers(-8, 8, size=(rows, k)).astype(np.int8))
+
+
+def test_int4_gemm_matches_dequantized_float_product():
+    """The integer route equals dequantize-then-multiply (library float64 matmul) up to
+    the two fp32 roundings of the epilogue."""
+    rng = np.random.default_rng(11)
+    cx, cw = _rand_codes(rng, 7, 96), _rand_codes(rng, 9, 96)
+    sx = rng.uniform(0.01, 2, 7).astype(np.float16)
+    sw = rng.uniform(0.01, 2, 9).astype(np.float16)
+    out = O.int4_gemm(cx, sx, cw, sw)
+    ref = O.dequantize(cx, sx) @ O.dequantize(cw, sw).T
+    assert out.dtype == np.float32
+    np.testing.assert_allclose(out, ref, rtol=2.5e-7, atol=0)
+
+
+def test_int4_gemm_unit_scales_give_the_integer_product():
+    rng = np.random.default_rng(12)
+    qx = rng.integers(-8, 8, size=(5, 64))
+    qw = rng.integers(-8, 8, size=(3, 64))
+    out = O.int4_gemm(O.pack_int4(qx.astype(np.int8)), np.ones(5, np.float16),
+                      O.pack_int4(qw.astype(np.int8)), np.ones(3, np.float16))
+    # an independent sum: element by element in Python integers
+    for t in range(5):
+        for j in range(3):
+            assert out[t, j] == float(sum(int(a) * int(b) for a, b in zip(qx[t], qw[j])))
+
+
+def test_int4_gemm_bf16_output_rounds_like_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(13)
+    cx, cw = _rand_codes(rng, 6, 64), _rand_codes(rng, 8, 64)
+    sx = rng.uniform(0.001, 3, 6).astype(np.float32)
+    sw = rng.uniform(0.001, 3, 8).astype(np.float32)
+    f32 = O.int4_gemm(cx, sx, cw, sw, "fp32")
+    bits = O.int4_gemm(cx, sx, cw, sw, "bf16")
+    ref = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, ref)
+    assert np.array_equal(O.int4_gemm(cx, sx, cw, sw, "fp16"), f32.astype(np.float16))
+
+
+def test_weight_side_factors_reproduce_the_layer_product():
+    """(X P)(P^-1 W^T) = X W^T with non-symmetric, non-orthogonal factors: a transposed or
+    non-inverted factor fails this."""
+    rng = np.random.default_rng(14)
+    n1, n2 = 3, 5
+    P1 = np.eye(n1) + 0.3 * rng.standard_normal((n1, n1))
+    P2 = np.eye(n2) + 0.3 * rng.standard_normal((n2, n2))
+    X = rng.standard_normal((4, n1 * n2))
+    W = rng.standard_normal((6, n1 * n2))
+    Q1, Q2 = O.weight_factors(P1, P2)
+    XP = O.transform(X, P1, P2)
+    WPinvT = O.transform(W, Q1, Q2)
+    np.testing.assert_allclose(XP @ WPinvT.T, X @ W.T, rtol=1e-10, atol=1e-10)
+    # with the dense Kronecker product written out: W P^-T
+    Pd = O.kron_library(P1, P2)
+    np.testing.assert_allclose(WPinvT, W @ np.linalg.inv(Pd).T, rtol=1e-10, atol=1e-10)
+
+
+def test_orthogonal_kronecker_transform_lowers_int4_gemm_error_on_outliers():
+    """End to end on the CPU: Q(X P) Q(P^-1 W^T) approximates X W^T better than Q(X) Q(W^T)
+    when X has outlier channels ("FlatQuant" page, The flatness target)."""
+    rng = np.random.default_rng(15)
+    n1, n2, T, N = 16, 32, 64, 48
+    n = n1 * n2
+    X = rng.standard_normal((T, n))
+    X[:, rng.choice(n, 6, replace=False)] *= 40.0
+    W = rng.standard_normal((N, n)) / np.sqrt(n)
+
+    def qmm(Xt, Wt):
+        qx, sx = O.quantize_per_token(Xt.astype(np.float32), np.float32(1.0), "fp32")
+        qw, sw = O.quantize_per_token(Wt.astype(np.float32), np.float32(1.0), "fp32")
+        return O.int4_gemm(O.pack_int4(qx), sx, O.pack_int4(qw), sw).astype(np.float64)
+
+    def orth(m):
+        q, r = np.linalg.qr(rng.standard_normal((m, m)))
+        return q * np.sign(np.diag(r))
+
+    P1, P2 = orth(n1), orth(n2)
+    ref = X @ W.T
+    rel = lambda Y: np.linalg.norm(Y - ref) / np.linalg.norm(ref)
+    Q1, Q2 = O.weight_factors(P1, P2)
+    XP, WP = O.transform(X, P1, P2), O.transform(W, Q1, Q2)
+    # both sides quantized (the INT4 GEMM): about 0.26 -> 0.21 here
+    err_plain, err_rot = rel(qmm(X, W)), rel(qmm(XP, WP))
+    assert err_rot < 0.85 * err_plain, (err_rot, err_plain)
+
+    # activation side alone (float weights): about 0.23 -> 0.17
+    def qdq(A):
+        q, s = O.quantize_per_token(A.astype(np.float32), np.float32(1.0), "fp32")
+        return O.dequantize(O.pack_int4(q), s)
+
+    assert rel(qdq(XP) @ WP.T) < 0.8 * rel(qdq(X) @ W.T)
