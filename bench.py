@@ -106,6 +106,61 @@ def cpu_baseline(inp, seconds: float):
     }
 
 
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+
+
+def bench_int4_gemm(args, torch, B, dev):
+    """kq_int4_gemm on random codes: [T x K] x [N x K]^T -> [T x N] bf16, rotated buffers."""
+    T, N, K = args.int4_gemm
+    set_bytes = (T + N) * K // 2 + T * N * 2
+    nsets = max(2, math.ceil(args.rotate_mib * 2 ** 20 / set_bytes))
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    sets = []
+    for _ in range(nsets):
+        xq = torch.randint(0, 256, (T, K // 2), dtype=torch.uint8, device=dev, generator=g)
+        wq = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g)
+        sx = torch.rand(T, device=dev, generator=g).to(torch.float16)
+        sw = torch.rand(N, device=dev, generator=g).to(torch.float16)
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        sets.append((xq, sx, wq, sw, out))
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+
+    def step(i):
+        xq, sx, wq, sw, out = sets[i % nsets]
+        B.kq_int4_gemm(xq, K // 2, sx, T, wq, K // 2, sw, N, K, "fp16", "bf16", out, N, sh)
+
+    K_steps = args.steps
+    span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    span[0].record(stream)
+    for i in range(K_steps):
+        step(i)
+    span[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    us = span[0].elapsed_time(span[1]) / K_steps * 1e3
+    ops = 2.0 * T * N * K
+    byts = (T + N) * K / 2 + T * N * 2
+    tops = ops / us / 1e6
+    log(f"[bench] int4 gemm T={T} N={N} K={K}: {us:.2f} us/launch, {tops:.0f} TOP/s, "
+        f"{byts / us / 1e3:.0f} GB/s of operands+output")
+    print(json.dumps({
+        "metric": "INT4 x INT4 GEMM (kq_int4_gemm) TOP/s", "value": tops, "unit": "TOP/s",
+        "n_gpus": 1, "steps": K_steps, "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / K_steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int4 (int8 MFMA)", "data": "synthetic",
+        "config": {"workload": "int4_gemm", "T": T, "N": N, "K": K, "out_dtype": "bf16",
+                   "buffer_sets": nsets},
+        "roofline": {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": tops / PEAK_INT8_TOPS, "traffic": None, "kernel_avg_us": us},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +177,8 @@ def main():
                     default="default", help="work split of the fused kernel (default: the plan's)")
     ap.add_argument("--per-launch-events", action="store_true",
                     help="also time every launch with its own event pair (diagnostic)")
+    ap.add_argument("--int4-gemm", type=int, nargs=3, metavar=("T", "N", "K"), default=None,
+                    help="time kq_int4_gemm on random codes instead (tokens, out channels, K)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -144,6 +201,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.int4_gemm:
+        bench_int4_gemm(args, torch, B, dev)
+        return
     wl = S.WORKLOADS[args.workload]
     t_gen = time.perf_counter()
     inp = S.make(wl, T=args.tokens)

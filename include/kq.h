@@ -128,6 +128,35 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
 kq_status kq_transform_quant(const kq_plan *plan, const void *X, int64_t T, int64_t ldx,
                              uint8_t *codes, void *scales, float *y_debug, void *stream);
 
+/*
+ * kq_int4_gemm -- the INT4 x INT4 consumer of two kq_transform_quant outputs, on the int8
+ * matrix cores ("FlatQuant" page, Putting It Together: the quantized activations feed an
+ * INT4 GEMM; "High-Rate Quantized Matrix Multiplication I", Technical Summary: product of
+ * two absmax-quantized matrices):
+ *     out[t][j] = cvt( fp32( fp32( fp32(acc[t][j]) * sx[t] ) * sw[j] ) ),
+ *     acc[t][j] = sum_k qx[t][k] * qw[j][k]  (exact, integer),
+ * cvt = identity for KQ_FP32 output, round-to-nearest-even for KQ_BF16 / KQ_FP16.
+ * The weight side is W's rows run through kq_transform_quant with the factors P1^-T and
+ * P2^-T ((X P)(P^-1 W^T) = X W^T, "FlatQuant" page, Learning the affine transformation),
+ * which for orthogonal factors are P1 and P2 themselves.
+ *   xq     device, T rows of K/2 code bytes, row stride ldxq bytes (as kq_transform_quant
+ *          writes them: ldxq = K/2), 16-byte aligned, ldxq a multiple of 16.
+ *   sx     device, T per-token steps of scale_dtype (KQ_FP16 or KQ_FP32).
+ *   wq     device, N rows of K/2 code bytes, row stride ldwq bytes, same rules as xq.
+ *   sw     device, N per-row steps of scale_dtype (fp32: 16-byte aligned).
+ *   K      codes per row: a multiple of 256, at most 65536 (the int32 accumulator range).
+ *   N      a multiple of 4.
+ *   out    device, T rows of N values of out_dtype (KQ_FP32, KQ_BF16, KQ_FP16), row stride
+ *          ldo elements; out and each row start aligned to 4 elements.
+ * T == 0 or N == 0 returns KQ_OK and launches nothing. Asynchronous on `stream`; no
+ * allocation. Errors: INVALID_ARG (NULLs, negative sizes, strides too small, dtypes),
+ * UNSUPPORTED (K or N not as above; T*ldxq or N*ldwq >= 4 GiB), ALIGNMENT, HIP.
+ */
+kq_status kq_int4_gemm(const uint8_t *xq, int64_t ldxq, const void *sx, int64_t T,
+                       const uint8_t *wq, int64_t ldwq, const void *sw, int64_t N, int64_t K,
+                       kq_dtype scale_dtype, kq_dtype out_dtype, void *out, int64_t ldo,
+                       void *stream);
+
 /* Free a plan and its device buffers. NULL is a no-op (returns KQ_OK). The caller must
  * make sure no enqueued kq_transform_quant on this plan is still running. */
 kq_status kq_destroy(kq_plan *plan);

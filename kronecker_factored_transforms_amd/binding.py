@@ -27,7 +27,7 @@ KQ_FLAG_SPLIT_PAIR = 0x200
 EXPORTS = (
     "kq_choose_factors", "kq_create", "kq_create_ex", "kq_transform_quant", "kq_destroy",
     "kq_plan_clip_ratio", "kq_plan_kernel_name", "kq_plan_kernel_name_for", "kq_status_string",
-    "kq_version",
+    "kq_version", "kq_int4_gemm",
 )
 
 _lib = None
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.kq_plan_kernel_name_for.restype = ctypes.c_char_p
     L.kq_status_string.argtypes = [i32]
     L.kq_status_string.restype = ctypes.c_char_p
+    L.kq_int4_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i32, i32, vp, i64, vp]
+    L.kq_int4_gemm.restype = i32
     L.kq_version.argtypes = []
     L.kq_version.restype = i32
     _lib = L
@@ -149,6 +151,29 @@ def kq_plan_kernel_name(plan) -> str:
 
 def kq_plan_kernel_name_for(plan, T: int) -> str:
     return lib().kq_plan_kernel_name_for(plan, int(T)).decode()
+
+
+def kq_int4_gemm(xq, ldxq, sx, T, wq, ldwq, sw, N, K, scale_dtype, out_dtype, out, ldo,
+                 stream=None) -> None:
+    st = lib().kq_int4_gemm(_ptr(xq), int(ldxq), _ptr(sx), int(T), _ptr(wq), int(ldwq), _ptr(sw),
+                            int(N), int(K), _dtype_code(scale_dtype), _dtype_code(out_dtype),
+                            _ptr(out), int(ldo), _stream(stream))
+    _check(st, "kq_int4_gemm")
+
+
+def int4_gemm(xq, sx, wq, sw, out_dtype="fp32", out=None, stream=None):
+    """Tensor convenience wrapper of kq_int4_gemm: xq [T, K/2] uint8 codes with sx [T],
+    wq [N, K/2] with sw [N] (same scale dtype) -> out [T, N] (allocated with torch)."""
+    import torch
+    T, N, K = int(xq.shape[0]), int(wq.shape[0]), int(xq.shape[1]) * 2
+    if int(wq.shape[1]) * 2 != K or sx.dtype != sw.dtype:
+        raise ValueError("xq/wq widths or scale dtypes differ")
+    odt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[out_dtype]
+    if out is None:
+        out = torch.empty((T, N), dtype=odt, device=xq.device)
+    kq_int4_gemm(xq, xq.stride(0), sx, T, wq, wq.stride(0), sw, N, K, sx.dtype, out_dtype, out,
+                 out.stride(0), stream)
+    return out
 
 
 # ------------------------------------------------------------------------------------

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkq.so")
-SOURCES = ["kq_api.hip", "kq_fused.hip", "kq_generic.hip"]
+SOURCES = ["kq_api.hip", "kq_fused.hip", "kq_generic.hip", "kq_gemm.hip"]
 ARCH = os.environ.get("KQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

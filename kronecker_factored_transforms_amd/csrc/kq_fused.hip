@@ -34,6 +34,7 @@
 // which reduction index each slot carries and the plan stores the factors in that order.
 
 #include "kq_internal.h"
+#include "kq_device.h"
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -427,52 +428,12 @@ struct StreamCfg {
   __device__ static constexpr int swz(int R) { return (R / RPB) % PPR; }
 };
 
-#define KQ_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
-
 // Cache policy of the streaming accesses: every input byte is read once and every code
 // byte written once, so both go non-temporal ("nt"), which keeps them from displacing
 // each other in the caches (measured on MI355X: read 16 KiB + write 4 KiB per token
 // streams about 12% faster than with the default policy).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8])
-constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0)
-constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0)
-
-// Wait, and keep both the compiler and the scheduler from moving memory accesses across.
-template <int IMM>
-__device__ __forceinline__ void wait_and_fence() {
-  __builtin_amdgcn_s_waitcnt(IMM);
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-// One global -> LDS DMA of 16 bytes per lane (global_load_lds_dwordx4, non-temporal):
-// lane i reads base + voff_i and its bytes land at lds_base + 16 i; base and lds_base
-// must be wave-uniform. Issued from inline asm on purpose: the compiler's wait insertion
-// cannot tell which LDS bytes a DMA writes, so for a builtin DMA it makes every later
-// LDS read wait for it, and with code stores in flight it turns that into a wait for all
-// vector-memory traffic (stores included). The kernels order their DMAs with explicit
-// s_waitcnt instead. m0 is saved and restored so that no value the compiler keeps there
-// is lost; the s_nop gives the m0 write and a VALU write of the base (readfirstlane)
-// the wait states a vector-memory read of them needs.
-__device__ __forceinline__ void dma16_nt(const void *base, uint32_t voff, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(base), "s"(lds_base)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)KQ_LDS_PTR(p);
-}
 
 // Quantize a wave's whole Y tile (lane holds yacc[m2][nt] = 4 consecutive columns of row
 // 16 nt + lr) into packed code words w[nt][q] (8 consecutive columns each).

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "kq.h")
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -117,3 +117,21 @@ def test_null_plan_paths(L):
     assert L.kq_plan_kernel_name(None) == b""
     assert L.kq_plan_kernel_name_for(None, 5) == b""
     assert L.kq_transform_quant(None, None, 0, 0, None, None, None, None) == B.KQ_ERR_INVALID_ARG
+
+
+def _gemm_raw(L, T=16, N=8, K=256, sd=B.KQ_FP16, od=B.KQ_FP32, xq=0x1000, wq=0x2000,
+              sx=0x3000, sw=0x4000, out=0x5000, ldxq=None, ldwq=None, ldo=None):
+    return L.kq_int4_gemm(xq, K // 2 if ldxq is None else ldxq, sx, T, wq,
+                          K // 2 if ldwq is None else ldwq, sw, N, K, sd, od, out,
+                          N if ldo is None else ldo, None)
+
+
+def test_int4_gemm_rejects_bad_arguments_before_touching_the_gpu(L):
+    assert _gemm_raw(L, T=0) == B.KQ_OK and _gemm_raw(L, N=0) == B.KQ_OK   # nothing to do
+    for kw in (dict(T=-1), dict(K=0), dict(sd=B.KQ_BF16), dict(od=7), dict(xq=None),
+               dict(sw=None), dict(out=None), dict(ldxq=64), dict(ldo=4)):
+        assert _gemm_raw(L, **kw) == B.KQ_ERR_INVALID_ARG, kw
+    for kw in (dict(K=384), dict(K=65536 + 256), dict(N=6)):
+        assert _gemm_raw(L, **kw) == B.KQ_ERR_UNSUPPORTED, kw
+    for kw in (dict(xq=0x1008), dict(ldxq=136), dict(out=0x5004), dict(ldo=10), dict(sd=B.KQ_FP32, sw=0x4004)):
+        assert _gemm_raw(L, **kw) == B.KQ_ERR_ALIGNMENT, kw
