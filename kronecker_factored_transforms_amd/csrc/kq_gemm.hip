@@ -21,9 +21,10 @@
 // over K in steps of 256 codes (128 bytes per row) double-buffered in LDS; every wave
 // owns 128 x 64 outputs (8 x 4 MFMA 16x16x64 tiles). Each step's tiles arrive by DMA,
 // 1 KiB of consecutive memory (8 rows x 128 bytes) per instruction, with the 16-byte
-// pieces of row R stored at position p ^ ((R / 2) % 8), so that the 16 rows of one
-// fragment read use 16 different bank slots. The weight side is the MFMA A operand, so a
-// lane ends with 4 consecutive output channels of one token (one vector store).
+// pieces of row R stored at position p ^ ((R / 2) % 8): the 16 rows of one fragment read
+// (16 bytes per lane, one piece) then spread evenly over the 8 bank groups of a row. The
+// weight side is the MFMA A operand, so a lane ends with 4 consecutive output channels
+// of one token (one vector store).
 #include "kq_internal.h"
 #include "kq_device.h"
 
@@ -31,6 +32,7 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;                   // weight rows (output channels) per workgroup
 constexpr int kBN = 256;                   // tokens per workgroup
@@ -115,23 +117,32 @@ __global__ __launch_bounds__(kGemmThreads) void kq_int4_gemm_kernel(
     if (ks + 1 < ksteps) dma_step(ks + 1, b ^ 1);
 
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // 64 codes (32 bytes) of the step per MFMA
-      // lane group g reads code bytes 32 s + 8 g .. +8: piece 2 s + g/2, half g%2
-      const int off = (((2 * s + (g >> 1)) ^ sw8) * 16) + (g & 1) * 8;
-      i32x4 a[kMI], bx[kNI];
+    for (int q = 0; q < 2; ++q) {  // 128 codes (64 bytes) of the step: two MFMA steps
+      // lane group g reads the whole piece 4 q + g (32 codes): its first 8 bytes feed the
+      // first MFMA step, the last 8 bytes the second (for every row of both operands)
+      const int off = ((4 * q + g) ^ sw8) * 16;
+      u32x4_t pa[kMI], pb[kNI];
 #pragma unroll
       for (int mi = 0; mi < kMI; ++mi)
-        a[mi] = unpack16(*reinterpret_cast<const u32x2 *>(
-            s_w[b] + (row_w + mi * 16) * kRowBytes + off));
+        pa[mi] = *reinterpret_cast<const u32x4_t *>(s_w[b] + (row_w + mi * 16) * kRowBytes + off);
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
-        bx[ni] = unpack16(*reinterpret_cast<const u32x2 *>(
-            s_x[b] + (row_x + ni * 16) * kRowBytes + off));
+        pb[ni] = *reinterpret_cast<const u32x4_t *>(s_x[b] + (row_x + ni * 16) * kRowBytes + off);
 #pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
+      for (int h = 0; h < 2; ++h) {
+        i32x4 a[kMI], bx[kNI];
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
+          a[mi] = unpack16(h ? u32x2{pa[mi].z, pa[mi].w} : u32x2{pa[mi].x, pa[mi].y});
 #pragma unroll
         for (int ni = 0; ni < kNI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mi], bx[ni], acc[mi][ni], 0, 0, 0);
+          bx[ni] = unpack16(h ? u32x2{pb[ni].z, pb[ni].w} : u32x2{pb[ni].x, pb[ni].y});
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < kNI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mi], bx[ni], acc[mi][ni], 0, 0, 0);
+      }
     }
     wait_and_fence<kWaitLgkm0>();  // this wave's reads of buffer b have returned
   }
