@@ -71,9 +71,19 @@ def cpu_baseline(inp, seconds: float):
     except Exception:  # pragma: no cover
         blas = []
 
+    from kronecker_factored_transforms_amd import synth as S
+
+    wl = inp.wl
+    if wl.per_row:  # identity left factor, one step per row of n2 values
+        P1 = S.to_bf16_bits(np.eye(wl.n1)) if wl.dtype == "bf16" else np.eye(wl.n1, dtype=np.float32)
+    else:
+        P1 = inp.P1
+
     def run(X):
-        Y = O.transform(X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
-        q, s = O.quantize_per_token(Y.astype(np.float32), O.clip_ratio(inp.alpha), inp.wl.scale_dtype)
+        Y = O.transform(X, P1, inp.P2, inp.c, wl.dtype).astype(np.float32)
+        if wl.per_row:
+            Y = Y.reshape(-1, wl.n2)
+        q, s = O.quantize_per_token(Y, O.clip_ratio(inp.alpha), wl.scale_dtype)
         return O.pack_int4(q), s
 
     T = inp.X.shape[0]
@@ -223,14 +233,20 @@ def main():
              "cols": B.KQ_FLAG_SPLIT_COLS, "deep": B.KQ_FLAG_SPLIT_DEEP,
              "stream": B.KQ_FLAG_SPLIT_STREAM, "pair": B.KQ_FLAG_SPLIT_PAIR,
              "generic": B.KQ_FLAG_FORCE_GENERIC}[args.split]
-    plan = B.Plan(dev_tensor(inp.P1), dev_tensor(inp.P2), c, inp.alpha, wl.scale_dtype, flags=flags)
+    if wl.per_row:  # identity left factor, one step per row of V
+        plan = B.Plan(None, dev_tensor(inp.P2), None, inp.alpha, wl.scale_dtype, flags=flags,
+                      n1=wl.n1)
+    else:
+        plan = B.Plan(dev_tensor(inp.P1), dev_tensor(inp.P2), c, inp.alpha, wl.scale_dtype,
+                      flags=flags)
     T, n = wl.T, wl.n
+    nscales = T * wl.n1 if wl.per_row else T
     esize = 2 if wl.dtype == "bf16" else 4
-    set_bytes = T * n * esize + T * n // 2 + T * 2
+    set_bytes = T * n * esize + T * n // 2 + nscales * 2
     nsets = max(2, math.ceil(args.rotate_mib * 2 ** 20 / set_bytes))
     Xs = [X0] + [X0.clone() for _ in range(nsets - 1)]
     outs = [(torch.empty((T, n // 2), dtype=torch.uint8, device=dev),
-             torch.empty((T,), dtype=plan.scale_dtype, device=dev)) for _ in range(nsets)]
+             torch.empty((nscales,), dtype=plan.scale_dtype, device=dev)) for _ in range(nsets)]
     stream = torch.cuda.current_stream()
     handle, sh = plan.handle, int(stream.cuda_stream)
     kname = plan.kernel_for(T)
@@ -319,6 +335,7 @@ def main():
             "workload": wl.name, "T": T, "n": n, "n1": wl.n1, "n2": wl.n2, "x_dtype": wl.dtype,
             "scale_dtype": wl.scale_dtype, "per_channel_c": inp.c is not None,
             "alpha": inp.alpha, "kernel": kname, "buffer_sets": nsets,
+            "scales_per_token": wl.n1 if wl.per_row else 1,
         },
         "roofline": {
             "bound": "hbm",

@@ -65,6 +65,15 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
                                     /* operands in registers, tokens double-buffered in   */
                                     /* LDS by DMA (no per-channel scale)                  */
 
+/* KQ_FLAG_PER_ROW: the left factor is the identity (pass P1 = NULL) and every row of V
+ * (n2 values, e.g. one attention head of a token) gets its own step, so `scales` holds
+ * T * n1 values (row i of token t at t * n1 + i) and codes keep the row-major Y order.
+ * This is the per-head key/value transform ahead of a quantized KV cache ("FlatQuant"
+ * page, Symbol Map: P_h, P_v; Transformer integration). bf16 only, n2 in {64, 128}, any
+ * n1 >= 1, no c, no other flag (KQ_ERR_INVALID_ARG / KQ_ERR_UNSUPPORTED otherwise);
+ * a call must have T * n1 < 2^31 rows (else KQ_ERR_UNSUPPORTED). */
+#define KQ_FLAG_PER_ROW 0x400u
+
 /*
  * kq_choose_factors -- factor a hidden size for the Kronecker transform.
  * Picks n1 <= n2 with n1*n2 == n minimising n1 + n2 ("FlatQuant" page, Deep Dive:
@@ -79,7 +88,8 @@ kq_status kq_choose_factors(int64_t n, int *n1, int *n2);
  *   n1, n2       factor sizes, n = n1*n2 must be even. n1, n2 >= 1.
  *   x_dtype      dtype of X, P1 and P2: KQ_BF16 or KQ_FP32 (P has the dtype of X).
  *   scale_dtype  KQ_FP16 (default in the bindings) or KQ_FP32 for the per-token scale.
- *   P1           device, n1 x n1 row-major, x_dtype ("left" factor, enters transposed).
+ *   P1           device, n1 x n1 row-major, x_dtype ("left" factor, enters transposed);
+ *                NULL (identity) exactly when KQ_FLAG_PER_ROW is given.
  *   P2           device, n2 x n2 row-major, x_dtype.
  *   c            device, n fp32 per-channel scale applied before the transform, or NULL
  *                (all ones).
@@ -117,7 +127,8 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
  *   T        number of tokens, >= 0. T == 0 returns KQ_OK and launches nothing.
  *   ldx      leading dimension of X in elements.
  *   codes    device, T x (n/2) bytes, row stride n/2, 16-byte aligned (written).
- *   scales   device, T scales of the plan's scale_dtype (written).
+ *   scales   device, T scales of the plan's scale_dtype (written); T * n1 of them for a
+ *            KQ_FLAG_PER_ROW plan.
  *   y_debug  device, T x n fp32, or NULL. When given, receives the exact fp32 Y that
  *            was quantized (for verification; adds 4n bytes of writes per token).
  * Caller owns X, codes, scales and y_debug. Outputs are written in full for every

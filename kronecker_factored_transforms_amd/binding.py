@@ -22,6 +22,7 @@ KQ_FLAG_SPLIT_COLS = 0x40
 KQ_FLAG_SPLIT_DEEP = 0x80
 KQ_FLAG_SPLIT_STREAM = 0x100
 KQ_FLAG_SPLIT_PAIR = 0x200
+KQ_FLAG_PER_ROW = 0x400
 
 # every symbol declared in include/kq.h
 EXPORTS = (
@@ -184,23 +185,33 @@ class Plan:
     dtype; c is float32 [n] or None. Outputs are allocated with torch on X's device.
     """
 
-    def __init__(self, P1, P2, c=None, alpha=math.inf, scale_dtype="fp16", stream=None, flags=0):
+    def __init__(self, P1, P2, c=None, alpha=math.inf, scale_dtype="fp16", stream=None, flags=0,
+                 n1=None):
+        """P1 = None means an identity left factor of size n1 (given) and one step per row
+        of V (KQ_FLAG_PER_ROW): scales then have shape [T, n1]."""
         import torch
-        if P1.dtype != P2.dtype or P1.dtype not in (torch.bfloat16, torch.float32):
-            raise TypeError("P1 and P2 must both be bfloat16 or both float32")
-        if not (P1.is_cuda and P2.is_cuda) or (c is not None and not c.is_cuda):
+        if P1 is None:
+            if n1 is None:
+                raise ValueError("n1 is required with an identity left factor (P1=None)")
+            flags |= KQ_FLAG_PER_ROW
+        elif P1.dtype != P2.dtype:
+            raise TypeError("P1 and P2 must have the same dtype")
+        if P2.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("factors must be bfloat16 or float32")
+        if not P2.is_cuda or (P1 is not None and not P1.is_cuda) or (c is not None and not c.is_cuda):
             raise ValueError("factors must live on the GPU")
-        P1 = P1.contiguous()
+        P1 = None if P1 is None else P1.contiguous()
         P2 = P2.contiguous()
         if c is not None:
             if c.dtype != torch.float32:
                 raise TypeError("c must be float32")
             c = c.contiguous()
-        self.n1, self.n2 = int(P1.shape[0]), int(P2.shape[0])
+        self.per_row = P1 is None
+        self.n1, self.n2 = (int(n1) if P1 is None else int(P1.shape[0])), int(P2.shape[0])
         self.n = self.n1 * self.n2
-        self.x_dtype = P1.dtype
+        self.x_dtype = P2.dtype
         self.scale_dtype = torch.float16 if _dtype_code(scale_dtype) == KQ_FP16 else torch.float32
-        self.handle = kq_create(self.n1, self.n2, P1.dtype, self.scale_dtype, P1, P2, c, alpha,
+        self.handle = kq_create(self.n1, self.n2, P2.dtype, self.scale_dtype, P1, P2, c, alpha,
                                 stream, flags)
         self.clip = kq_plan_clip_ratio(self.handle)
         self.kernel = kq_plan_kernel_name(self.handle)
@@ -212,7 +223,8 @@ class Plan:
         T = X.shape[0]
         if out is None:
             codes = torch.empty((T, self.n // 2), dtype=torch.uint8, device=X.device)
-            scales = torch.empty((T,), dtype=self.scale_dtype, device=X.device)
+            scales = torch.empty((T, self.n1) if self.per_row else (T,), dtype=self.scale_dtype,
+                                 device=X.device)
         else:
             codes, scales = out
         y = torch.empty((T, self.n), dtype=torch.float32, device=X.device) if y_debug else None

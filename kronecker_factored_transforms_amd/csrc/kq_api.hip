@@ -98,6 +98,52 @@ kq_status kq_choose_factors(int64_t n, int *n1, int *n2) {
   return KQ_ERR_INVALID_ARG;
 }
 
+// A plan of the rows kernel: identity left factor (P1 == NULL), one step per row of V.
+kq_status create_rows_plan(kq_plan **out, int n1, int n2, kq_dtype scale_dtype, const void *P2,
+                           float alpha, hipStream_t s) {
+  const kq_fused_variant *fv = kq_fused_lookup_rows(n2);
+  if (!fv) return KQ_ERR_UNSUPPORTED;
+  kq_plan *p = static_cast<kq_plan *>(calloc(1, sizeof(kq_plan)));
+  if (!p) return KQ_ERR_OUT_OF_MEMORY;
+  p->n1 = n1;
+  p->n2 = n2;
+  p->n = n1 * n2;
+  p->x_dtype = KQ_BF16;
+  p->scale_dtype = scale_dtype;
+  p->clip = clip_from_alpha(alpha);
+  p->kind = KQ_KIND_FUSED_MFMA;
+  p->kname = fv->name;
+  p->launch = fv->launch;
+  p->per_row = 1;
+  kq_status st = KQ_OK;
+  std::vector<uint16_t> h2((size_t)n2 * n2), a2((size_t)n2 * n2);
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipMemcpyAsync(h2.data(), P2, h2.size() * 2, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    st = KQ_ERR_HIP;
+    goto fail;
+  }
+  p->device = dev;
+  kq_fused_arrange_p2_rows(h2.data(), n2, a2.data());
+  if ((st = upload(&p->p2op, a2.data(), a2.size() * 2, s)) != KQ_OK) goto fail;
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fv->kernel_symbol, fv->threads, 0) !=
+          hipSuccess) {
+    st = KQ_ERR_HIP;
+    goto fail;
+  }
+  if (per_cu < 1) { st = KQ_ERR_UNSUPPORTED; goto fail; }
+  p->grid_cap = ncu * per_cu;
+  *out = p;
+  return KQ_OK;
+fail:
+  free_plan_buffers(p);
+  free(p);
+  return st;
+}
+
 kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype scale_dtype,
                        const void *P1, const void *P2, const float *c, float alpha, void *stream,
                        unsigned flags) {
@@ -108,8 +154,14 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   if (n % 2) return KQ_ERR_INVALID_ARG;
   if (x_dtype != KQ_BF16 && x_dtype != KQ_FP32) return KQ_ERR_INVALID_ARG;
   if (scale_dtype != KQ_FP16 && scale_dtype != KQ_FP32) return KQ_ERR_INVALID_ARG;
-  if (!P1 || !P2) return KQ_ERR_INVALID_ARG;
   if (isnan(alpha)) return KQ_ERR_INVALID_ARG;
+  if (flags & KQ_FLAG_PER_ROW) {
+    // identity left factor only; bf16; no per-channel scale, no other flag
+    if (P1 || !P2 || c || x_dtype != KQ_BF16 || (flags & ~KQ_FLAG_PER_ROW))
+      return KQ_ERR_INVALID_ARG;
+    return create_rows_plan(out, n1, n2, scale_dtype, P2, alpha, static_cast<hipStream_t>(stream));
+  }
+  if (!P1 || !P2) return KQ_ERR_INVALID_ARG;
   const unsigned split_flags =
       flags & (KQ_FLAG_SPLIT_REG1 | KQ_FLAG_SPLIT_REG2 | KQ_FLAG_SPLIT_COLS | KQ_FLAG_SPLIT_DEEP |
                KQ_FLAG_SPLIT_STREAM | KQ_FLAG_SPLIT_PAIR);
@@ -281,6 +333,7 @@ kq_status kq_transform_quant(const kq_plan *p, const void *X, int64_t T, int64_t
     return KQ_ERR_ALIGNMENT;
   if (y_debug && !is_aligned(y_debug, 16)) return KQ_ERR_ALIGNMENT;
   if (T > ((int64_t)1 << 40) / p->n) return KQ_ERR_INVALID_ARG;
+  if (p->per_row && T * p->n1 >= ((int64_t)1 << 31)) return KQ_ERR_UNSUPPORTED;
   hipError_t e;
   if (p->small_launch && T < p->small_max_T) {
     kq_plan v = *p;  // the same plan seen through the small-batch variant's operands

@@ -57,6 +57,33 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t 
   }
 }
 
+// The same DMA with a full 64-bit address per lane (rows that are not one stride apart).
+template <bool NT>
+__device__ __forceinline__ void dma16_addr(const void *gaddr, uint32_t lds_base) {
+  uint32_t saved;
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gaddr), "s"(lds_base)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gaddr), "s"(lds_base)
+        : "memory");
+  }
+}
+
 __device__ __forceinline__ void dma16_nt(const void *base, uint32_t voff, uint32_t lds_base) {
   dma16<true>(base, voff, lds_base);
 }

@@ -864,6 +864,187 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// rows kernel: identity left factor, one step per row of V (per-head transform)
+// ------------------------------------------------------------------------------------
+// With P1 = I the rows of V never mix: row r (token t = r / n1, head i = r % n1) is
+// y = x P2 on its own and gets its own INT4 step ("FlatQuant" page, Symbol Map and
+// Transformer integration: the per-head transforms of keys and values ahead of the
+// quantized KV cache). Rows are streamed in tiles of 16, whatever n1 is; 8 waves per CU,
+// each with a ring of 4 LDS slots (three tiles in flight while it computes one) and all of
+// P2's B operands in registers. P2's columns are permuted in the plan so that after the single MFMA stage a lane holds
+// NT consecutive columns of each of its 4 rows: one code word per row, and the row's
+// absmax is a 16-lane DPP reduction.
+template <int N2>
+struct RowsCfg {
+  static_assert(N2 == 64 || N2 == 128, "rows kernel: n2 in {64, 128}");
+  static constexpr int WAVES = 8;
+  static constexpr int SLOTS = 4;               // ring of tiles per wave (3 in flight)
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int NT = N2 / 16;            // column tiles = consecutive columns per lane
+  static constexpr int KS = N2 / 32;            // reduction steps
+  static constexpr int RB = N2 * 2;             // bytes per row
+  static constexpr int PPR = RB / 16;           // 16-byte pieces per row
+  static constexpr int RPB = 256 / RB;          // rows per 256-byte bank row
+  static constexpr int RPI = 1024 / RB;         // rows per DMA instruction
+  static constexpr int TILE = 16 * RB;          // bytes per 16-row tile
+  static constexpr int LOADS = TILE / 1024;     // DMA instructions per tile
+  static_assert(WAVES * SLOTS * TILE <= 160 * 1024, "LDS budget");
+  __device__ static constexpr int swz(int R) { return (R / RPB) % PPR; }
+  // vmcnt(k LOADS): at most k later tiles' loads still in flight
+  template <int K>
+  static constexpr int wait_imm = 0x0F70 | ((K * LOADS) & 15) | (((K * LOADS) >> 4) << 14);
+};
+
+// 4 consecutive values -> 2 code bytes (value e in bits 4e..4e+3), clamped to [-8, 7]
+__device__ __forceinline__ uint32_t quant4(const float (&y)[4], float inv) {
+  constexpr float kMagic = 12582920.0f;   // 1.5 * 2^23 + 8 (see quant8)
+  constexpr int kLo = 0x4B400000, kHi = 0x4B40000F;
+  uint32_t u[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float t = __fadd_rn(__fmul_rn(y[e], inv), kMagic);
+    u[e] = (uint32_t)min(max(__float_as_int(t), kLo), kHi) & 0xFu;
+  }
+  return ((u[0] | (u[1] << 4) | (u[2] << 8) | (u[3] << 12)) ^ 0x8888u);
+}
+
+template <int N2, bool YDBG>
+__global__ __launch_bounds__(512) void kq_rows_kernel(
+    const __bf16 *__restrict__ X, int64_t T, int n1, int64_t ldx,
+    const bf16x8 *__restrict__ p2op, float clip, int scale_fp16,
+    uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
+  using C = RowsCfg<N2>;
+  __shared__ __align__(16) unsigned char s_tile[C::WAVES][C::SLOTS][C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, lr = lane & 15;
+  const int64_t R = T * (int64_t)n1;              // rows
+  const int64_t ntiles = (R + 15) / 16;
+  const int64_t stride = (int64_t)gridDim.x * C::WAVES;
+  const int64_t first = (int64_t)blockIdx.x * C::WAVES + wave;
+
+  // DMA of tile `tl` into slot b: instruction j fills tile rows RPI j .. RPI j + RPI - 1;
+  // lane i lands at row RPI j + i / PPR, position i % PPR (piece (i % PPR) ^ swz(row)).
+  // Rows past the end read the last row (their results are not stored).
+  // (R < 2^31 is checked on the host: 32-bit row arithmetic)
+  auto dma_tile = [&](int64_t tl, int b) {
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int Rl = j * C::RPI + lane / C::PPR;
+      uint32_t r = (uint32_t)(tl * 16) + (uint32_t)Rl;
+      r = r < (uint32_t)R ? r : (uint32_t)R - 1u;
+      const uint32_t t = r / (uint32_t)n1, hd = r - t * (uint32_t)n1;
+      const int piece = (lane % C::PPR) ^ C::swz(Rl);
+      dma16_addr<true>(X + (int64_t)t * ldx + hd * N2 + piece * 8,
+                       lds_addr(s_tile[wave][b] + j * 1024));
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < C::SLOTS; ++k)
+    if (first + k * stride < ntiles) dma_tile(first + k * stride, k);
+
+  bf16x8 p2r[C::KS][C::NT];  // all of P2's B operands, resident in registers
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) p2r[ks][nt] = p2op[(ks * C::NT + nt) * 64 + lane];
+  // operands resident (and the first tiles landed) before the loop counts DMAs: the
+  // compiler's own waits for these loads know nothing of the DMAs
+  wait_and_fence<kWaitVm0>();
+
+  uint32_t pend[4] = {0u, 0u, 0u, 0u};  // codes of the previous tile's 4 rows of this lane
+  TokenScale pend_s[4];
+  int64_t pend_row = -1;                // first of those rows (row 16 tile + 4 g)
+
+  int it = 0;
+  for (int64_t tl = first; tl < ntiles; tl += stride, ++it) {
+    const int b = it % C::SLOTS;
+    // this tile has landed once at most the later tiles' loads (up to SLOTS - 1 tiles, all
+    // issued before any later store) are in flight: loads complete in issue order
+    const int64_t later = (ntiles - 1 - tl) / stride;  // tiles of this wave after this one
+    if (later >= 3) wait_and_fence<C::template wait_imm<3>>();
+    else if (later == 2) wait_and_fence<C::template wait_imm<2>>();
+    else if (later == 1) wait_and_fence<C::template wait_imm<1>>();
+    else wait_and_fence<kWaitVm0>();
+    const unsigned char *tile = s_tile[wave][b];
+    bf16x8 av[C::KS];  // A operands: row lr, piece 4 ks + g
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      av[ks] = *reinterpret_cast<const bf16x8 *>(tile + lr * C::RB + (((ks * 4 + g) ^ C::swz(lr)) * 16));
+    wait_and_fence<kWaitLgkm0>();  // slot b is free again
+    if (pend_row >= 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = pend_row + r;
+        if (row < R) {
+          uint8_t *dst = codes + row * (N2 / 2) + lr * (C::NT / 2);
+          if constexpr (N2 == 128) __builtin_nontemporal_store(pend[r], reinterpret_cast<uint32_t *>(dst));
+          else __builtin_nontemporal_store((uint16_t)pend[r], reinterpret_cast<uint16_t *>(dst));
+          if (lr == 0) store_scale(scales, row, pend_s[r], scale_fp16);
+        }
+      }
+    }
+    if (tl + C::SLOTS * stride < ntiles) dma_tile(tl + C::SLOTS * stride, b);
+
+    f32x4 zacc[C::NT];
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) zacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+        zacc[nt] = mfma(av[ks], p2r[ks][nt], zacc[nt]);
+
+    // lane holds Y[row 16 tl + 4 g + r][lr NT + nt]; absmax per row over the 16 lanes of g
+    const int64_t row0 = tl * 16 + 4 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) m = fmaxf(m, fabsf(zacc[nt][r]));
+      m = dpp_step<0xB1>(m);
+      m = dpp_step<0x4E>(m);
+      m = dpp_step<0x141>(m);
+      m = dpp_step<0x140>(m);
+      const TokenScale ts = token_scale(m, clip, scale_fp16);
+      if constexpr (N2 == 128) {
+        const float yv[8] = {zacc[0][r], zacc[1][r], zacc[2][r], zacc[3][r],
+                             zacc[4][r], zacc[5][r], zacc[6][r], zacc[7][r]};
+        pend[r] = quant8<true>(yv, ts.inv);
+      } else {
+        const float yv[4] = {zacc[0][r], zacc[1][r], zacc[2][r], zacc[3][r]};
+        pend[r] = quant4(yv, ts.inv);
+      }
+      pend_s[r] = ts;
+      if constexpr (YDBG) {
+        if (row0 + r < R) {
+          float *yp = ydbg + (row0 + r) * N2 + lr * C::NT;
+#pragma unroll
+          for (int q = 0; q < C::NT / 4; ++q)
+            reinterpret_cast<float4 *>(yp)[q] =
+                make_float4(zacc[4 * q][r], zacc[4 * q + 1][r], zacc[4 * q + 2][r], zacc[4 * q + 3][r]);
+        }
+      }
+    }
+    pend_row = row0;
+  }
+  if (pend_row >= 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = pend_row + r;
+      if (row < R) {
+        uint8_t *dst = codes + row * (N2 / 2) + lr * (C::NT / 2);
+        if constexpr (N2 == 128) __builtin_nontemporal_store(pend[r], reinterpret_cast<uint32_t *>(dst));
+        else __builtin_nontemporal_store((uint16_t)pend[r], reinterpret_cast<uint16_t *>(dst));
+        if (lr == 0) store_scale(scales, row, pend_s[r], scale_fp16);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // column kernel: W = n2/32 waves per token
 // ------------------------------------------------------------------------------------
 // Waves per workgroup of the column kernel: one per 32 output columns of a token, at
@@ -1152,6 +1333,20 @@ hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
                    &launch_pair<A, B>,                                                 \
                    reinterpret_cast<const void *>(&kq_pair_kernel<A, B, false>),       \
                    "fused_mfma_bf16_pair_" #A "x" #B}
+template <int N2>
+hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
+                       void *scales, float *y_debug, hipStream_t stream) {
+  using C = RowsCfg<N2>;
+  const int64_t ntiles = (T * p->n1 + 15) / 16;
+  const int64_t groups = (ntiles + C::WAVES - 1) / C::WAVES;
+  const int grid = (int)(groups < (int64_t)p->grid_cap ? groups : (int64_t)p->grid_cap);
+  auto k = y_debug ? &kq_rows_kernel<N2, true> : &kq_rows_kernel<N2, false>;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream, static_cast<const __bf16 *>(X),
+                     T, p->n1, ldx, static_cast<const bf16x8 *>(p->p2op), p->clip,
+                     p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
+  return hipGetLastError();
+}
+
 #define KQ_STREAM(A, B)                                                                \
   kq_fused_variant{A, B, false, KQ_SPLIT_STREAM, (B), StreamCfg<A, B>::THREADS,          \
                    &launch_stream<A, B, false>,                                        \
@@ -1225,6 +1420,36 @@ const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split) {
   return nullptr;
 }
 
+
+namespace {
+const kq_fused_variant kRowsVariants[] = {
+    kq_fused_variant{0, 64, false, KQ_SPLIT_ROWS, 0, RowsCfg<64>::THREADS, &launch_rows<64>,
+                     reinterpret_cast<const void *>(&kq_rows_kernel<64, false>),
+                     "fused_mfma_bf16_rows_64"},
+    kq_fused_variant{0, 128, false, KQ_SPLIT_ROWS, 0, RowsCfg<128>::THREADS, &launch_rows<128>,
+                     reinterpret_cast<const void *>(&kq_rows_kernel<128, false>),
+                     "fused_mfma_bf16_rows_128"},
+};
+}  // namespace
+
+const kq_fused_variant *kq_fused_lookup_rows(int n2) {
+  for (const kq_fused_variant &e : kRowsVariants)
+    if (e.n2 == n2) return &e;
+  return nullptr;
+}
+
+// P2 as B operands of the rows kernel: [ks][tile a][lane L][slot v] =
+//   P2[32 ks + 8 g + v][(L%16) NT + a],   g = L/16, NT = n2/16,
+// so that after the MFMA lane L holds columns (L%16) NT + [0, NT) of its rows.
+void kq_fused_arrange_p2_rows(const uint16_t *P2, int n2, uint16_t *out) {
+  const int KS = n2 / 32, NT = n2 / 16;
+  size_t o = 0;
+  for (int ks = 0; ks < KS; ++ks)
+    for (int a = 0; a < NT; ++a)
+      for (int L = 0; L < 64; ++L)
+        for (int v = 0; v < 8; ++v)
+          out[o++] = P2[(size_t)(32 * ks + 8 * (L / 16) + v) * n2 + (L % 16) * NT + a];
+}
 
 size_t kq_fused_p1op_elems(int n1) { return (size_t)((n1 + 31) / 32) * (n1 / 16) * 512; }
 size_t kq_fused_p2op_elems(int n2) { return (size_t)n2 * (size_t)n2; }

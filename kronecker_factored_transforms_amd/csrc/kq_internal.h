@@ -45,6 +45,8 @@ struct kq_plan {
   void *small_p2op;
   int small_grid_cap;
   int64_t small_max_T;
+  // 1: identity left factor and one step per row of V (T * n1 scales)
+  int per_row;
 };
 
 // ---- fused MFMA family (kq_fused.hip) ----
@@ -53,7 +55,7 @@ struct kq_plan {
 // column kernel (n2/32 waves per token, token staged in LDS), or the stream kernel (one
 // wave per token, next token prefetched into an LDS slot by DMA).
 enum { KQ_SPLIT_REG1 = 1, KQ_SPLIT_REG2 = 2, KQ_SPLIT_COLS = 3, KQ_SPLIT_DEEP = 4,
-       KQ_SPLIT_STREAM = 5, KQ_SPLIT_PAIR = 6 };
+       KQ_SPLIT_STREAM = 5, KQ_SPLIT_PAIR = 6, KQ_SPLIT_ROWS = 7 };
 
 struct kq_fused_variant {
   int n1, n2;
@@ -68,6 +70,9 @@ struct kq_fused_variant {
 
 // The variant for (n1, n2, has_c) with the given split (0: the default one), or nullptr.
 const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split);
+// The rows kernel (identity left factor, one step per row of V) for n2, or nullptr.
+const kq_fused_variant *kq_fused_lookup_rows(int n2);
+void kq_fused_arrange_p2_rows(const uint16_t *P2, int n2, uint16_t *out);
 // Element counts of the operand-ordered bf16 copies of P1 / P2.
 size_t kq_fused_p1op_elems(int n1);
 size_t kq_fused_p2op_elems(int n2);

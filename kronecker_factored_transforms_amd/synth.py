@@ -53,6 +53,7 @@ class Workload:
     alpha_mu: float = 2.0
     alpha_sd: float = 0.5
     scale_dtype: str = "fp16"
+    per_row: bool = False            # identity left factor, one step per row of V
 
     @property
     def n(self) -> int:
@@ -88,6 +89,12 @@ WORKLOADS = {
         "prefill_n8192_t65536", 5, T=65536, n1=64, n2=128, dtype="bf16",
         x_kind="student_t3", n_outliers=8, outlier_scale=30.0, p_kind="orthogonal",
         alpha=3.0),
+    # keys of a grouped-query attention layer ahead of the KV cache: 8 heads of 128 per
+    # token (V = 8 x 128, identity left factor, one step per head), 64k-token prefill; a few
+    # outlier channels inside the head dimension
+    "kv_h8_d128": Workload(
+        "kv_h8_d128", 7, T=65536, n1=8, n2=128, dtype="bf16", x_kind="normal",
+        n_outliers=4, outlier_scale=20.0, p_kind="orthogonal", alpha=3.0, per_row=True),
     # a larger factor than 128: the 70B-class FFN down-projection input, 28672 = 128 x 224
     "down_proj_n28672": Workload(
         "down_proj_n28672", 6, T=4096, n1=128, n2=224, dtype="bf16", x_kind="silu_gate",

@@ -105,6 +105,16 @@ def test_split_flags_are_validated_on_the_host(L):
     assert st == B.KQ_ERR_UNSUPPORTED and h is None
 
 
+def test_per_row_flag_is_validated_on_the_host(L):
+    # P1 must be NULL with the flag, bf16 only, no c, no other flag
+    for kw in (dict(flags=B.KQ_FLAG_PER_ROW),                              # P1 given
+               dict(flags=B.KQ_FLAG_PER_ROW, p1=None, xd=B.KQ_FP32),
+               dict(flags=B.KQ_FLAG_PER_ROW, p1=None, c=0x3000),
+               dict(flags=B.KQ_FLAG_PER_ROW | B.KQ_FLAG_SPLIT_REG1, p1=None)):
+        st, h = _create_raw(L, 8, 128, **kw)
+        assert st == B.KQ_ERR_INVALID_ARG and h is None, kw
+
+
 def test_create_reports_unsupported_shapes(L):
     # fp32 beyond the generic kernel's on-chip limit and no MFMA variant for it
     st, h = _create_raw(L, 256, 128, xd=B.KQ_FP32)
