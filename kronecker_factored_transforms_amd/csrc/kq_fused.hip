@@ -549,6 +549,10 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
       store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
       if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
     }
+    // The two waves of a SIMD alternate between MFMA-heavy stages and the VALU-heavy
+    // quantizer: a higher issue priority for the MFMA phase keeps the matrix core fed
+    // while the other wave's VALU work fills the gaps (measured on MI355X: about 2 %).
+    __builtin_amdgcn_s_setprio(1);
     // ---- stages 1 and 2 per half of the output columns ----
     // A column tile of Y needs only the same column tile of Z, so each half runs stage 1
     // (Z = V P2 for its columns) and stage 2 (Y^T = Z^T P1) on its own: only half of
@@ -631,6 +635,7 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- epilogue: lane holds Y[16 nt + lr][LPL g + 4 m2 + r] ----
 #pragma unroll
     for (int w = C::NT / 2; w >= 1; w /= 2)
