@@ -70,6 +70,7 @@ __all__ = [
     "quantize_per_token",
     "weight_factors",
     "int4_gemm",
+    "pack_int8",
     "pack_int4",
     "unpack_int4",
     "dequantize",
@@ -239,20 +240,23 @@ def clip_ratio(alpha: float) -> np.float32:
     return np.float32(v)
 
 
-def quantize_per_token(Y32, clip, scale_dtype: str = "fp16"):
-    """Per-token symmetric INT4 round-to-nearest of an fp32 [T, n] tensor.
+def quantize_per_token(Y32, clip, scale_dtype: str = "fp16", bits: int = 4):
+    """Per-token symmetric b-bit round-to-nearest of an fp32 [T, n] tensor (b = 4 or 8).
 
     [FQ TL;DR]: plain round-to-nearest (RTN) quantization; [FQ Symbol Map]: Q(.) maps
     values to b-bit integer points with step s; [HR absmax INT]: the step comes from the
-    l-infinity norm (absmax) of the vector. Steps (readings R4-R9), each one rounded
-    fp32 (or fp16) operation:
+    l-infinity norm (absmax) of the vector. With M = 2^(b-1) - 1 (7 for INT4, 127 for
+    INT8), steps (readings R4-R9), each one rounded fp32 (or fp16) operation:
         a   = max_k |y_k|                          (exact)
-        s32 = fp32( fp32(clip * a) / 7 )
+        s32 = fp32( fp32(clip * a) / M )
         s   = fp16_rne(s32)   (or s32 when scale_dtype == "fp32")
         s == 0 -> all codes 0
-        inv = fp32(1 / s);  q = clamp(rint(fp32(y * inv)), -8, 7)
+        inv = fp32(1 / s);  q = clamp(rint(fp32(y * inv)), -M - 1, M)
     Returns (q int8 [T, n], scales float16|float32 [T]).
     """
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    M = np.float32(2 ** (bits - 1) - 1)
     y = np.asarray(Y32)
     if y.dtype != np.float32:
         raise TypeError("the quantizer takes the fp32 transformed tensor")
@@ -263,7 +267,7 @@ def quantize_per_token(Y32, clip, scale_dtype: str = "fp16"):
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         a = np.abs(y).max(axis=1) if y.shape[1] else np.zeros(T, np.float32)
         a = a.astype(np.float32)
-        s32 = (clip32 * a).astype(np.float32) / np.float32(7.0)
+        s32 = (clip32 * a).astype(np.float32) / M
         s32 = s32.astype(np.float32)
         if scale_dtype == "fp16":
             s_store = s32.astype(np.float16)
@@ -276,7 +280,7 @@ def quantize_per_token(Y32, clip, scale_dtype: str = "fp16"):
         inv = (np.float32(1.0) / np.where(zero, np.float32(1.0), s_f)).astype(np.float32)
         v = (y * inv[:, None]).astype(np.float32)
         q = np.rint(v)
-        q = np.clip(q, -8.0, 7.0)
+        q = np.clip(q, -M - 1, M)
         q = np.where(zero[:, None], 0.0, q)
     return q.astype(np.int8), s_store
 
@@ -293,6 +297,11 @@ def pack_int4(q: np.ndarray) -> np.ndarray:
         raise ValueError("codes outside [-8, 7]")
     u = (q.astype(np.int16) & 0xF).astype(np.uint8)
     return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def pack_int8(q: np.ndarray) -> np.ndarray:
+    """INT8 codes stored as bytes (two's complement), one per element, row-major order."""
+    return np.ascontiguousarray(np.asarray(q, dtype=np.int8)).view(np.uint8)
 
 
 def unpack_int4(codes: np.ndarray) -> np.ndarray:

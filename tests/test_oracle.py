@@ -438,3 +438,44 @@ def test_orthogonal_kronecker_transform_lowers_int4_gemm_error_on_outliers():
         return O.dequantize(O.pack_int4(q), s)
 
     assert rel(qdq(XP) @ WP.T) < 0.8 * rel(qdq(X) @ W.T)
+
+
+# ---- INT8 codes ----------------------------------------------------------------------
+@pytest.mark.parametrize("k", [-3, 0, 2])
+def test_int8_power_of_two_scales_match_library_qint8_quantizer(k):
+    """With absmax = 127*2^k and clip 1 the step is exactly 2^k, so the INT8 quantizer
+    (RNE, clamp) must agree with PyTorch's per-tensor qint8 quantizer, ties included."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(200 + k)
+    T, n = 5, 96
+    step = 2.0 ** k
+    y = rng.uniform(-1, 1, (T, n)) * 127 * step
+    y[np.arange(T), rng.integers(0, n, T)] = 127 * step * rng.choice([-1, 1], T)
+    y[:, 1] = (np.arange(T) * 11 - 20.5) * step   # exact midpoints
+    y = y.astype(np.float32)
+    q, s = O.quantize_per_token(y, np.float32(1.0), "fp32", bits=8)
+    assert np.all(s == np.float32(step))
+    for t in range(T):
+        ref = torch.quantize_per_tensor(torch.from_numpy(y[t]), step, 0, torch.qint8).int_repr().numpy()
+        assert np.array_equal(q[t], ref), t
+    assert np.array_equal(O.pack_int8(q).view(np.int8), q)
+
+
+def test_int8_integer_tokens_and_error_bound():
+    rng = np.random.default_rng(201)
+    # integer tokens with absmax 127 and clip 1: step 1, codes = the integers
+    yi = rng.integers(-127, 128, size=(4, 64)).astype(np.float32)
+    yi[:, 0] = 127.0
+    q, s = O.quantize_per_token(yi, np.float32(1.0), "fp16", bits=8)
+    assert np.all(s == np.float16(1.0)) and np.array_equal(q, yi.astype(np.int8))
+    # error bound inside the clip range, range of the codes
+    y = rng.standard_normal((50, 256)).astype(np.float32) * rng.uniform(0.1, 10, (50, 1)).astype(np.float32)
+    clip = np.float32(0.9)
+    q, s = O.quantize_per_token(y, clip, "fp32", bits=8)
+    assert q.min() >= -128 and q.max() <= 127
+    sf = s.astype(np.float64)[:, None]
+    inside = np.abs(y) <= 0.9 * np.abs(y).max(axis=1, keepdims=True)
+    err = np.abs(y.astype(np.float64) - q * sf)
+    assert np.all(err[inside] <= sf.repeat(256, 1)[inside] / 2 * (1 + 2 ** -20))
+    with pytest.raises(ValueError):
+        O.quantize_per_token(y, clip, "fp32", bits=3)
