@@ -11,7 +11,7 @@ same K launches, divided by K. Default workload: hidden size 8192 with factors 6
 clip logit 3).
 
 Prints ONE JSON line on stdout. Algorithmic work per token: 2*n*(n1+n2) FLOP and
-2.5*n bytes (bf16 in + packed int4 out; 4.5*n for fp32 input). Input/output buffer sets are rotated so that consecutive steps never hit data left in
+2.5*n bytes (bf16 in + packed int4 out; 4.5*n for fp32 input; 3*n with --bits 8). Input/output buffer sets are rotated so that consecutive steps never hit data left in
 the 256 MB last-level (Infinity) cache.
 """
 from __future__ import annotations
@@ -60,7 +60,7 @@ def traffic_from_profile(workload: str, kernel: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(inp, seconds: float):
+def cpu_baseline(inp, seconds: float, bits: int = 4):
     """Time the CPU oracle (as it stands) on a bounded sample of the workload's tokens."""
     import numpy as np
     from oracle import kq_oracle as O
@@ -83,8 +83,8 @@ def cpu_baseline(inp, seconds: float):
         Y = O.transform(X, P1, inp.P2, inp.c, wl.dtype).astype(np.float32)
         if wl.per_row:
             Y = Y.reshape(-1, wl.n2)
-        q, s = O.quantize_per_token(Y, O.clip_ratio(inp.alpha), wl.scale_dtype)
-        return O.pack_int4(q), s
+        q, s = O.quantize_per_token(Y, O.clip_ratio(inp.alpha), wl.scale_dtype, bits=bits)
+        return (O.pack_int4(q) if bits == 4 else O.pack_int8(q)), s
 
     T = inp.X.shape[0]
     k = min(T, 64)
@@ -187,6 +187,8 @@ def main():
                     default="default", help="work split of the fused kernel (default: the plan's)")
     ap.add_argument("--per-launch-events", action="store_true",
                     help="also time every launch with its own event pair (diagnostic)")
+    ap.add_argument("--bits", type=int, choices=[4, 8], default=4,
+                    help="code width: 4 (packed nibbles, the default) or 8 (one byte per value)")
     ap.add_argument("--int4-gemm", type=int, nargs=3, metavar=("T", "N", "K"), default=None,
                     help="time kq_int4_gemm on random codes instead (tokens, out channels, K)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -235,17 +237,18 @@ def main():
              "generic": B.KQ_FLAG_FORCE_GENERIC}[args.split]
     if wl.per_row:  # identity left factor, one step per row of V
         plan = B.Plan(None, dev_tensor(inp.P2), None, inp.alpha, wl.scale_dtype, flags=flags,
-                      n1=wl.n1)
+                      n1=wl.n1, bits=args.bits)
     else:
         plan = B.Plan(dev_tensor(inp.P1), dev_tensor(inp.P2), c, inp.alpha, wl.scale_dtype,
-                      flags=flags)
+                      flags=flags, bits=args.bits)
     T, n = wl.T, wl.n
     nscales = T * wl.n1 if wl.per_row else T
     esize = 2 if wl.dtype == "bf16" else 4
-    set_bytes = T * n * esize + T * n // 2 + nscales * 2
+    code_bytes = n * args.bits // 8  # per token
+    set_bytes = T * n * esize + T * code_bytes + nscales * 2
     nsets = max(2, math.ceil(args.rotate_mib * 2 ** 20 / set_bytes))
     Xs = [X0] + [X0.clone() for _ in range(nsets - 1)]
-    outs = [(torch.empty((T, n // 2), dtype=torch.uint8, device=dev),
+    outs = [(torch.empty((T, code_bytes), dtype=torch.uint8, device=dev),
              torch.empty((nscales,), dtype=plan.scale_dtype, device=dev)) for _ in range(nsets)]
     stream = torch.cuda.current_stream()
     handle, sh = plan.handle, int(stream.cuda_stream)
@@ -304,7 +307,7 @@ def main():
                       "min_us": kernel_ms[0] * 1e3, "max_us": kernel_ms[-1] * 1e3}
 
     flop_tok = 2 * n * (wl.n1 + wl.n2)
-    byte_tok = (esize + 0.5) * n
+    byte_tok = esize * n + code_bytes
     tokens_per_s = T / (ms_per_step / 1e3)
     achieved_gbs = T * byte_tok / k_avg_s / 1e9
     achieved_tflops = T * flop_tok / k_avg_s / 1e12
@@ -315,7 +318,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
+        cpu = cpu_baseline(inp, args.cpu_seconds, args.bits)
         log(f"[bench] cpu oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} cores")
 
     out = {
@@ -335,7 +338,7 @@ def main():
             "workload": wl.name, "T": T, "n": n, "n1": wl.n1, "n2": wl.n2, "x_dtype": wl.dtype,
             "scale_dtype": wl.scale_dtype, "per_channel_c": inp.c is not None,
             "alpha": inp.alpha, "kernel": kname, "buffer_sets": nsets,
-            "scales_per_token": wl.n1 if wl.per_row else 1,
+            "scales_per_token": wl.n1 if wl.per_row else 1, "code_bits": args.bits,
         },
         "roofline": {
             "bound": "hbm",

@@ -74,6 +74,14 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
  * a call must have T * n1 < 2^31 rows (else KQ_ERR_UNSUPPORTED). */
 #define KQ_FLAG_PER_ROW 0x400u
 
+/* KQ_FLAG_INT8: INT8 codes instead of INT4 ("FlatQuant" page, mixed-precision settings
+ * such as W4A8): step s32 = fp32(fp32(clip * a) / 127), q = clamp(rint(fp32(y * inv)),
+ * -128, 127), one two's-complement byte per value, so `codes` holds T x n bytes (row
+ * stride n). bf16 plans of the stream kernel's shapes only: n2 in {64, 128} with n1 in
+ * {16, 32, 48, 64}, without c, or n2 = 64 with c (KQ_ERR_UNSUPPORTED otherwise); not with
+ * KQ_FLAG_PER_ROW or KQ_FLAG_FORCE_GENERIC. */
+#define KQ_FLAG_INT8 0x800u
+
 /*
  * kq_choose_factors -- factor a hidden size for the Kronecker transform.
  * Picks n1 <= n2 with n1*n2 == n minimising n1 + n2 ("FlatQuant" page, Deep Dive:
@@ -126,7 +134,8 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
  *            multiple of 16 bytes (else KQ_ERR_ALIGNMENT).
  *   T        number of tokens, >= 0. T == 0 returns KQ_OK and launches nothing.
  *   ldx      leading dimension of X in elements.
- *   codes    device, T x (n/2) bytes, row stride n/2, 16-byte aligned (written).
+ *   codes    device, T x (n/2) bytes, row stride n/2, 16-byte aligned (written); T x n
+ *            bytes, row stride n, for a KQ_FLAG_INT8 plan.
  *   scales   device, T scales of the plan's scale_dtype (written); T * n1 of them for a
  *            KQ_FLAG_PER_ROW plan.
  *   y_debug  device, T x n fp32, or NULL. When given, receives the exact fp32 Y that

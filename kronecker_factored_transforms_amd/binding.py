@@ -23,6 +23,7 @@ KQ_FLAG_SPLIT_DEEP = 0x80
 KQ_FLAG_SPLIT_STREAM = 0x100
 KQ_FLAG_SPLIT_PAIR = 0x200
 KQ_FLAG_PER_ROW = 0x400
+KQ_FLAG_INT8 = 0x800
 
 # every symbol declared in include/kq.h
 EXPORTS = (
@@ -186,10 +187,15 @@ class Plan:
     """
 
     def __init__(self, P1, P2, c=None, alpha=math.inf, scale_dtype="fp16", stream=None, flags=0,
-                 n1=None):
+                 n1=None, bits=4):
         """P1 = None means an identity left factor of size n1 (given) and one step per row
         of V (KQ_FLAG_PER_ROW): scales then have shape [T, n1]."""
         import torch
+        if bits not in (4, 8):
+            raise ValueError("bits must be 4 or 8")
+        if bits == 8:
+            flags |= KQ_FLAG_INT8
+        self.bits = bits
         if P1 is None:
             if n1 is None:
                 raise ValueError("n1 is required with an identity left factor (P1=None)")
@@ -222,7 +228,7 @@ class Plan:
             raise ValueError("X must be [T, n] of the plan's dtype with unit column stride")
         T = X.shape[0]
         if out is None:
-            codes = torch.empty((T, self.n // 2), dtype=torch.uint8, device=X.device)
+            codes = torch.empty((T, self.n * self.bits // 8), dtype=torch.uint8, device=X.device)
             scales = torch.empty((T, self.n1) if self.per_row else (T,), dtype=self.scale_dtype,
                                  device=X.device)
         else:

@@ -115,6 +115,7 @@ kq_status create_rows_plan(kq_plan **out, int n1, int n2, kq_dtype scale_dtype, 
   p->kname = fv->name;
   p->launch = fv->launch;
   p->per_row = 1;
+  p->bits = 4;
   kq_status st = KQ_OK;
   std::vector<uint16_t> h2((size_t)n2 * n2), a2((size_t)n2 * n2);
   int dev = 0, ncu = 0, per_cu = 0;
@@ -162,6 +163,10 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
     return create_rows_plan(out, n1, n2, scale_dtype, P2, alpha, static_cast<hipStream_t>(stream));
   }
   if (!P1 || !P2) return KQ_ERR_INVALID_ARG;
+  const int bits = (flags & KQ_FLAG_INT8) ? 8 : 4;
+  // INT8 codes: bf16 MFMA kernels only (no generic fallback)
+  if (bits == 8 && (x_dtype != KQ_BF16 || (flags & KQ_FLAG_FORCE_GENERIC))) return KQ_ERR_INVALID_ARG;
+  flags &= ~KQ_FLAG_INT8;
   const unsigned split_flags =
       flags & (KQ_FLAG_SPLIT_REG1 | KQ_FLAG_SPLIT_REG2 | KQ_FLAG_SPLIT_COLS | KQ_FLAG_SPLIT_DEEP |
                KQ_FLAG_SPLIT_STREAM | KQ_FLAG_SPLIT_PAIR);
@@ -184,7 +189,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   int kind = -1;
   const kq_fused_variant *fv = nullptr;
   if (x_dtype == KQ_BF16 && !(flags & KQ_FLAG_FORCE_GENERIC)) {
-    fv = kq_fused_lookup(n1, n2, c != nullptr, split);
+    fv = kq_fused_lookup(n1, n2, c != nullptr, split, bits);
     if (fv) {
       fn = fv->launch;
       kname = fv->name;
@@ -193,7 +198,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
     }
   }
   if (!fn) {
-    if (split || n > kq_generic_max_n()) return KQ_ERR_UNSUPPORTED;
+    if (split || bits == 8 || n > kq_generic_max_n()) return KQ_ERR_UNSUPPORTED;
     fn = kq_generic_launcher(&kname, &ksym);
     kind = KQ_KIND_GENERIC;
   }
@@ -210,6 +215,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   p->kind = kind;
   p->kname = kname;
   p->launch = fn;
+  p->bits = bits;
 
   kq_status st = KQ_OK;
   const size_t es = elem_size(x_dtype);
@@ -256,7 +262,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
     // per token, 2-wave workgroups) finishes a small batch sooner (measured on MI355X:
     // 64 tokens of 64x128 in 5.4 us vs 9.0 us; break-even near 1024 tokens).
     if (split == 0 && fv->split == KQ_SPLIT_STREAM) {
-      const kq_fused_variant *sv = kq_fused_lookup(n1, n2, c != nullptr, KQ_SPLIT_PAIR);
+      const kq_fused_variant *sv = kq_fused_lookup(n1, n2, c != nullptr, KQ_SPLIT_PAIR, bits);
       int small_per_cu = 0;
       if (sv) {
         std::vector<uint16_t> b2(kq_fused_p2op_elems(n2));

@@ -122,9 +122,11 @@ struct TokenScale {
   float inv;
 };
 
-__device__ __forceinline__ TokenScale token_scale(float amax, float clip, int scale_fp16) {
+// qmax = 2^(b-1) - 1: 7 for INT4 codes, 127 for INT8 codes
+__device__ __forceinline__ TokenScale token_scale(float amax, float clip, int scale_fp16,
+                                                  float qmax = 7.0f) {
   TokenScale t;
-  t.s32 = __fdiv_rn(__fmul_rn(clip, amax), 7.0f);
+  t.s32 = __fdiv_rn(__fmul_rn(clip, amax), qmax);
   t.s16 = (_Float16)t.s32;
   const float sf = scale_fp16 ? (float)t.s16 : t.s32;
   t.inv = (sf == 0.f) ? 0.f : __fdiv_rn(1.0f, sf);
@@ -451,6 +453,51 @@ __device__ __forceinline__ void quant_tile(const f32x4 (&yacc)[NT][MT], float in
     }
 }
 
+// INT8: 4 consecutive values -> one dword of two's-complement bytes (value e in byte e).
+// Adding 1.5*2^23 in fp32 rounds v = fp32(y * inv) to the nearest integer, ties to even,
+// and leaves q in the low mantissa bits (|v| < 2^22); clamping the bit pattern clamps q to
+// [-128, 127], and its low byte is then q as a two's-complement byte.
+__device__ __forceinline__ uint32_t quant4x8(float y0, float y1, float y2, float y3, float inv) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23, bit pattern 0x4B400000
+  constexpr int kLo = 0x4B400000 - 128, kHi = 0x4B400000 + 127;
+  const float y[4] = {y0, y1, y2, y3};
+  uint32_t u[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    u[e] = (uint32_t)min(max(__float_as_int(__fadd_rn(__fmul_rn(y[e], inv), kMagic)), kLo), kHi);
+  const uint32_t lo = __builtin_amdgcn_perm(u[1], u[0], 0x0C0C0400u);  // [u0.b0, u1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(u[3], u[2], 0x04000C0Cu);  // [0, 0, u2.b0, u3.b0]
+  return lo | hi;
+}
+
+// INT8 codes of a wave's Y tile (lane holds yacc[m2][nt] = 4 consecutive columns of row
+// 16 nt + lr): w[nt][m2] holds those 4 values as bytes.
+template <int MT, int NT>
+__device__ __forceinline__ void quant_tile8(const f32x4 (&yacc)[NT][MT], float inv,
+                                            uint32_t (&w)[MT][NT]) {
+#pragma unroll
+  for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+    for (int m2 = 0; m2 < NT; ++m2)
+      w[nt][m2] = quant4x8(yacc[m2][nt][0], yacc[m2][nt][1], yacc[m2][nt][2], yacc[m2][nt][3], inv);
+}
+
+// INT8 code rows: lane stores 4 NT bytes (its LPL consecutive columns) of row 16 nt + lr
+template <int N1, int N2>
+__device__ __forceinline__ void store_codes8(uint8_t *codes, int64_t tok,
+                                             const uint32_t (*w)[N2 / 16], int lr, int g) {
+  uint8_t *crow = codes + tok * (int64_t)(N1 * N2);
+#pragma unroll
+  for (int nt = 0; nt < N1 / 16; ++nt) {
+    uint8_t *dst = crow + (nt * 16 + lr) * N2 + g * (N2 / 4);
+#pragma unroll
+    for (int q = 0; q < N2 / 64; ++q) {
+      const u32x4_t v = {w[nt][4 * q], w[nt][4 * q + 1], w[nt][4 * q + 2], w[nt][4 * q + 3]};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst + 16 * q));
+    }
+  }
+}
+
 template <int N1, int N2>
 __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t tok, const uint32_t (*w)[N2 / 32],
                                             int lr, int g) {
@@ -468,7 +515,7 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t tok, const u
   }
 }
 
-template <int N1, int N2, bool HAS_C, bool YDBG>
+template <int N1, int N2, bool HAS_C, bool YDBG, int BITS = 4>
 __global__ __launch_bounds__(512) void kq_stream_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
@@ -539,16 +586,19 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
   __syncthreads();  // P2 visible (this also waits for every load issued so far)
   const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
 
-  uint32_t pend[C::MT][C::NT / 2];  // codes of the previous token, stored one step late
+  // codes of the previous token, stored one step late (8 or 4 values per dword)
+  uint32_t pend[C::MT][BITS == 4 ? C::NT / 2 : C::NT];
   TokenScale pend_s{0.f, (_Float16)0.f, 0.f};
   int64_t pend_tok = -1;
+  auto store_pending = [&]() {
+    if constexpr (BITS == 4) store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
+    else store_codes8<N1, N2>(codes, pend_tok, pend, lr, g);
+    if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
+  };
 
   for (; tok < T; tok += stride) {
     wait_and_fence<kWaitVm0>();  // this token's tile (and older stores) have landed
-    if (pend_tok >= 0) {
-      store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
-      if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
-    }
+    if (pend_tok >= 0) store_pending();
     // The two waves of a SIMD alternate between MFMA-heavy stages and the VALU-heavy
     // quantizer: a higher issue priority for the MFMA phase keeps the matrix core fed
     // while the other wave's VALU work fills the gaps (measured on MI355X: about 2 %).
@@ -645,8 +695,10 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
     // the absmax and the clamp decision are wave-uniform: broadcast them so that the
     // choice below is one scalar branch, not a per-lane select
     const float amax = wave_max_uniform(m);
-    const TokenScale ts = token_scale(amax, clip, scale_fp16);
-    if (__builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, ts.s32) ? 1 : 0)) {
+    const TokenScale ts = token_scale(amax, clip, scale_fp16, BITS == 4 ? 7.0f : 127.0f);
+    if constexpr (BITS == 8) {
+      quant_tile8<C::MT, C::NT>(yacc, ts.inv, pend);
+    } else if (__builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, ts.s32) ? 1 : 0)) {
       quant_tile<true, C::MT, C::NT>(yacc, ts.inv, pend);
     } else {
       quant_tile<false, C::MT, C::NT>(yacc, ts.inv, pend);
@@ -663,10 +715,7 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
       }
     }
   }
-  if (pend_tok >= 0) {
-    store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
-    if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
-  }
+  if (pend_tok >= 0) store_pending();
 }
 
 // ------------------------------------------------------------------------------------
@@ -1302,7 +1351,7 @@ hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
   return hipGetLastError();
 }
 
-template <int N1, int N2, bool HAS_C>
+template <int N1, int N2, bool HAS_C, int BITS = 4>
 hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
                          void *scales, float *y_debug, hipStream_t stream) {
   using C = StreamCfg<N1, N2, HAS_C>;
@@ -1310,7 +1359,8 @@ hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
   // the debug output has its own instantiation so that the timed kernel keeps its
   // registers; both compute Y with the same per-accumulator MFMA order
-  auto k = y_debug ? &kq_stream_kernel<N1, N2, HAS_C, true> : &kq_stream_kernel<N1, N2, HAS_C, false>;
+  auto k = y_debug ? &kq_stream_kernel<N1, N2, HAS_C, true, BITS>
+                   : &kq_stream_kernel<N1, N2, HAS_C, false, BITS>;
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
@@ -1334,7 +1384,7 @@ hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
 }
 
 #define KQ_PAIR(A, B)                                                                  \
-  kq_fused_variant{A, B, false, KQ_SPLIT_PAIR, (B) / 2, PairCfg<A, B>::THREADS,          \
+  kq_fused_variant{A, B, false, KQ_SPLIT_PAIR, 4, (B) / 2, PairCfg<A, B>::THREADS,          \
                    &launch_pair<A, B>,                                                 \
                    reinterpret_cast<const void *>(&kq_pair_kernel<A, B, false>),       \
                    "fused_mfma_bf16_pair_" #A "x" #B}
@@ -1353,25 +1403,30 @@ hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
 }
 
 #define KQ_STREAM(A, B)                                                                \
-  kq_fused_variant{A, B, false, KQ_SPLIT_STREAM, (B), StreamCfg<A, B>::THREADS,          \
+  kq_fused_variant{A, B, false, KQ_SPLIT_STREAM, 4, (B), StreamCfg<A, B>::THREADS,          \
                    &launch_stream<A, B, false>,                                        \
                    reinterpret_cast<const void *>(&kq_stream_kernel<A, B, false, false>), \
                    "fused_mfma_bf16_stream_" #A "x" #B}
+#define KQ_STREAM8(A, B, HC, SUF)                                                      \
+  kq_fused_variant{A, B, HC, KQ_SPLIT_STREAM, 8, (B), StreamCfg<A, B, HC>::THREADS,       \
+                   &launch_stream<A, B, HC, 8>,                                        \
+                   reinterpret_cast<const void *>(&kq_stream_kernel<A, B, HC, false, 8>), \
+                   "fused_mfma_bf16_stream_" #A "x" #B SUF "_int8"}
 #define KQ_STREAM_C(A, B)                                                              \
-  kq_fused_variant{A, B, true, KQ_SPLIT_STREAM, (B), StreamCfg<A, B, true>::THREADS,     \
+  kq_fused_variant{A, B, true, KQ_SPLIT_STREAM, 4, (B), StreamCfg<A, B, true>::THREADS,     \
                    &launch_stream<A, B, true>,                                         \
                    reinterpret_cast<const void *>(&kq_stream_kernel<A, B, true, false>), \
                    "fused_mfma_bf16_stream_" #A "x" #B "_c"}
 #define KQ_REG(A, B, WPT, HC, SUF)                                                     \
-  kq_fused_variant{A, B, HC, WPT, (B) / (WPT), kThreads, &launch_reg<A, B, WPT, HC, false>, \
+  kq_fused_variant{A, B, HC, WPT, 4, (B) / (WPT), kThreads, &launch_reg<A, B, WPT, HC, false>, \
                    reinterpret_cast<const void *>(&kq_reg_kernel<A, B, WPT, HC, false>), \
                    "fused_mfma_bf16_reg" #WPT "_" #A "x" #B SUF}
 #define KQ_DEEP(A, B, HC, SUF)                                                         \
-  kq_fused_variant{A, B, HC, KQ_SPLIT_DEEP, (B), kThreads, &launch_reg<A, B, 1, HC, true>, \
+  kq_fused_variant{A, B, HC, KQ_SPLIT_DEEP, 4, (B), kThreads, &launch_reg<A, B, 1, HC, true>, \
                    reinterpret_cast<const void *>(&kq_reg_kernel<A, B, 1, HC, true>),   \
                    "fused_mfma_bf16_deep_" #A "x" #B SUF}
 #define KQ_COLS(A, B, HC, SUF)                                                         \
-  kq_fused_variant{A, B, HC, KQ_SPLIT_COLS, 32, ColsCfg<A, B, HC>::THREADS, &launch_cols<A, B, HC>, \
+  kq_fused_variant{A, B, HC, KQ_SPLIT_COLS, 4, 32, ColsCfg<A, B, HC>::THREADS, &launch_cols<A, B, HC>, \
                    reinterpret_cast<const void *>(&kq_cols_kernel<A, B, HC>),          \
                    "fused_mfma_bf16_cols_" #A "x" #B SUF}
 #define KQ_ALL1(A, B)                                                                  \
@@ -1411,6 +1466,12 @@ const kq_fused_variant kVariants[] = {
     KQ_DEEP(64, 128, false, ""), KQ_DEEP(64, 64, false, ""), KQ_DEEP(64, 64, true, "_c"),
     KQ_STREAM(16, 64), KQ_STREAM(32, 64), KQ_STREAM(48, 64), KQ_STREAM(64, 64),
     KQ_STREAM_C(16, 64), KQ_STREAM_C(32, 64), KQ_STREAM_C(48, 64), KQ_STREAM_C(64, 64),
+    // INT8 codes (stream kernel shapes)
+    KQ_STREAM8(16, 64, false, ""), KQ_STREAM8(32, 64, false, ""), KQ_STREAM8(48, 64, false, ""),
+    KQ_STREAM8(64, 64, false, ""), KQ_STREAM8(16, 128, false, ""), KQ_STREAM8(32, 128, false, ""),
+    KQ_STREAM8(48, 128, false, ""), KQ_STREAM8(64, 128, false, ""),
+    KQ_STREAM8(16, 64, true, "_c"), KQ_STREAM8(32, 64, true, "_c"), KQ_STREAM8(48, 64, true, "_c"),
+    KQ_STREAM8(64, 64, true, "_c"),
     KQ_STREAM(16, 128), KQ_STREAM(32, 128), KQ_STREAM(48, 128),
     KQ_PAIR(16, 64), KQ_PAIR(32, 64), KQ_PAIR(48, 64), KQ_PAIR(64, 64),
     KQ_PAIR(16, 128), KQ_PAIR(32, 128), KQ_PAIR(48, 128), KQ_PAIR(64, 128),
@@ -1418,9 +1479,10 @@ const kq_fused_variant kVariants[] = {
 
 }  // namespace
 
-const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split) {
+const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split, int bits) {
   for (const kq_fused_variant &e : kVariants)
-    if (e.n1 == n1 && e.n2 == n2 && e.has_c == has_c && (split == 0 || e.split == split))
+    if (e.n1 == n1 && e.n2 == n2 && e.has_c == has_c && e.bits == bits &&
+        (split == 0 || e.split == split))
       return &e;
   return nullptr;
 }
@@ -1428,10 +1490,10 @@ const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split) {
 
 namespace {
 const kq_fused_variant kRowsVariants[] = {
-    kq_fused_variant{0, 64, false, KQ_SPLIT_ROWS, 0, RowsCfg<64>::THREADS, &launch_rows<64>,
+    kq_fused_variant{0, 64, false, KQ_SPLIT_ROWS, 4, 0, RowsCfg<64>::THREADS, &launch_rows<64>,
                      reinterpret_cast<const void *>(&kq_rows_kernel<64, false>),
                      "fused_mfma_bf16_rows_64"},
-    kq_fused_variant{0, 128, false, KQ_SPLIT_ROWS, 0, RowsCfg<128>::THREADS, &launch_rows<128>,
+    kq_fused_variant{0, 128, false, KQ_SPLIT_ROWS, 4, 0, RowsCfg<128>::THREADS, &launch_rows<128>,
                      reinterpret_cast<const void *>(&kq_rows_kernel<128, false>),
                      "fused_mfma_bf16_rows_128"},
 };

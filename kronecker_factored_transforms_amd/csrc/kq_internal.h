@@ -47,6 +47,7 @@ struct kq_plan {
   int64_t small_max_T;
   // 1: identity left factor and one step per row of V (T * n1 scales)
   int per_row;
+  int bits;             // code width: 4 or 8
 };
 
 // ---- fused MFMA family (kq_fused.hip) ----
@@ -61,6 +62,7 @@ struct kq_fused_variant {
   int n1, n2;
   bool has_c;
   int split;      // KQ_SPLIT_*
+  int bits;       // code width: 4 (INT4, two per byte) or 8 (INT8)
   int p2_block;   // output columns per P2 operand block (kq_fused_arrange_p2)
   int threads;    // workgroup size
   kq_launch_fn launch;
@@ -68,8 +70,9 @@ struct kq_fused_variant {
   const char *name;
 };
 
-// The variant for (n1, n2, has_c) with the given split (0: the default one), or nullptr.
-const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split);
+// The variant for (n1, n2, has_c) with the given split (0: the default one) and code width,
+// or nullptr.
+const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split, int bits = 4);
 // The rows kernel (identity left factor, one step per row of V) for n2, or nullptr.
 const kq_fused_variant *kq_fused_lookup_rows(int n2);
 void kq_fused_arrange_p2_rows(const uint16_t *P2, int n2, uint16_t *out);

@@ -115,6 +115,16 @@ def test_per_row_flag_is_validated_on_the_host(L):
         assert st == B.KQ_ERR_INVALID_ARG and h is None, kw
 
 
+def test_int8_flag_is_validated_on_the_host(L):
+    for kw in (dict(flags=B.KQ_FLAG_INT8, xd=B.KQ_FP32),
+               dict(flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_FORCE_GENERIC),
+               dict(flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_PER_ROW, p1=None)):
+        st, h = _create_raw(L, 64, 128, **kw)
+        assert st == B.KQ_ERR_INVALID_ARG and h is None, kw
+    st, h = _create_raw(L, 64, 128, flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_SPLIT_COLS)
+    assert st == B.KQ_ERR_UNSUPPORTED and h is None
+
+
 def test_create_reports_unsupported_shapes(L):
     # fp32 beyond the generic kernel's on-chip limit and no MFMA variant for it
     st, h = _create_raw(L, 256, 128, xd=B.KQ_FP32)

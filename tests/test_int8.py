@@ -1,0 +1,74 @@
+"""GPU tests of INT8 plans (KQ_FLAG_INT8): the same transform, codes from the b = 8
+quantizer (divisor 127, clamp to [-128, 127], one byte per value). Codes and scales must
+be bit-exact against the oracle quantizer on the GPU's own fp32 Y; Y within the bf16
+tolerance of the fp64 oracle."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import kqtest as K
+from kronecker_factored_transforms_amd import binding as B
+from kronecker_factored_transforms_amd import synth as S
+from oracle import kq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _plan(inp, dev="cuda:0", scale_dtype=None):
+    X, P1, P2, c = K.device_inputs(inp, dev)
+    return B.Plan(P1, P2, c, inp.alpha, scale_dtype or inp.wl.scale_dtype, bits=8), X
+
+
+def _check(inp, codes, scales, y, clip, token_ids=None, scale_dtype=None):
+    X = inp.X if token_ids is None else inp.X[token_ids]
+    Y = O.transform(X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
+    rel = K.rel_l2(y, Y)
+    assert rel <= K.TOL[inp.wl.dtype], f"rel-L2 {rel:.3e}"
+    q, s = O.quantize_per_token(np.ascontiguousarray(y, np.float32), np.float32(clip),
+                                scale_dtype or inp.wl.scale_dtype, bits=8)
+    assert np.array_equal(np.asarray(codes), O.pack_int8(q)), "codes differ"
+    assert np.array_equal(np.asarray(scales).view(np.uint8), s.view(np.uint8)), "scales differ"
+
+
+SHAPES = [(64, 128, False), (64, 64, True), (32, 128, False), (16, 64, True), (48, 64, False),
+          (16, 128, False)]
+
+
+@pytest.mark.parametrize("n1,n2,with_c", SHAPES)
+@pytest.mark.parametrize("T", [1, 203])
+def test_int8_parity(gpu, n1, n2, with_c, T):
+    import torch
+    base = S.WORKLOADS["attn_n4096"] if with_c else S.WORKLOADS["hidden_n8192"]
+    wl = replace(base, n1=n1, n2=n2, n_outliers=4, pivot_channels=0)
+    inp = S.make(wl, T=T)
+    plan, X = _plan(inp)
+    assert plan.kernel.endswith("_int8") and plan.kernel_for(T) == plan.kernel
+    codes, scales, y = K.run(plan, X, y_debug=True)
+    codes2, scales2 = K.run(plan, X, y_debug=False)
+    assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
+    assert tuple(codes.shape) == (T, n1 * n2)
+    _check(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+def test_int8_full_size_sampled(gpu):
+    import torch
+    inp = S.make("hidden_n8192")
+    plan, X = _plan(inp)
+    codes, scales = K.run(plan, X, y_debug=False)
+    rng = np.random.default_rng(8)
+    ids = np.unique(np.concatenate([[0, inp.wl.T - 1], rng.integers(0, inp.wl.T, 200)]))
+    sub = S.make("hidden_n8192", token_ids=ids)
+    Xs = K.torch_from(sub.X, "bf16").to("cuda:0")
+    cs, ss, ys = K.run(plan, Xs, y_debug=True)
+    idx = torch.from_numpy(ids).cuda()
+    assert torch.equal(codes[idx], cs) and torch.equal(scales[idx], ss)
+    _check(sub, cs.cpu().numpy(), K.np_scales(ss), ys.cpu().numpy(), plan.clip)
+
+
+def test_int8_unsupported_shapes(gpu):
+    inp = S.make("down_proj_n14336", T=4)
+    X, P1, P2, c = K.device_inputs(inp)
+    with pytest.raises(B.KqError) as e:
+        B.kq_create(112, 128, "bf16", "fp16", P1, P2, c, 1.0, None, B.KQ_FLAG_INT8)
+    assert e.value.status == B.KQ_ERR_UNSUPPORTED
