@@ -962,6 +962,14 @@ __device__ __forceinline__ uint32_t quant4(const float (&y)[4], float inv) {
   return ((u[0] | (u[1] << 4) | (u[2] << 8) | (u[3] << 12)) ^ 0x8888u);
 }
 
+// Scale of row (lr & 3) of each lane's quad; the other rows' steps arrive by quad
+// broadcasts, so each lane computes one step instead of four.
+template <int R>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), R | (R << 2) | (R << 4) | (R << 6),
+                                                 0xF, 0xF, false));
+}
+
 template <int N2, bool YDBG>
 __global__ __launch_bounds__(512) void kq_rows_kernel(
     const __bf16 *__restrict__ X, int64_t T, int n1, int64_t ldx,
@@ -974,30 +982,45 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, lr = lane & 15;
-  const int64_t R = T * (int64_t)n1;              // rows
-  const int64_t ntiles = (R + 15) / 16;
-  const int64_t stride = (int64_t)gridDim.x * C::WAVES;
-  const int64_t first = (int64_t)blockIdx.x * C::WAVES + wave;
+  // rows: R = T n1 < 2^31 (checked on the host), so row and tile indices are 32-bit
+  const uint32_t uT = (uint32_t)T, un1 = (uint32_t)n1;
+  const uint32_t R = uT * un1;
+  const uint32_t ntiles = (R + 15u) / 16u;
+  const uint32_t stride = gridDim.x * C::WAVES;
+  const uint32_t first = blockIdx.x * C::WAVES + wave;
+  const int ntl = first < ntiles ? (int)((ntiles - 1u - first) / stride) + 1 : 0;  // my tiles
 
-  // DMA of tile `tl` into slot b: instruction j fills tile rows RPI j .. RPI j + RPI - 1;
-  // lane i lands at row RPI j + i / PPR, position i % PPR (piece (i % PPR) ^ swz(row)).
-  // Rows past the end read the last row (their results are not stored).
-  // (R < 2^31 is checked on the host: 32-bit row arithmetic)
-  auto dma_tile = [&](int64_t tl, int b) {
+  // DMA cursor: for instruction j, the (token, head) of this lane's row in the next tile
+  // to load. Instruction j fills tile rows RPI j .. RPI j + RPI - 1; lane i lands at row
+  // RPI j + i / PPR, position i % PPR (piece (i % PPR) ^ swz(row)). The cursor moves on
+  // by stride * 16 rows per tile without a division. Rows past the end (token >= T) read
+  // the last row; their results are not stored.
+  const uint32_t adv = stride * 16u;
+  const uint32_t adv_t = adv / un1, adv_h = adv - adv_t * un1;
+  uint32_t ct[C::LOADS], ch[C::LOADS];
+#pragma unroll
+  for (int j = 0; j < C::LOADS; ++j) {
+    const uint32_t r = first * 16u + (uint32_t)(j * C::RPI + lane / C::PPR);
+    ct[j] = r / un1;
+    ch[j] = r - ct[j] * un1;
+  }
+  auto dma_next = [&](int b) {
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) {
-      const int Rl = j * C::RPI + lane / C::PPR;
-      uint32_t r = (uint32_t)(tl * 16) + (uint32_t)Rl;
-      r = r < (uint32_t)R ? r : (uint32_t)R - 1u;
-      const uint32_t t = r / (uint32_t)n1, hd = r - t * (uint32_t)n1;
-      const int piece = (lane % C::PPR) ^ C::swz(Rl);
-      dma16_addr<true>(X + (int64_t)t * ldx + hd * N2 + piece * 8,
+      const bool past = ct[j] >= uT;
+      const uint32_t t = past ? uT - 1u : ct[j], hd = past ? un1 - 1u : ch[j];
+      const int piece = (lane % C::PPR) ^ C::swz(j * C::RPI + lane / C::PPR);
+      dma16_addr<true>(X + (uint64_t)t * (uint64_t)ldx + (hd * N2 + piece * 8),
                        lds_addr(s_tile[wave][b] + j * 1024));
+      ch[j] += adv_h;
+      const uint32_t wrap = ch[j] >= un1 ? 1u : 0u;  // branch-free carry into the token
+      ch[j] -= wrap * un1;
+      ct[j] += adv_t + wrap;
     }
   };
 #pragma unroll
   for (int k = 0; k < C::SLOTS; ++k)
-    if (first + k * stride < ntiles) dma_tile(first + k * stride, k);
+    if (k < ntl) dma_next(k);
 
   bf16x8 p2r[C::KS][C::NT];  // all of P2's B operands, resident in registers
 #pragma unroll
@@ -1008,16 +1031,31 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
   // compiler's own waits for these loads know nothing of the DMAs
   wait_and_fence<kWaitVm0>();
 
-  uint32_t pend[4] = {0u, 0u, 0u, 0u};  // codes of the previous tile's 4 rows of this lane
-  TokenScale pend_s[4];
-  int64_t pend_row = -1;                // first of those rows (row 16 tile + 4 g)
+  // the previous tile's results: this lane's code word of each of its 4 rows (row
+  // 16 tile + 4 g + r), and the step of row 16 tile + 4 g + (lr & 3)
+  uint32_t pend[4] = {0u, 0u, 0u, 0u};
+  TokenScale pend_s{};
+  uint32_t pend_row = 0;  // 16 tile + 4 g
 
-  int it = 0;
-  for (int64_t tl = first; tl < ntiles; tl += stride, ++it) {
+  auto store_pend = [&](bool tail) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t row = pend_row + (uint32_t)r;
+      if (!tail || row < R) {
+        uint8_t *dst = codes + (uint64_t)row * (N2 / 2) + lr * (C::NT / 2);
+        if constexpr (N2 == 128) __builtin_nontemporal_store(pend[r], reinterpret_cast<uint32_t *>(dst));
+        else __builtin_nontemporal_store((uint16_t)pend[r], reinterpret_cast<uint16_t *>(dst));
+      }
+    }
+    const uint32_t srow = pend_row + (uint32_t)(lr & 3);
+    if (lr < 4 && (!tail || srow < R)) store_scale(scales, srow, pend_s, scale_fp16);
+  };
+
+  for (int it = 0; it < ntl; ++it) {
     const int b = it % C::SLOTS;
-    // this tile has landed once at most the later tiles' loads (up to SLOTS - 1 tiles, all
-    // issued before any later store) are in flight: loads complete in issue order
-    const int64_t later = (ntiles - 1 - tl) / stride;  // tiles of this wave after this one
+    // this tile has landed once at most the later tiles' loads (up to SLOTS - 1 tiles) are
+    // in flight: loads complete in issue order, and stores are not counted on
+    const int later = ntl - 1 - it;
     if (later >= 3) wait_and_fence<C::template wait_imm<3>>();
     else if (later == 2) wait_and_fence<C::template wait_imm<2>>();
     else if (later == 1) wait_and_fence<C::template wait_imm<1>>();
@@ -1028,19 +1066,9 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
     for (int ks = 0; ks < C::KS; ++ks)
       av[ks] = *reinterpret_cast<const bf16x8 *>(tile + lr * C::RB + (((ks * 4 + g) ^ C::swz(lr)) * 16));
     wait_and_fence<kWaitLgkm0>();  // slot b is free again
-    if (pend_row >= 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = pend_row + r;
-        if (row < R) {
-          uint8_t *dst = codes + row * (N2 / 2) + lr * (C::NT / 2);
-          if constexpr (N2 == 128) __builtin_nontemporal_store(pend[r], reinterpret_cast<uint32_t *>(dst));
-          else __builtin_nontemporal_store((uint16_t)pend[r], reinterpret_cast<uint16_t *>(dst));
-          if (lr == 0) store_scale(scales, row, pend_s[r], scale_fp16);
-        }
-      }
-    }
-    if (tl + C::SLOTS * stride < ntiles) dma_tile(tl + C::SLOTS * stride, b);
+    // tiles stored inside the loop are never a wave's last tile, hence never ragged
+    if (it > 0) store_pend(false);
+    if (later >= C::SLOTS) dma_next(b);
 
     f32x4 zacc[C::NT];
 #pragma unroll
@@ -1052,29 +1080,37 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
         zacc[nt] = mfma(av[ks], p2r[ks][nt], zacc[nt]);
 
     // lane holds Y[row 16 tl + 4 g + r][lr NT + nt]; absmax per row over the 16 lanes of g
-    const int64_t row0 = tl * 16 + 4 * g;
+    const uint32_t tl = first + (uint32_t)it * stride;
+    const uint32_t row0 = tl * 16u + 4u * (uint32_t)g;
+    float m[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float m = 0.f;
+      float v = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) m = fmaxf(m, fabsf(zacc[nt][r]));
-      m = dpp_step<0xB1>(m);
-      m = dpp_step<0x4E>(m);
-      m = dpp_step<0x141>(m);
-      m = dpp_step<0x140>(m);
-      const TokenScale ts = token_scale(m, clip, scale_fp16);
+      for (int nt = 0; nt < C::NT; ++nt) v = fmaxf(v, fabsf(zacc[nt][r]));
+      v = dpp_step<0xB1>(v);
+      v = dpp_step<0x4E>(v);
+      v = dpp_step<0x141>(v);
+      m[r] = dpp_step<0x140>(v);
+    }
+    const int rr = lr & 3;
+    const float mr = rr == 0 ? m[0] : rr == 1 ? m[1] : rr == 2 ? m[2] : m[3];
+    pend_s = token_scale(mr, clip, scale_fp16);
+    const float inv[4] = {quad_bcast<0>(pend_s.inv), quad_bcast<1>(pend_s.inv),
+                          quad_bcast<2>(pend_s.inv), quad_bcast<3>(pend_s.inv)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
       if constexpr (N2 == 128) {
         const float yv[8] = {zacc[0][r], zacc[1][r], zacc[2][r], zacc[3][r],
                              zacc[4][r], zacc[5][r], zacc[6][r], zacc[7][r]};
-        pend[r] = quant8<true>(yv, ts.inv);
+        pend[r] = quant8<true>(yv, inv[r]);
       } else {
         const float yv[4] = {zacc[0][r], zacc[1][r], zacc[2][r], zacc[3][r]};
-        pend[r] = quant4(yv, ts.inv);
+        pend[r] = quant4(yv, inv[r]);
       }
-      pend_s[r] = ts;
       if constexpr (YDBG) {
         if (row0 + r < R) {
-          float *yp = ydbg + (row0 + r) * N2 + lr * C::NT;
+          float *yp = ydbg + (uint64_t)(row0 + r) * N2 + lr * C::NT;
 #pragma unroll
           for (int q = 0; q < C::NT / 4; ++q)
             reinterpret_cast<float4 *>(yp)[q] =
@@ -1084,18 +1120,7 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
     }
     pend_row = row0;
   }
-  if (pend_row >= 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = pend_row + r;
-      if (row < R) {
-        uint8_t *dst = codes + row * (N2 / 2) + lr * (C::NT / 2);
-        if constexpr (N2 == 128) __builtin_nontemporal_store(pend[r], reinterpret_cast<uint32_t *>(dst));
-        else __builtin_nontemporal_store((uint16_t)pend[r], reinterpret_cast<uint16_t *>(dst));
-        if (lr == 0) store_scale(scales, row, pend_s[r], scale_fp16);
-      }
-    }
-  }
+  if (ntl > 0) store_pend(true);
 }
 
 // ------------------------------------------------------------------------------------
