@@ -70,7 +70,7 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
  * T * n1 values (row i of token t at t * n1 + i) and codes keep the row-major Y order.
  * This is the per-head key/value transform ahead of a quantized KV cache ("FlatQuant"
  * page, Symbol Map: P_h, P_v; Transformer integration). bf16 only, n2 in {64, 128}, any
- * n1 >= 1, no c, no other flag (KQ_ERR_INVALID_ARG / KQ_ERR_UNSUPPORTED otherwise);
+ * 1 <= n1 <= 2^20, no c, no other flag (KQ_ERR_INVALID_ARG / KQ_ERR_UNSUPPORTED otherwise);
  * a call must have T * n1 < 2^31 rows (else KQ_ERR_UNSUPPORTED). */
 #define KQ_FLAG_PER_ROW 0x400u
 

@@ -102,7 +102,7 @@ kq_status kq_choose_factors(int64_t n, int *n1, int *n2) {
 kq_status create_rows_plan(kq_plan **out, int n1, int n2, kq_dtype scale_dtype, const void *P2,
                            float alpha, hipStream_t s) {
   const kq_fused_variant *fv = kq_fused_lookup_rows(n2);
-  if (!fv) return KQ_ERR_UNSUPPORTED;
+  if (!fv || n1 > (1 << 20)) return KQ_ERR_UNSUPPORTED;  // rows kernel: n1 <= 2^20
   kq_plan *p = static_cast<kq_plan *>(calloc(1, sizeof(kq_plan)));
   if (!p) return KQ_ERR_OUT_OF_MEMORY;
   p->n1 = n1;

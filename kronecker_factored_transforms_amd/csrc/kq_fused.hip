@@ -66,10 +66,21 @@ __device__ __forceinline__ float wave_max(float v) {
 // Max over the wave of a non-negative value, returned wave-uniform: within each row of 16
 // lanes with DPP (quad swaps, half-row and row mirrors), then the four row maxima read
 // into scalars. No LDS round trips.
+// Maxima of absolute values (x >= 0, never NaN: the in-lane maxima start from 0 and
+// fmaxf drops NaN operands). For such x the float order is the order of the bit patterns
+// as unsigned integers, so the cross-lane steps use the integer max, which takes its DPP
+// operand directly (every DPP pattern used here reads a valid lane: no "old" value).
+__device__ __forceinline__ float max_nn(float a, float b) {
+  const uint32_t x = __float_as_uint(a), y = __float_as_uint(b);
+  return __uint_as_float(x > y ? x : y);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp_step(float v) {
-  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
-  return fmaxf(v, __int_as_float(o));
+  return max_nn(v, dpp_read<CTRL>(v));
 }
 __device__ __forceinline__ float wave_max_uniform(float v) {
   v = dpp_step<0xB1>(v);   // quad_perm [1,0,3,2]
@@ -81,7 +92,7 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(i, 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(i, 32));
   const float r3 = __int_as_float(__builtin_amdgcn_readlane(i, 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  return max_nn(max_nn(r0, r1), max_nn(r2, r3));
 }
 
 __device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b) {
@@ -923,33 +934,50 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
 // With P1 = I the rows of V never mix: row r (token t = r / n1, head i = r % n1) is
 // y = x P2 on its own and gets its own INT4 step ("FlatQuant" page, Symbol Map and
 // Transformer integration: the per-head transforms of keys and values ahead of the
-// quantized KV cache). Rows are streamed in tiles of 16, whatever n1 is; 8 waves per CU,
-// each with a ring of 4 LDS slots (three tiles in flight while it computes one) and all of
-// P2's B operands in registers. P2's columns are permuted in the plan so that after the single MFMA stage a lane holds
-// NT consecutive columns of each of its 4 rows: one code word per row, and the row's
-// absmax is a 16-lane DPP reduction.
+// quantized KV cache). Rows are streamed in tiles of 16 MT, whatever n1 is; 8 waves per
+// CU, each with a ring of SLOTS LDS tiles and all of P2's B operands in registers. A wave
+// works on the MT 16-row groups of a tile at once: the groups' MFMA chains, row maxima,
+// steps and quantizers are independent, which hides their latencies with only two waves
+// per SIMD. P2's columns are permuted in the plan so that after the single MFMA stage a
+// lane holds NT consecutive columns of each of its 4 rows per group: one code word per
+// row, and the row's absmax is a 16-lane DPP reduction.
 template <int N2>
 struct RowsCfg {
   static_assert(N2 == 64 || N2 == 128, "rows kernel: n2 in {64, 128}");
   static constexpr int WAVES = 8;
-  static constexpr int SLOTS = 4;               // ring of tiles per wave (3 in flight)
+  static constexpr int MT = 1;                  // 16-row groups per tile
+  static constexpr int SLOTS = 4;               // ring of tiles per wave
   static constexpr int THREADS = WAVES * 64;
+  static constexpr int ROWS = 16 * MT;          // rows per tile
   static constexpr int NT = N2 / 16;            // column tiles = consecutive columns per lane
   static constexpr int KS = N2 / 32;            // reduction steps
   static constexpr int RB = N2 * 2;             // bytes per row
   static constexpr int PPR = RB / 16;           // 16-byte pieces per row
   static constexpr int RPB = 256 / RB;          // rows per 256-byte bank row
   static constexpr int RPI = 1024 / RB;         // rows per DMA instruction
-  static constexpr int TILE = 16 * RB;          // bytes per 16-row tile
+  static constexpr int TILE = ROWS * RB;        // bytes per tile
   static constexpr int LOADS = TILE / 1024;     // DMA instructions per tile
   static_assert(WAVES * SLOTS * TILE <= 160 * 1024, "LDS budget");
   __device__ static constexpr int swz(int R) { return (R / RPB) % PPR; }
   // vmcnt(k LOADS): at most k later tiles' loads still in flight
   template <int K>
   static constexpr int wait_imm = 0x0F70 | ((K * LOADS) & 15) | (((K * LOADS) >> 4) << 14);
+  static_assert((SLOTS - 1) * LOADS < 64, "vmcnt field");
+  // wait for the tile that has `later` of this wave's tiles after it (at most K in flight)
+  template <int K>
+  __device__ static void wait_tile(int later) {
+    if constexpr (K == 0) {
+      wait_and_fence<kWaitVm0>();
+    } else {
+      if (later >= K) wait_and_fence<wait_imm<K>>();
+      else wait_tile<K - 1>(later);
+    }
+  }
 };
 
 // 4 consecutive values -> 2 code bytes (value e in bits 4e..4e+3), clamped to [-8, 7]
+// (CLAMP = false only where the clamp is a no-op, as for quant8)
+template <bool CLAMP = true>
 __device__ __forceinline__ uint32_t quant4(const float (&y)[4], float inv) {
   constexpr float kMagic = 12582920.0f;   // 1.5 * 2^23 + 8 (see quant8)
   constexpr int kLo = 0x4B400000, kHi = 0x4B40000F;
@@ -957,10 +985,15 @@ __device__ __forceinline__ uint32_t quant4(const float (&y)[4], float inv) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float t = __fadd_rn(__fmul_rn(y[e], inv), kMagic);
-    u[e] = (uint32_t)min(max(__float_as_int(t), kLo), kHi) & 0xFu;
+    u[e] = (CLAMP ? (uint32_t)min(max(__float_as_int(t), kLo), kHi) : __float_as_uint(t)) & 0xFu;
   }
   return ((u[0] | (u[1] << 4) | (u[2] << 8) | (u[3] << 12)) ^ 0x8888u);
 }
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
 // Scale of row (lr & 3) of each lane's quad; the other rows' steps arrive by quad
 // broadcasts, so each lane computes one step instead of four.
@@ -973,9 +1006,10 @@ __device__ __forceinline__ float quad_bcast(float v) {
 template <int N2, bool YDBG>
 __global__ __launch_bounds__(512) void kq_rows_kernel(
     const __bf16 *__restrict__ X, int64_t T, int n1, int64_t ldx,
-    const bf16x8 *__restrict__ p2op, float clip, int scale_fp16,
+    const bf16x8 *__restrict__ p2op, float clip, int scale_fp16, int clip_allows_no_clamp,
     uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
   using C = RowsCfg<N2>;
+  constexpr int MT = C::MT;
   __shared__ __align__(16) unsigned char s_tile[C::WAVES][C::SLOTS][C::TILE];
 
   const int tid = threadIdx.x;
@@ -985,38 +1019,60 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
   // rows: R = T n1 < 2^31 (checked on the host), so row and tile indices are 32-bit
   const uint32_t uT = (uint32_t)T, un1 = (uint32_t)n1;
   const uint32_t R = uT * un1;
-  const uint32_t ntiles = (R + 15u) / 16u;
+  const uint32_t ntiles = (R + (C::ROWS - 1)) / (uint32_t)C::ROWS;
   const uint32_t stride = gridDim.x * C::WAVES;
   const uint32_t first = blockIdx.x * C::WAVES + wave;
   const int ntl = first < ntiles ? (int)((ntiles - 1u - first) / stride) + 1 : 0;  // my tiles
+  const bool contiguous = ldx == (int64_t)un1 * N2;  // rows one after another in memory
 
-  // DMA cursor: for instruction j, the (token, head) of this lane's row in the next tile
-  // to load. Instruction j fills tile rows RPI j .. RPI j + RPI - 1; lane i lands at row
-  // RPI j + i / PPR, position i % PPR (piece (i % PPR) ^ swz(row)). The cursor moves on
-  // by stride * 16 rows per tile without a division. Rows past the end (token >= T) read
-  // the last row; their results are not stored.
-  const uint32_t adv = stride * 16u;
+  // DMA cursor: first row of the next tile to load and its (token, head), wave-uniform;
+  // it moves on by stride * ROWS rows per tile without a division. Instruction j fills
+  // tile rows RPI j .. RPI j + RPI - 1; lane i lands at row RPI j + i / PPR, position
+  // i % PPR (piece (i % PPR) ^ swz(row)).
+  //  - a whole tile of contiguous rows is one block of memory: the lanes' offsets in it
+  //    are fixed (voff) and the base is uniform;
+  //  - otherwise a lane's head offset x = h0 + row < n1 + ROWS is split into
+  //    (x / n1, x % n1) in floating point: with rn1 = fp32(1 / n1), fp32(fp32(x + 1/2) rn1)
+  //    lies within 2^-23 relative of (x + 1/2) / n1, which is at least 1/(2 n1) away from
+  //    any integer, so truncation gives x / n1 exactly for x < 2^22 (n1 <= 2^20 is checked
+  //    on the host). Rows past the end (token >= T) read the last row; their results are
+  //    not stored.
+  const uint32_t adv = stride * (uint32_t)C::ROWS;
   const uint32_t adv_t = adv / un1, adv_h = adv - adv_t * un1;
-  uint32_t ct[C::LOADS], ch[C::LOADS];
+  const float rn1 = __fdiv_rn(1.0f, (float)un1);
+  uint32_t crow = first * (uint32_t)C::ROWS;
+  uint32_t ct = crow / un1, ch = crow - ct * un1;
+  uint32_t voff[C::LOADS];
 #pragma unroll
   for (int j = 0; j < C::LOADS; ++j) {
-    const uint32_t r = first * 16u + (uint32_t)(j * C::RPI + lane / C::PPR);
-    ct[j] = r / un1;
-    ch[j] = r - ct[j] * un1;
+    const int Rl = j * C::RPI + lane / C::PPR;
+    voff[j] = (uint32_t)(Rl * C::RB + (((lane % C::PPR) ^ C::swz(Rl)) * 16));
   }
   auto dma_next = [&](int b) {
+    if (contiguous && crow + (uint32_t)C::ROWS <= R) {
+      const __bf16 *base = X + (uint64_t)crow * N2;
 #pragma unroll
-    for (int j = 0; j < C::LOADS; ++j) {
-      const bool past = ct[j] >= uT;
-      const uint32_t t = past ? uT - 1u : ct[j], hd = past ? un1 - 1u : ch[j];
-      const int piece = (lane % C::PPR) ^ C::swz(j * C::RPI + lane / C::PPR);
-      dma16_addr<true>(X + (uint64_t)t * (uint64_t)ldx + (hd * N2 + piece * 8),
-                       lds_addr(s_tile[wave][b] + j * 1024));
-      ch[j] += adv_h;
-      const uint32_t wrap = ch[j] >= un1 ? 1u : 0u;  // branch-free carry into the token
-      ch[j] -= wrap * un1;
-      ct[j] += adv_t + wrap;
+      for (int j = 0; j < C::LOADS; ++j)
+        dma16<true>(base, voff[j], lds_addr(s_tile[wave][b] + j * 1024));
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::LOADS; ++j) {
+        const int Rl = j * C::RPI + lane / C::PPR;
+        const uint32_t x = ch + (uint32_t)Rl;
+        const uint32_t q = (uint32_t)__fmul_rn(__fadd_rn((float)x, 0.5f), rn1);
+        const uint32_t t0 = ct + q, h0 = x - q * un1;
+        const bool past = t0 >= uT;
+        const uint32_t t = past ? uT - 1u : t0, hd = past ? un1 - 1u : h0;
+        const int piece = (lane % C::PPR) ^ C::swz(Rl);
+        dma16_addr<true>(X + (uint64_t)t * (uint64_t)ldx + (hd * N2 + piece * 8),
+                         lds_addr(s_tile[wave][b] + j * 1024));
+      }
     }
+    crow += adv;
+    ch += adv_h;
+    const uint32_t wrap = ch >= un1 ? 1u : 0u;
+    ch -= wrap * un1;
+    ct += adv_t + wrap;
   };
 #pragma unroll
   for (int k = 0; k < C::SLOTS; ++k)
@@ -1031,24 +1087,33 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
   // compiler's own waits for these loads know nothing of the DMAs
   wait_and_fence<kWaitVm0>();
 
-  // the previous tile's results: this lane's code word of each of its 4 rows (row
-  // 16 tile + 4 g + r), and the step of row 16 tile + 4 g + (lr & 3)
-  uint32_t pend[4] = {0u, 0u, 0u, 0u};
-  TokenScale pend_s{};
-  uint32_t pend_row = 0;  // 16 tile + 4 g
+  // the previous tile's results: this lane's code word of each of its rows (row
+  // pend_trow + 16 mt + 4 g + r), and the step of row pend_trow + 16 mt + 4 g + (lr & 3)
+  uint32_t pend[MT][4];
+  TokenScale pend_s[MT];
+  uint32_t pend_trow = 0;  // first row of that tile (wave-uniform)
+  const int esz = scale_fp16 ? 2 : 4;
 
   auto store_pend = [&](bool tail) {
+    uint8_t *cbase = codes + (uint64_t)pend_trow * (N2 / 2);
+    unsigned char *sbase = static_cast<unsigned char *>(scales) + (uint64_t)pend_trow * esz;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t row = pend_row + (uint32_t)r;
-      if (!tail || row < R) {
-        uint8_t *dst = codes + (uint64_t)row * (N2 / 2) + lr * (C::NT / 2);
-        if constexpr (N2 == 128) __builtin_nontemporal_store(pend[r], reinterpret_cast<uint32_t *>(dst));
-        else __builtin_nontemporal_store((uint16_t)pend[r], reinterpret_cast<uint16_t *>(dst));
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t rl = (uint32_t)(16 * mt + 4 * g + r);
+        if (!tail || pend_trow + rl < R) {
+          uint8_t *dst = cbase + rl * (N2 / 2) + lr * (C::NT / 2);
+          if constexpr (N2 == 128) __builtin_nontemporal_store(pend[mt][r], reinterpret_cast<uint32_t *>(dst));
+          else __builtin_nontemporal_store((uint16_t)pend[mt][r], reinterpret_cast<uint16_t *>(dst));
+        }
+      }
+      const uint32_t srl = (uint32_t)(16 * mt + 4 * g + (lr & 3));
+      if (lr < 4 && (!tail || pend_trow + srl < R)) {
+        if (scale_fp16) *reinterpret_cast<_Float16 *>(sbase + srl * 2) = pend_s[mt].s16;
+        else *reinterpret_cast<float *>(sbase + srl * 4) = pend_s[mt].s32;
       }
     }
-    const uint32_t srow = pend_row + (uint32_t)(lr & 3);
-    if (lr < 4 && (!tail || srow < R)) store_scale(scales, srow, pend_s, scale_fp16);
   };
 
   for (int it = 0; it < ntl; ++it) {
@@ -1056,69 +1121,98 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
     // this tile has landed once at most the later tiles' loads (up to SLOTS - 1 tiles) are
     // in flight: loads complete in issue order, and stores are not counted on
     const int later = ntl - 1 - it;
-    if (later >= 3) wait_and_fence<C::template wait_imm<3>>();
-    else if (later == 2) wait_and_fence<C::template wait_imm<2>>();
-    else if (later == 1) wait_and_fence<C::template wait_imm<1>>();
-    else wait_and_fence<kWaitVm0>();
+    C::template wait_tile<C::SLOTS - 1>(later);
     const unsigned char *tile = s_tile[wave][b];
-    bf16x8 av[C::KS];  // A operands: row lr, piece 4 ks + g
+    bf16x8 av[MT][C::KS];  // A operands: row 16 mt + lr, piece 4 ks + g
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      av[ks] = *reinterpret_cast<const bf16x8 *>(tile + lr * C::RB + (((ks * 4 + g) ^ C::swz(lr)) * 16));
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        av[mt][ks] = *reinterpret_cast<const bf16x8 *>(
+            tile + (16 * mt + lr) * C::RB + (((ks * 4 + g) ^ C::swz(16 * mt + lr)) * 16));
     wait_and_fence<kWaitLgkm0>();  // slot b is free again
     // tiles stored inside the loop are never a wave's last tile, hence never ragged
     if (it > 0) store_pend(false);
     if (later >= C::SLOTS) dma_next(b);
 
-    f32x4 zacc[C::NT];
+    f32x4 zacc[MT][C::NT];
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) zacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) zacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt)
-        zacc[nt] = mfma(av[ks], p2r[ks][nt], zacc[nt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          zacc[mt][nt] = mfma(av[mt][ks], p2r[ks][nt], zacc[mt][nt]);
 
-    // lane holds Y[row 16 tl + 4 g + r][lr NT + nt]; absmax per row over the 16 lanes of g
-    const uint32_t tl = first + (uint32_t)it * stride;
-    const uint32_t row0 = tl * 16u + 4u * (uint32_t)g;
-    float m[4];
+    // lane holds Y[row trow + 16 mt + 4 g + r][lr NT + nt]
+    const uint32_t trow = (first + (uint32_t)it * stride) * (uint32_t)C::ROWS;
+    const bool b0 = (lr & 1) != 0, b1 = (lr & 2) != 0;
+    bool need_clamp = false;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = 0.f;
+    for (int mt = 0; mt < MT; ++mt) {
+      float m[4];
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) v = fmaxf(v, fabsf(zacc[nt][r]));
-      v = dpp_step<0xB1>(v);
-      v = dpp_step<0x4E>(v);
-      v = dpp_step<0x141>(v);
-      m[r] = dpp_step<0x140>(v);
-    }
-    const int rr = lr & 3;
-    const float mr = rr == 0 ? m[0] : rr == 1 ? m[1] : rr == 2 ? m[2] : m[3];
-    pend_s = token_scale(mr, clip, scale_fp16);
-    const float inv[4] = {quad_bcast<0>(pend_s.inv), quad_bcast<1>(pend_s.inv),
-                          quad_bcast<2>(pend_s.inv), quad_bcast<3>(pend_s.inv)};
+      for (int r = 0; r < 4; ++r) {
+        float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (N2 == 128) {
-        const float yv[8] = {zacc[0][r], zacc[1][r], zacc[2][r], zacc[3][r],
-                             zacc[4][r], zacc[5][r], zacc[6][r], zacc[7][r]};
-        pend[r] = quant8<true>(yv, inv[r]);
-      } else {
-        const float yv[4] = {zacc[0][r], zacc[1][r], zacc[2][r], zacc[3][r]};
-        pend[r] = quant4(yv, inv[r]);
+        for (int nt = 0; nt < C::NT; ++nt) v = fmaxf(v, fabsf(zacc[mt][nt][r]));
+        m[r] = v;
       }
-      if constexpr (YDBG) {
-        if (row0 + r < R) {
-          float *yp = ydbg + (uint64_t)(row0 + r) * N2 + lr * C::NT;
+      // transposing butterfly over the 16 lanes of g: after the two quad steps a lane
+      // holds the quad's max of row 4 g + (lr & 3) (rows b0 and 2 + b0 after the first),
+      // and two row rotations by 4 and 8 lanes combine the four quads
+      const float k0 = max_nn(b0 ? m[1] : m[0], dpp_read<0xB1>(b0 ? m[0] : m[1]));
+      const float k1 = max_nn(b0 ? m[3] : m[2], dpp_read<0xB1>(b0 ? m[2] : m[3]));
+      float k = max_nn(b1 ? k1 : k0, dpp_read<0x4E>(b1 ? k0 : k1));
+      k = dpp_step<0x124>(k);  // row_ror:4
+      k = dpp_step<0x128>(k);  // row_ror:8
+      pend_s[mt] = token_scale(k, clip, scale_fp16);
+      need_clamp |= clamp_needed(clip_allows_no_clamp, pend_s[mt].s32);
+    }
+    // the clamp is skipped only when no row of the wave can need it (one branch for all
+    // rows of the tile)
+    auto quantize = [&](auto clamp_tag) {
+      constexpr bool CL = decltype(clamp_tag)::value;
 #pragma unroll
-          for (int q = 0; q < C::NT / 4; ++q)
-            reinterpret_cast<float4 *>(yp)[q] =
-                make_float4(zacc[4 * q][r], zacc[4 * q + 1][r], zacc[4 * q + 2][r], zacc[4 * q + 3][r]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const float inv[4] = {quad_bcast<0>(pend_s[mt].inv), quad_bcast<1>(pend_s[mt].inv),
+                              quad_bcast<2>(pend_s[mt].inv), quad_bcast<3>(pend_s[mt].inv)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (N2 == 128) {
+            const float yv[8] = {zacc[mt][0][r], zacc[mt][1][r], zacc[mt][2][r], zacc[mt][3][r],
+                                 zacc[mt][4][r], zacc[mt][5][r], zacc[mt][6][r], zacc[mt][7][r]};
+            pend[mt][r] = quant8<CL>(yv, inv[r]);
+          } else {
+            const float yv[4] = {zacc[mt][0][r], zacc[mt][1][r], zacc[mt][2][r], zacc[mt][3][r]};
+            pend[mt][r] = quant4<CL>(yv, inv[r]);
+          }
         }
       }
+    };
+    if (__builtin_amdgcn_ballot_w64(need_clamp) != 0) quantize(BoolTag<true>{});
+    else quantize(BoolTag<false>{});
+    if constexpr (YDBG) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t row = trow + (uint32_t)(16 * mt + 4 * g + r);
+          if (row < R) {
+            float *yp = ydbg + (uint64_t)row * N2 + lr * C::NT;
+#pragma unroll
+            for (int q = 0; q < C::NT / 4; ++q)
+              reinterpret_cast<float4 *>(yp)[q] =
+                  make_float4(zacc[mt][4 * q][r], zacc[mt][4 * q + 1][r], zacc[mt][4 * q + 2][r],
+                              zacc[mt][4 * q + 3][r]);
+          }
+        }
     }
-    pend_row = row0;
+    pend_trow = trow;
   }
   if (ntl > 0) store_pend(true);
 }
@@ -1417,13 +1511,14 @@ template <int N2>
 hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
                        void *scales, float *y_debug, hipStream_t stream) {
   using C = RowsCfg<N2>;
-  const int64_t ntiles = (T * p->n1 + 15) / 16;
+  const int64_t ntiles = (T * p->n1 + C::ROWS - 1) / C::ROWS;
   const int64_t groups = (ntiles + C::WAVES - 1) / C::WAVES;
   const int grid = (int)(groups < (int64_t)p->grid_cap ? groups : (int64_t)p->grid_cap);
   auto k = y_debug ? &kq_rows_kernel<N2, true> : &kq_rows_kernel<N2, false>;
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream, static_cast<const __bf16 *>(X),
                      T, p->n1, ldx, static_cast<const bf16x8 *>(p->p2op), p->clip,
-                     p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
+                     p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes,
+                     scales, y_debug);
   return hipGetLastError();
 }
 

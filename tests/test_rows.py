@@ -56,6 +56,23 @@ def test_rows_parity(gpu, n1, n2, T, scale_dtype):
            scale_dtype=scale_dtype)
 
 
+@pytest.mark.parametrize("n1,n2,T", [(8, 128, 300), (3, 64, 41)])
+@pytest.mark.parametrize("alpha", [0.0, 2.0])
+def test_rows_parity_clamped(gpu, n1, n2, T, alpha):
+    """Clip ratios below 0.935 (sigmoid(0) = 0.5, sigmoid(2) = 0.88): the clamp to [-8, 7]
+    changes codes, so the kernel must take its clamping quantizer."""
+    wl = replace(S.WORKLOADS["kv_h8_d128"], n1=n1, n2=n2, n_outliers=3, alpha=alpha)
+    inp = S.make(wl, T=T)
+    plan = _plan(inp)
+    assert plan.clip < 0.935
+    X = K.torch_from(inp.X, "bf16").to("cuda:0")
+    codes, scales, y = K.run(plan, X, y_debug=True)
+    _check(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+    # some codes sit at the clamp bound -8 (nibble 8) or 7
+    nib = np.concatenate([codes.cpu().numpy() & 15, codes.cpu().numpy() >> 4]).ravel()
+    assert np.any(nib == 7) and np.any(nib == 8)
+
+
 def test_rows_strided_tokens(gpu):
     """Rows of a token sit at t * ldx + i * n2 (e.g. the key slice of a fused QKV output)."""
     import torch
