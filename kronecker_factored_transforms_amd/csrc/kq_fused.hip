@@ -1254,6 +1254,13 @@ struct ColsCfg {
   static constexpr int VPLANES = HAS_C ? 2 : 1;     // hi (+ lo) bf16 planes of x*c
   static_assert(!HAS_C || P2_LDS, "column kernel with c: n2 <= 128");
   static constexpr int VBUF = TPI * V_BYTES * VPLANES;
+  // Large n2 (P2 outside LDS): each wave keeps its 32-column block of P2 in registers and
+  // the next token's tile arrives by DMA in a second LDS buffer, when two tiles and P1 fit
+  static constexpr bool DMA = !P2_LDS && 2 * VBUF + P1_BYTES + 64 <= 160 * 1024;
+  static constexpr int VBUFS = DMA ? 2 : 1;
+  static constexpr int SLOTS = N1 * ROW_CHUNKS;      // 16-byte LDS slots of one tile
+  static constexpr int DMA_INSTR = (SLOTS + 63) / 64;
+  static_assert(!DMA || (TPI == 1 && SLOTS % 64 == 0), "tile DMA: whole instructions");
 };
 
 // byte offset of 16-byte chunk `cc` of row `r` of a token tile in LDS
@@ -1263,7 +1270,7 @@ __device__ __forceinline__ int vchunk_off(int r, int cc) {
   else return (r * (CH + 1) + cc) * 16;
 }
 
-template <int N1, int N2, bool HAS_C>
+template <int N1, int N2, bool HAS_C, bool YDBG = false>
 __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
@@ -1273,7 +1280,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
   constexpr int n = N1 * N2;
   __shared__ __align__(16) unsigned char s_p2[C::P2_BYTES];
   __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
-  __shared__ __align__(16) unsigned char s_v[C::VBUF];
+  __shared__ __align__(16) unsigned char s_v[C::VBUF * C::VBUFS];
   __shared__ float s_red[C::WAVES];
 
   const int tid = threadIdx.x;
@@ -1337,34 +1344,72 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
     }
   };
 
+  // Large n2: P2 does not fit in LDS next to the tile and P1, but one wave only ever uses
+  // its own 32-column block of P2 (n2 x 32 values, KS x 2 operands), which it keeps in
+  // registers for the whole kernel. The workgroup loads the next token's tile by DMA into
+  // the other LDS buffer: LDS slot q of the tile (row q / ROW_CHUNKS, chunk q % ROW_CHUNKS;
+  // the padding chunk re-reads chunk 0) is written by lane q % 64 of instruction q / 64.
+  // No other global load sits inside the token loop, so one wait before the end-of-token
+  // barrier covers the DMA.
+  auto dma_tile = [&](int64_t t, int b) {
+    const __bf16 *base = X + t * ldx;
+    for (int j = wave; j < C::DMA_INSTR; j += C::WAVES) {
+      const int q = j * 64 + lane;
+      const int r = q / C::ROW_CHUNKS, cc = q % C::ROW_CHUNKS;
+      const uint32_t voff = (uint32_t)((r * N2 + (cc < C::CH ? cc : 0) * 8) * 2);
+      dma16<true>(base, voff, __builtin_amdgcn_readfirstlane(lds_addr(s_v + b * C::VBUF + j * 1024)));
+    }
+  };
+  bf16x8 p2w[C::DMA ? C::KS : 1][2];
+  if constexpr (C::DMA) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      p2w[ks][0] = p2op[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
+      p2w[ks][1] = p2op[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
+    }
+  }
+
   int64_t grp = blockIdx.x;
-  if (grp < ngroups) issue_loads(grp);
-  lds_barrier();  // factors visible
+  if constexpr (C::DMA) {
+    if (grp < ngroups) dma_tile(grp, 0);
+    wait_and_fence<kWaitVm0>();  // the first tile and P2's registers have landed
+  } else {
+    if (grp < ngroups) issue_loads(grp);
+  }
+  lds_barrier();  // factors (and the first DMA tile) visible
 
   const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
   const bf16x8 *sp1 = reinterpret_cast<const bf16x8 *>(s_p1);
 
-  for (; grp < ngroups; grp += gridDim.x) {
-    store_lds();
-    lds_barrier();
-    {
-      const int64_t nxt = grp + gridDim.x;
+  for (int it = 0; grp < ngroups; grp += gridDim.x, ++it) {
+    const int64_t nxt = grp + gridDim.x;
+    const unsigned char *vt;
+    if constexpr (C::DMA) {
+      // the other buffer was last read in the previous iteration, before its final barrier
+      if (nxt < ngroups) dma_tile(nxt, (it + 1) & 1);
+      vt = s_v + (it & 1) * C::VBUF;
+    } else {
+      store_lds();
+      lds_barrier();
       if (nxt < ngroups) issue_loads(nxt);  // in flight while this group computes
+      vt = s_v + ts * C::V_BYTES;
     }
     const int64_t tok = grp * C::TPI + ts;
-    const unsigned char *vt = s_v + ts * C::V_BYTES;
 
     // ---- stage 1: Z[:, block] = V P2[:, block]  (M = n1 rows, K = n2, N = 32) ----
     f32x4 zacc[C::MT][2];
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) zacc[mt][0] = zacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // (large n2: a rolled loop, so that only one step's operands are in registers)
-#pragma unroll(C::P2_LDS ? C::KS : 1)
+    // (n2 = 256: a rolled loop, so that only one step's operands are in registers)
+#pragma unroll(C::P2_LDS || C::DMA ? C::KS : 1)
     for (int ks = 0; ks < C::KS; ++ks) {
       bf16x8 b0, b1;
       if constexpr (C::P2_LDS) {
         b0 = sp2[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
         b1 = sp2[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
+      } else if constexpr (C::DMA) {
+        b0 = p2w[ks][0];
+        b1 = p2w[ks][1];
       } else {  // from the plan's copy in global memory (L2-resident, shared by all CUs)
         b0 = p2op[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
         b1 = p2op[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
@@ -1422,14 +1467,16 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
 
     if (tok < T) {
       // lane holds Y[j = nt*16 + lr][wt*32 + 8g + 4h + r]: 8 consecutive codes -> 1 dword
+      // a uniform row base plus a 32-bit lane offset (nothing 64-bit per lane to keep)
       uint8_t *crow = codes + tok * (int64_t)(n / 2);
+      const uint32_t loff = (uint32_t)(lr * (N2 / 2) + wt * 16 + g * 4);
 #pragma unroll
       for (int nt = 0; nt < C::MT; ++nt) {
         const int j = nt * 16 + lr;
         const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
                              yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
-        *reinterpret_cast<uint32_t *>(crow + j * (N2 / 2) + wt * 16 + g * 4) = quant8(yv, sc.inv);
-        if (ydbg != nullptr) {
+        *reinterpret_cast<uint32_t *>(crow + (loff + (uint32_t)(nt * 16 * (N2 / 2)))) = quant8(yv, sc.inv);
+        if constexpr (YDBG) {
           float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wt * 32 + g * 8);
           yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
           yp[1] = make_float4(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]);
@@ -1437,6 +1484,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
       }
       if (wt == 0 && lane == 0) store_scale(scales, tok, sc, scale_fp16);
     }
+    if constexpr (C::DMA) wait_and_fence<kWaitVm0>();  // the next tile has landed
     lds_barrier();  // V tile and s_red are reused by the next iteration
   }
 }
@@ -1463,7 +1511,9 @@ hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
   using C = ColsCfg<N1, N2, HAS_C>;
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
-  hipLaunchKernelGGL((kq_cols_kernel<N1, N2, HAS_C>), dim3(grid), dim3(C::THREADS), 0, stream,
+  // the debug output has its own instantiation, so that the timed kernel keeps its registers
+  auto k = y_debug ? &kq_cols_kernel<N1, N2, HAS_C, true> : &kq_cols_kernel<N1, N2, HAS_C, false>;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
                      p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
