@@ -56,3 +56,25 @@ def test_split_parity(gpu, n1, n2, with_c, split):
     import torch
     assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
     K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+@pytest.mark.parametrize("n2", [160, 224, 256])
+def test_cols_large_n2_several_tokens_per_workgroup_strided(gpu, n2):
+    """More tokens than workgroups, so each workgroup loads its next tile while it computes
+    one (by DMA into a second LDS buffer for n2 <= 224), with a row stride larger than the
+    row; the same codes as the contiguous call, and the oracle's."""
+    import torch
+    wl = replace(S.WORKLOADS["hidden_n8192"], n1=128, n2=n2, n_outliers=4, pivot_channels=0)
+    T = 3 * 256 + 77
+    inp = S.make(wl, T=T)
+    plan, X = K.make_plan(inp)
+    assert plan.kernel == f"fused_mfma_bf16_cols_128x{n2}", plan.kernel
+    n = inp.wl.n
+    wide = torch.zeros((T, n + 64), dtype=torch.bfloat16, device=gpu)
+    wide[:, 32:32 + n] = X
+    Xs = wide[:, 32:32 + n]
+    assert Xs.stride(0) == n + 64
+    codes, scales, y = K.run(plan, Xs)
+    c2, s2 = K.run(plan, X, y_debug=False)
+    assert torch.equal(codes, c2) and torch.equal(scales, s2)
+    K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
