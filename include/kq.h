@@ -70,16 +70,18 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
  * T * n1 values (row i of token t at t * n1 + i) and codes keep the row-major Y order.
  * This is the per-head key/value transform ahead of a quantized KV cache ("FlatQuant"
  * page, Symbol Map: P_h, P_v; Transformer integration). bf16 only, n2 in {64, 128}, any
- * 1 <= n1 <= 2^20, no c, no other flag (KQ_ERR_INVALID_ARG / KQ_ERR_UNSUPPORTED otherwise);
+ * 1 <= n1 <= 2^20, no c, no other flag but KQ_FLAG_INT8 (KQ_ERR_INVALID_ARG /
+ * KQ_ERR_UNSUPPORTED otherwise);
  * a call must have T * n1 < 2^31 rows (else KQ_ERR_UNSUPPORTED). */
 #define KQ_FLAG_PER_ROW 0x400u
 
 /* KQ_FLAG_INT8: INT8 codes instead of INT4 ("FlatQuant" page, mixed-precision settings
  * such as W4A8): step s32 = fp32(fp32(clip * a) / 127), q = clamp(rint(fp32(y * inv)),
  * -128, 127), one two's-complement byte per value, so `codes` holds T x n bytes (row
- * stride n). bf16 plans of the stream kernel's shapes only: n2 in {64, 128} with n1 in
- * {16, 32, 48, 64}, without c, or n2 = 64 with c (KQ_ERR_UNSUPPORTED otherwise); not with
- * KQ_FLAG_PER_ROW or KQ_FLAG_FORCE_GENERIC. */
+ * stride n). bf16 plans of the stream kernel's shapes: n2 in {64, 128} with n1 in
+ * {16, 32, 48, 64}, without c, or n2 = 64 with c; and per-row plans (KQ_FLAG_PER_ROW, one
+ * step per row of n2 values) with n2 in {64, 128} (KQ_ERR_UNSUPPORTED otherwise); not with
+ * KQ_FLAG_FORCE_GENERIC. */
 #define KQ_FLAG_INT8 0x800u
 
 /*

@@ -100,8 +100,8 @@ kq_status kq_choose_factors(int64_t n, int *n1, int *n2) {
 
 // A plan of the rows kernel: identity left factor (P1 == NULL), one step per row of V.
 kq_status create_rows_plan(kq_plan **out, int n1, int n2, kq_dtype scale_dtype, const void *P2,
-                           float alpha, hipStream_t s) {
-  const kq_fused_variant *fv = kq_fused_lookup_rows(n2);
+                           float alpha, int bits, hipStream_t s) {
+  const kq_fused_variant *fv = kq_fused_lookup_rows(n2, bits);
   if (!fv || n1 > (1 << 20)) return KQ_ERR_UNSUPPORTED;  // rows kernel: n1 <= 2^20
   kq_plan *p = static_cast<kq_plan *>(calloc(1, sizeof(kq_plan)));
   if (!p) return KQ_ERR_OUT_OF_MEMORY;
@@ -115,7 +115,7 @@ kq_status create_rows_plan(kq_plan **out, int n1, int n2, kq_dtype scale_dtype, 
   p->kname = fv->name;
   p->launch = fv->launch;
   p->per_row = 1;
-  p->bits = 4;
+  p->bits = bits;
   kq_status st = KQ_OK;
   std::vector<uint16_t> h2((size_t)n2 * n2), a2((size_t)n2 * n2);
   int dev = 0, ncu = 0, per_cu = 0;
@@ -157,10 +157,11 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   if (scale_dtype != KQ_FP16 && scale_dtype != KQ_FP32) return KQ_ERR_INVALID_ARG;
   if (isnan(alpha)) return KQ_ERR_INVALID_ARG;
   if (flags & KQ_FLAG_PER_ROW) {
-    // identity left factor only; bf16; no per-channel scale, no other flag
-    if (P1 || !P2 || c || x_dtype != KQ_BF16 || (flags & ~KQ_FLAG_PER_ROW))
+    // identity left factor only; bf16; no per-channel scale; no other flag but INT8
+    if (P1 || !P2 || c || x_dtype != KQ_BF16 || (flags & ~(KQ_FLAG_PER_ROW | KQ_FLAG_INT8)))
       return KQ_ERR_INVALID_ARG;
-    return create_rows_plan(out, n1, n2, scale_dtype, P2, alpha, static_cast<hipStream_t>(stream));
+    return create_rows_plan(out, n1, n2, scale_dtype, P2, alpha, (flags & KQ_FLAG_INT8) ? 8 : 4,
+                            static_cast<hipStream_t>(stream));
   }
   if (!P1 || !P2) return KQ_ERR_INVALID_ARG;
   const int bits = (flags & KQ_FLAG_INT8) ? 8 : 4;

@@ -1003,7 +1003,7 @@ __device__ __forceinline__ float quad_bcast(float v) {
                                                  0xF, 0xF, false));
 }
 
-template <int N2, bool YDBG>
+template <int N2, bool YDBG, int BITS = 4>
 __global__ __launch_bounds__(512) void kq_rows_kernel(
     const __bf16 *__restrict__ X, int64_t T, int n1, int64_t ldx,
     const bf16x8 *__restrict__ p2op, float clip, int scale_fp16, int clip_allows_no_clamp,
@@ -1087,15 +1087,18 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
   // compiler's own waits for these loads know nothing of the DMAs
   wait_and_fence<kWaitVm0>();
 
-  // the previous tile's results: this lane's code word of each of its rows (row
-  // pend_trow + 16 mt + 4 g + r), and the step of row pend_trow + 16 mt + 4 g + (lr & 3)
-  uint32_t pend[MT][4];
+  // the previous tile's results: this lane's code words of each of its rows (row
+  // pend_trow + 16 mt + 4 g + r: one dword of NT nibbles, or NT / 4 dwords of bytes), and
+  // the step of row pend_trow + 16 mt + 4 g + (lr & 3)
+  constexpr int CW = BITS == 4 ? 1 : C::NT / 4;  // code dwords per lane and row
+  constexpr int ROWB = N2 * BITS / 8;            // code bytes per row
+  uint32_t pend[MT][4][CW];
   TokenScale pend_s[MT];
   uint32_t pend_trow = 0;  // first row of that tile (wave-uniform)
   const int esz = scale_fp16 ? 2 : 4;
 
   auto store_pend = [&](bool tail) {
-    uint8_t *cbase = codes + (uint64_t)pend_trow * (N2 / 2);
+    uint8_t *cbase = codes + (uint64_t)pend_trow * ROWB;
     unsigned char *sbase = static_cast<unsigned char *>(scales) + (uint64_t)pend_trow * esz;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -1103,9 +1106,16 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
       for (int r = 0; r < 4; ++r) {
         const uint32_t rl = (uint32_t)(16 * mt + 4 * g + r);
         if (!tail || pend_trow + rl < R) {
-          uint8_t *dst = cbase + rl * (N2 / 2) + lr * (C::NT / 2);
-          if constexpr (N2 == 128) __builtin_nontemporal_store(pend[mt][r], reinterpret_cast<uint32_t *>(dst));
-          else __builtin_nontemporal_store((uint16_t)pend[mt][r], reinterpret_cast<uint16_t *>(dst));
+          uint8_t *dst = cbase + rl * ROWB + lr * (C::NT * BITS / 8);
+          if constexpr (BITS == 8 && CW == 2) {
+            typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(u32x2_t{pend[mt][r][0], pend[mt][r][1]},
+                                        reinterpret_cast<u32x2_t *>(dst));
+          } else if constexpr (BITS == 8 || N2 == 128) {
+            __builtin_nontemporal_store(pend[mt][r][0], reinterpret_cast<uint32_t *>(dst));
+          } else {
+            __builtin_nontemporal_store((uint16_t)pend[mt][r][0], reinterpret_cast<uint16_t *>(dst));
+          }
         }
       }
       const uint32_t srl = (uint32_t)(16 * mt + 4 * g + (lr & 3));
@@ -1170,8 +1180,8 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
       float k = max_nn(b1 ? k1 : k0, dpp_read<0x4E>(b1 ? k0 : k1));
       k = dpp_step<0x124>(k);  // row_ror:4
       k = dpp_step<0x128>(k);  // row_ror:8
-      pend_s[mt] = token_scale(k, clip, scale_fp16);
-      need_clamp |= clamp_needed(clip_allows_no_clamp, pend_s[mt].s32);
+      pend_s[mt] = token_scale(k, clip, scale_fp16, BITS == 4 ? 7.0f : 127.0f);
+      need_clamp |= BITS == 8 || clamp_needed(clip_allows_no_clamp, pend_s[mt].s32);
     }
     // the clamp is skipped only when no row of the wave can need it (one branch for all
     // rows of the tile)
@@ -1183,13 +1193,18 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
                               quad_bcast<2>(pend_s[mt].inv), quad_bcast<3>(pend_s[mt].inv)};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if constexpr (N2 == 128) {
+          if constexpr (BITS == 8) {  // INT8 codes always clamp (quant4x8)
+#pragma unroll
+            for (int q = 0; q < CW; ++q)
+              pend[mt][r][q] = quant4x8(zacc[mt][4 * q][r], zacc[mt][4 * q + 1][r],
+                                        zacc[mt][4 * q + 2][r], zacc[mt][4 * q + 3][r], inv[r]);
+          } else if constexpr (N2 == 128) {
             const float yv[8] = {zacc[mt][0][r], zacc[mt][1][r], zacc[mt][2][r], zacc[mt][3][r],
                                  zacc[mt][4][r], zacc[mt][5][r], zacc[mt][6][r], zacc[mt][7][r]};
-            pend[mt][r] = quant8<CL>(yv, inv[r]);
+            pend[mt][r][0] = quant8<CL>(yv, inv[r]);
           } else {
             const float yv[4] = {zacc[mt][0][r], zacc[mt][1][r], zacc[mt][2][r], zacc[mt][3][r]};
-            pend[mt][r] = quant4<CL>(yv, inv[r]);
+            pend[mt][r][0] = quant4<CL>(yv, inv[r]);
           }
         }
       }
@@ -1557,14 +1572,14 @@ hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
                    &launch_pair<A, B>,                                                 \
                    reinterpret_cast<const void *>(&kq_pair_kernel<A, B, false>),       \
                    "fused_mfma_bf16_pair_" #A "x" #B}
-template <int N2>
+template <int N2, int BITS = 4>
 hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
                        void *scales, float *y_debug, hipStream_t stream) {
   using C = RowsCfg<N2>;
   const int64_t ntiles = (T * p->n1 + C::ROWS - 1) / C::ROWS;
   const int64_t groups = (ntiles + C::WAVES - 1) / C::WAVES;
   const int grid = (int)(groups < (int64_t)p->grid_cap ? groups : (int64_t)p->grid_cap);
-  auto k = y_debug ? &kq_rows_kernel<N2, true> : &kq_rows_kernel<N2, false>;
+  auto k = y_debug ? &kq_rows_kernel<N2, true, BITS> : &kq_rows_kernel<N2, false, BITS>;
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream, static_cast<const __bf16 *>(X),
                      T, p->n1, ldx, static_cast<const bf16x8 *>(p->p2op), p->clip,
                      p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes,
@@ -1660,18 +1675,17 @@ const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split, i
 
 namespace {
 const kq_fused_variant kRowsVariants[] = {
-    kq_fused_variant{0, 64, false, KQ_SPLIT_ROWS, 4, 0, RowsCfg<64>::THREADS, &launch_rows<64>,
-                     reinterpret_cast<const void *>(&kq_rows_kernel<64, false>),
-                     "fused_mfma_bf16_rows_64"},
-    kq_fused_variant{0, 128, false, KQ_SPLIT_ROWS, 4, 0, RowsCfg<128>::THREADS, &launch_rows<128>,
-                     reinterpret_cast<const void *>(&kq_rows_kernel<128, false>),
-                     "fused_mfma_bf16_rows_128"},
+#define KQ_ROWS(B, BITS, SUF)                                                          \
+  kq_fused_variant{0, B, false, KQ_SPLIT_ROWS, BITS, 0, RowsCfg<B>::THREADS, &launch_rows<B, BITS>, \
+                   reinterpret_cast<const void *>(&kq_rows_kernel<B, false, BITS>),       \
+                   "fused_mfma_bf16_rows_" #B SUF}
+    KQ_ROWS(64, 4, ""), KQ_ROWS(128, 4, ""), KQ_ROWS(64, 8, "_int8"), KQ_ROWS(128, 8, "_int8"),
 };
 }  // namespace
 
-const kq_fused_variant *kq_fused_lookup_rows(int n2) {
+const kq_fused_variant *kq_fused_lookup_rows(int n2, int bits) {
   for (const kq_fused_variant &e : kRowsVariants)
-    if (e.n2 == n2) return &e;
+    if (e.n2 == n2 && e.bits == bits) return &e;
   return nullptr;
 }
 

@@ -74,7 +74,7 @@ struct kq_fused_variant {
 // or nullptr.
 const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split, int bits = 4);
 // The rows kernel (identity left factor, one step per row of V) for n2, or nullptr.
-const kq_fused_variant *kq_fused_lookup_rows(int n2);
+const kq_fused_variant *kq_fused_lookup_rows(int n2, int bits);
 void kq_fused_arrange_p2_rows(const uint16_t *P2, int n2, uint16_t *out);
 // Element counts of the operand-ordered bf16 copies of P1 / P2.
 size_t kq_fused_p1op_elems(int n1);

@@ -118,10 +118,14 @@ def test_per_row_flag_is_validated_on_the_host(L):
 def test_int8_flag_is_validated_on_the_host(L):
     for kw in (dict(flags=B.KQ_FLAG_INT8, xd=B.KQ_FP32),
                dict(flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_FORCE_GENERIC),
-               dict(flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_PER_ROW, p1=None)):
+               dict(flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_PER_ROW, p1=None, xd=B.KQ_FP32),
+               dict(flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_PER_ROW | B.KQ_FLAG_FORCE_GENERIC, p1=None)):
         st, h = _create_raw(L, 64, 128, **kw)
         assert st == B.KQ_ERR_INVALID_ARG and h is None, kw
     st, h = _create_raw(L, 64, 128, flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_SPLIT_COLS)
+    assert st == B.KQ_ERR_UNSUPPORTED and h is None
+    # per-row INT8 exists for n2 in {64, 128} only
+    st, h = _create_raw(L, 8, 32, p1=None, flags=B.KQ_FLAG_INT8 | B.KQ_FLAG_PER_ROW)
     assert st == B.KQ_ERR_UNSUPPORTED and h is None
 
 

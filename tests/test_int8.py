@@ -72,3 +72,32 @@ def test_int8_unsupported_shapes(gpu):
     with pytest.raises(B.KqError) as e:
         B.kq_create(112, 128, "bf16", "fp16", P1, P2, c, 1.0, None, B.KQ_FLAG_INT8)
     assert e.value.status == B.KQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n1,n2,T", [(8, 128, 777), (3, 64, 41), (1, 128, 5), (32, 128, 129)])
+@pytest.mark.parametrize("alpha", [3.0, 0.0])
+def test_int8_per_row_parity(gpu, n1, n2, T, alpha):
+    """Per-row plans with INT8 codes (a per-head transform ahead of an 8-bit KV cache):
+    one byte per value in row-major Y order, one step per row, bit-exact against the
+    oracle quantizer applied to each row of the GPU's own Y."""
+    import torch
+    wl = replace(S.WORKLOADS["kv_h8_d128"], n1=n1, n2=n2, n_outliers=3, alpha=alpha)
+    inp = S.make(wl, T=T)
+    _, _, P2, _ = K.device_inputs(inp)
+    plan = B.Plan(None, P2, None, inp.alpha, inp.wl.scale_dtype, n1=n1, bits=8)
+    assert plan.kernel == f"fused_mfma_bf16_rows_{n2}_int8"
+    X = K.torch_from(inp.X, "bf16").to("cuda:0")
+    codes, scales, y = K.run(plan, X, y_debug=True)
+    codes2, scales2 = K.run(plan, X, y_debug=False)
+    assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
+    assert tuple(codes.shape) == (T, n1 * n2) and tuple(scales.shape) == (T, n1)
+    eye = S.to_bf16_bits(np.eye(n1))
+    Y = O.transform(inp.X, eye, inp.P2, None, "bf16")
+    assert K.rel_l2(y.cpu().numpy(), Y) <= 1e-5
+    rows = np.ascontiguousarray(y.cpu().numpy(), dtype=np.float32).reshape(T * n1, n2)
+    q, s = O.quantize_per_token(rows, np.float32(plan.clip), inp.wl.scale_dtype, bits=8)
+    assert np.array_equal(codes.cpu().numpy(), O.pack_int8(q).reshape(T, -1)), "codes differ"
+    assert np.array_equal(K.np_scales(scales).reshape(-1).view(np.uint8), s.view(np.uint8))
+    if alpha == 0.0:  # clip 0.5: the clamp to [-128, 127] is reached
+        qq = codes.cpu().numpy().view(np.int8)
+        assert qq.max() == 127 and qq.min() == -128
