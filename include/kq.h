@@ -129,7 +129,8 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
 
 /*
  * kq_transform_quant -- the hot path: transform + quantize T tokens, enqueued on
- * `stream`, asynchronous. No allocation, no synchronization, no host<->device copy.
+ * `stream`, asynchronous. No allocation, no synchronization, no host<->device copy, so a
+ * call may be captured into a HIP graph and replayed (the buffers stay bound).
  *   plan     from kq_create.
  *   X        device, T rows of n elements of the plan's x_dtype; row t starts at
  *            X + t*ldx elements. 16-byte aligned; ldx >= n and ldx*sizeof(elem) a
