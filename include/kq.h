@@ -26,7 +26,8 @@
  *   - Every entry point returns a kq_status; nothing is thrown or printed across the
  *     ABI. Argument errors are detected before anything is enqueued.
  *   - A plan is immutable after kq_create: calls on one plan from several host threads
- *     or streams are safe.
+ *     or streams are safe. It belongs to the device that was current at kq_create, and
+ *     kq_transform_quant returns KQ_ERR_INVALID_ARG when another device is current.
  */
 #ifndef KQ_H
 #define KQ_H

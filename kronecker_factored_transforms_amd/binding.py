@@ -79,11 +79,14 @@ def lib() -> ctypes.CDLL:
 
 # ------------------------------------------------------------------------------------
 def _ptr(x) -> int | None:
-    """Device pointer of a tensor, an int address, or None."""
+    """Device pointer of a GPU tensor, an int address, or None. A host tensor is refused:
+    its address would reach the kernels as a device address."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise ValueError("libkq takes device tensors; got one on " + str(getattr(x, "device", "?")))
     return int(x.data_ptr())
 
 

@@ -140,6 +140,7 @@ kq_status create_rows_plan(kq_plan **out, int n1, int n2, kq_dtype scale_dtype, 
   *out = p;
   return KQ_OK;
 fail:
+  (void)hipStreamSynchronize(s);  // no copy still in flight into a buffer freed below
   free_plan_buffers(p);
   free(p);
   return st;
@@ -318,6 +319,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   return KQ_OK;
 
 fail:
+  (void)hipStreamSynchronize(s);  // no copy still in flight into a buffer freed below
   free_plan_buffers(p);
   free(p);
   return st;
@@ -341,6 +343,8 @@ kq_status kq_transform_quant(const kq_plan *p, const void *X, int64_t T, int64_t
   if (y_debug && !is_aligned(y_debug, 16)) return KQ_ERR_ALIGNMENT;
   if (T > ((int64_t)1 << 40) / p->n) return KQ_ERR_INVALID_ARG;
   if (p->per_row && T * p->n1 >= ((int64_t)1 << 31)) return KQ_ERR_UNSUPPORTED;
+  int dev = -1;  // the plan's buffers live on the device that was current at create time
+  if (hipGetDevice(&dev) != hipSuccess || dev != p->device) return KQ_ERR_INVALID_ARG;
   hipError_t e;
   if (p->small_launch && T < p->small_max_T) {
     kq_plan v = *p;  // the same plan seen through the small-batch variant's operands

@@ -159,3 +159,10 @@ def test_int4_gemm_rejects_bad_arguments_before_touching_the_gpu(L):
         assert _gemm_raw(L, **kw) == B.KQ_ERR_UNSUPPORTED, kw
     for kw in (dict(xq=0x1008), dict(ldxq=136), dict(out=0x5004), dict(ldo=10), dict(sd=B.KQ_FP32, sw=0x4004)):
         assert _gemm_raw(L, **kw) == B.KQ_ERR_ALIGNMENT, kw
+
+
+def test_host_tensors_are_refused_before_any_call():
+    import torch
+    with pytest.raises(ValueError):
+        B._ptr(torch.zeros(4))
+    assert B._ptr(None) is None and B._ptr(0x1000) == 0x1000
