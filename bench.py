@@ -112,7 +112,8 @@ def cpu_baseline(inp, seconds: float, bits: int = 4):
         "kind": "oracle",
         "sample": (f"first {k} of {T} tokens of the same workload, {passes} pass(es); float64 "
                    f"factored transform (numpy.matmul) + fp32 quantizer + packing, {wall:.1f} s "
-                   f"wall, {cpu:.1f} s CPU; BLAS {blas}; host cpu_count {os.cpu_count()}"),
+                   f"wall, {cpu:.1f} s CPU; BLAS {blas}; host cpu_count {os.cpu_count()}, "
+                   f"affinity {len(os.sched_getaffinity(0))}"),
     }
 
 
