@@ -305,6 +305,7 @@ def main():
         torch.cuda.synchronize()
         kernel_ms = sorted(a.elapsed_time(b) for a, b in ev)
         per_launch = {"mean_us": sum(kernel_ms) / K * 1e3, "median_us": kernel_ms[K // 2] * 1e3,
+                      "p10_us": kernel_ms[K // 10] * 1e3, "p90_us": kernel_ms[(9 * K) // 10] * 1e3,
                       "min_us": kernel_ms[0] * 1e3, "max_us": kernel_ms[-1] * 1e3}
 
     flop_tok = 2 * n * (wl.n1 + wl.n2)
@@ -359,6 +360,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if per_launch:  # diagnostic: an event pair around every launch (adds a few us each)
+        out["per_launch_events_us"] = per_launch
     print(json.dumps(out), flush=True)
     plan.close()
 
