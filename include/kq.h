@@ -117,7 +117,9 @@ kq_status kq_create(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype sc
 
 /* Shapes with a kernel (anything else: KQ_ERR_UNSUPPORTED from kq_create):
  *   bf16, bf16 MFMA kernels, with or without c: n2 = 32 with n1 in {16, 32}; n2 = 64
- *     with n1 in {16, 32, 48, 64}; n2 = 128 with n1 in {16, 32, ..., 128}. Without c
+ *     with n1 in {16, 32, 48, 64}; n2 = 128 with n1 in {16, 32, ..., 128}, and with
+ *     n1 in {86, 108} (hidden sizes 11008 and 13824; P1 is zero-padded to whole 16-row
+ *     tiles inside the plan, results are unchanged). Without c
  *     also n1 = 128 with n2 in {160, 192, 224, 256} (hidden sizes 20480 ... 32768, e.g.
  *     28672 = 128 x 224).
  *   fp32 (and bf16 shapes not listed above): the generic fp32 kernel, n <= 16384.

@@ -1241,16 +1241,21 @@ constexpr int cols_waves(int n2) { return n2 / 32 > kWaves ? n2 / 32 : kWaves; }
 
 template <int N1, int N2, bool HAS_C>
 struct ColsCfg {
-  static_assert(N1 % 16 == 0 && N1 >= 16 && N1 <= 128, "n1 must be a multiple of 16 up to 128");
+  static_assert(N1 >= 16 && N1 <= 128, "n1 in [16, 128]");
   static_assert(N2 % 32 == 0 && N2 >= 32 && N2 <= 256, "n2 must be a multiple of 32 up to 256");
   static constexpr int W = N2 / 32;                 // waves per token
   static constexpr int WAVES = cols_waves(N2);      // waves per workgroup
   static constexpr int THREADS = WAVES * 64;
   static constexpr int TPI = WAVES / W;             // tokens per workgroup iteration
-  static constexpr int MT = N1 / 16;                // 16-row tiles of V / Z
+  // n1 that is not a multiple of 16 is padded to whole row tiles: the padded rows of V
+  // stay zero in LDS, P1's operands are zero beyond n1, so the padded rows of Y are zero
+  // (no effect on the absmax) and are not stored
+  static constexpr bool PADDED = (N1 % 16) != 0;
+  static constexpr int MT = (N1 + 15) / 16;         // 16-row tiles of V / Z
+  static constexpr int N1P = MT * 16;
   static constexpr int KS = N2 / 32;                // stage-1 reduction steps
-  static constexpr int KK = (N1 + 31) / 32;         // stage-2 reduction steps of 32
-  static constexpr bool KHALF = (N1 % 32) != 0;     // last step holds 16 rows + 16 zeros
+  static constexpr int KK = (N1P + 31) / 32;        // stage-2 reduction steps of 32
+  static constexpr bool KHALF = (N1P % 32) != 0;    // last step holds 16 rows + 16 zeros
   static constexpr int CH = N2 / 8;                 // 16-byte chunks per V row
   // row layout in LDS: an XOR swizzle of the chunks when CH is a power of two, else rows
   // padded by one chunk; either way the 16 rows of one A-operand read hit 16 different
@@ -1258,9 +1263,9 @@ struct ColsCfg {
   static constexpr bool POW2 = (CH & (CH - 1)) == 0;
   static constexpr int ROW_CHUNKS = POW2 ? CH : CH + 1;
   static constexpr int TOK_CHUNKS = N1 * CH;
-  static constexpr int CPT = TPI * TOK_CHUNKS / THREADS;  // chunks per thread per iter
-  static_assert(CPT * THREADS == TPI * TOK_CHUNKS, "token tile must split evenly");
-  static constexpr int V_BYTES = N1 * ROW_CHUNKS * 16;
+  static constexpr int CPT = (TPI * TOK_CHUNKS + THREADS - 1) / THREADS;  // chunks per thread
+  static constexpr bool EVEN = CPT * THREADS == TPI * TOK_CHUNKS;        // no idle slots
+  static constexpr int V_BYTES = N1P * ROW_CHUNKS * 16;
   // P2 operands: shared in LDS while they fit, else read from the plan's copy in global
   // memory, which stays in the L2 caches
   static constexpr bool P2_LDS = N2 <= 128;
@@ -1276,6 +1281,7 @@ struct ColsCfg {
   static constexpr int SLOTS = N1 * ROW_CHUNKS;      // 16-byte LDS slots of one tile
   static constexpr int DMA_INSTR = (SLOTS + 63) / 64;
   static_assert(!DMA || (TPI == 1 && SLOTS % 64 == 0), "tile DMA: whole instructions");
+  static_assert(!PADDED || P2_LDS, "padded n1: n2 <= 128");
 };
 
 // byte offset of 16-byte chunk `cc` of row `r` of a token tile in LDS
@@ -1309,12 +1315,21 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
 
   if constexpr (C::P2_LDS) copy_to_lds(s_p2, p2op, C::P2_BYTES, tid, C::THREADS);
   copy_to_lds(s_p1, p1op, C::P1_BYTES, tid, C::THREADS);
+  if constexpr (C::PADDED) {  // rows n1 .. n1P of every tile plane stay zero
+    constexpr int PAD_UNITS = (C::N1P - N1) * C::ROW_CHUNKS;  // 16-byte units per plane
+    for (int q = tid; q < C::TPI * C::VPLANES * PAD_UNITS; q += C::THREADS)
+      *reinterpret_cast<uint4 *>(s_v + (q / PAD_UNITS) * C::V_BYTES + N1 * C::ROW_CHUNKS * 16 +
+                                 (q % PAD_UNITS) * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
 
   // per-thread chunk coordinates (fixed for the whole kernel)
   int c_ts[C::CPT], c_row[C::CPT], c_cc[C::CPT];
+  bool c_ok[C::CPT];  // chunk q exists (threads can outnumber a padded tile's chunks)
 #pragma unroll
   for (int i = 0; i < C::CPT; ++i) {
-    const int q = tid + C::THREADS * i;
+    const int q0 = tid + C::THREADS * i;
+    c_ok[i] = C::EVEN || q0 < C::TPI * C::TOK_CHUNKS;
+    const int q = c_ok[i] ? q0 : 0;
     c_ts[i] = q / C::TOK_CHUNKS;
     const int qq = q % C::TOK_CHUNKS;
     c_row[i] = qq / C::CH;
@@ -1337,7 +1352,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int64_t t = grp * C::TPI + c_ts[i];
-      if (t < T) {
+      if (c_ok[i] && t < T) {
         pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + c_row[i] * N2 + c_cc[i] * 8);
       } else {
         pre[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -1347,6 +1362,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
   auto store_lds = [&]() {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
+      if (!c_ok[i]) continue;
       const int off = c_ts[i] * C::V_BYTES + vchunk_off<C::CH>(c_row[i], c_cc[i]);
       if constexpr (HAS_C) {
         uint4 hi, lo;
@@ -1488,6 +1504,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
 #pragma unroll
       for (int nt = 0; nt < C::MT; ++nt) {
         const int j = nt * 16 + lr;
+        if (C::PADDED && j >= N1) continue;  // padded rows of Y are not stored
         const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
                              yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
         *reinterpret_cast<uint32_t *>(crow + (loff + (uint32_t)(nt * 16 * (N2 / 2)))) = quant8(yv, sc.inv);
@@ -1641,6 +1658,8 @@ const kq_fused_variant kVariants[] = {
     KQ_COLS(80, 128, false, ""),   KQ_COLS(80, 128, true, "_c"),
     KQ_COLS(96, 128, false, ""),   KQ_COLS(96, 128, true, "_c"),
     KQ_COLS(112, 128, false, ""),  KQ_COLS(112, 128, true, "_c"),
+    KQ_COLS(86, 128, false, ""),   KQ_COLS(86, 128, true, "_c"),   // 11008 (padded to 96)
+    KQ_COLS(108, 128, false, ""),  KQ_COLS(108, 128, true, "_c"),  // 13824 (padded to 112)
     KQ_COLS(128, 128, false, ""),  KQ_COLS(128, 128, true, "_c"),
     // hidden sizes whose larger factor exceeds 128 (e.g. 28672 -> 128 x 224)
     KQ_COLS(128, 160, false, ""),  KQ_COLS(128, 192, false, ""),
@@ -1702,7 +1721,10 @@ void kq_fused_arrange_p2_rows(const uint16_t *P2, int n2, uint16_t *out) {
           out[o++] = P2[(size_t)(32 * ks + 8 * (L / 16) + v) * n2 + (L % 16) * NT + a];
 }
 
-size_t kq_fused_p1op_elems(int n1) { return (size_t)((n1 + 31) / 32) * (n1 / 16) * 512; }
+size_t kq_fused_p1op_elems(int n1) {
+  const int mt = (n1 + 15) / 16;  // n1 padded to whole 16-row tiles
+  return (size_t)((mt * 16 + 31) / 32) * mt * 512;
+}
 size_t kq_fused_p2op_elems(int n2) { return (size_t)n2 * (size_t)n2; }
 
 // P2 as stage-1 B operands, in blocks of `cb` output columns (one block per wave that
@@ -1725,17 +1747,18 @@ void kq_fused_arrange_p2(const uint16_t *P2, int n2, int cb, uint16_t *out) {
 }
 
 // P1 as stage-2 B operands: [kk][tile t][lane L][slot v] =
-//   P1[32 kk + 16 (v/4) + 4 g + (v%4)][16 t + L%16]   (zero where that row is >= n1)
-// i.e. the slot order of the stage-1 accumulators of row tiles 2kk and 2kk+1.
+//   P1[32 kk + 16 (v/4) + 4 g + (v%4)][16 t + L%16]   (zero where that row or column is
+// >= n1: n1 is padded to whole 16-row tiles), i.e. the slot order of the stage-1
+// accumulators of row tiles 2kk and 2kk+1.
 void kq_fused_arrange_p1(const uint16_t *P1, int n1, uint16_t *out) {
-  const int MT = n1 / 16, KK = (n1 + 31) / 32;
+  const int MT = (n1 + 15) / 16, KK = (MT * 16 + 31) / 32;
   size_t o = 0;
   for (int kk = 0; kk < KK; ++kk)
     for (int t = 0; t < MT; ++t)
       for (int L = 0; L < 64; ++L)
         for (int v = 0; v < 8; ++v) {
           const int g = L / 16;
-          const int i = 32 * kk + 16 * (v / 4) + 4 * g + (v % 4);
-          out[o++] = i < n1 ? P1[(size_t)i * n1 + 16 * t + L % 16] : (uint16_t)0;
+          const int i = 32 * kk + 16 * (v / 4) + 4 * g + (v % 4), j = 16 * t + L % 16;
+          out[o++] = i < n1 && j < n1 ? P1[(size_t)i * n1 + j] : (uint16_t)0;
         }
 }

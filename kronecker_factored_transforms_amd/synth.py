@@ -95,6 +95,12 @@ WORKLOADS = {
     "kv_h8_d128": Workload(
         "kv_h8_d128", 7, T=65536, n1=8, n2=128, dtype="bf16", x_kind="normal",
         n_outliers=4, outlier_scale=20.0, p_kind="orthogonal", alpha=3.0, per_row=True),
+    # MLP down-projection input of a 7B-class model: 11008 = 86 x 128 (n1 not a multiple
+    # of 16), SiLU-gated activations, per-channel c
+    "ffn_n11008": Workload(
+        "ffn_n11008", 8, T=8192, n1=86, n2=128, dtype="bf16", x_kind="silu_gate",
+        p_kind="near_identity", p_eps=0.05, c_kind="loguniform", c_lo=0.25, c_hi=4.0,
+        alpha=None),
     # a larger factor than 128: the 70B-class FFN down-projection input, 28672 = 128 x 224
     "down_proj_n28672": Workload(
         "down_proj_n28672", 6, T=4096, n1=128, n2=224, dtype="bf16", x_kind="silu_gate",

@@ -33,6 +33,7 @@ SMALL = [
     ("decode_n8192_t64", 64),
     ("prefill_n8192_t65536", 777),
     ("down_proj_n28672", 203),
+    ("ffn_n11008", 301),
 ]
 
 
@@ -50,7 +51,7 @@ def test_parity_against_full_oracle(gpu, name, T):
 
 
 FULL = ["attn_n4096", "hidden_n8192", "down_proj_n14336", "decode_n8192_t64",
-        "prefill_n8192_t65536", "down_proj_n28672"]
+        "prefill_n8192_t65536", "down_proj_n28672", "ffn_n11008"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -17,6 +17,7 @@ def test_workload_shapes():
     assert shapes["prefill_n8192_t65536"] == (65536, 64, 128, "bf16")
     assert shapes["down_proj_n28672"] == (4096, 128, 224, "bf16")
     assert shapes["kv_h8_d128"] == (65536, 8, 128, "bf16")
+    assert shapes["ffn_n11008"] == (8192, 86, 128, "bf16")
 
 
 def test_same_seed_same_bytes_and_token_subsets_agree():

@@ -19,7 +19,8 @@ DEEP_SHAPES = {(64, 128, False), (64, 64, False), (64, 64, True)}
 SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (32, 128, False),
           (48, 128, True), (16, 64, True), (48, 64, False), (32, 32, True), (16, 32, False),
           (112, 128, False), (112, 128, True), (96, 128, False), (128, 128, True), (80, 128, False),
-          (128, 160, False), (128, 224, False), (128, 256, False), (128, 224, True)]
+          (128, 160, False), (128, 224, False), (128, 256, False), (128, 224, True),
+          (86, 128, False), (86, 128, True), (108, 128, False), (108, 128, True)]
 
 
 def _available(n1, n2, split, with_c=False):
@@ -74,6 +75,27 @@ def test_cols_large_n2_several_tokens_per_workgroup_strided(gpu, n2):
     wide[:, 32:32 + n] = X
     Xs = wide[:, 32:32 + n]
     assert Xs.stride(0) == n + 64
+    codes, scales, y = K.run(plan, Xs)
+    c2, s2 = K.run(plan, X, y_debug=False)
+    assert torch.equal(codes, c2) and torch.equal(scales, s2)
+    K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+@pytest.mark.parametrize("n1", [86, 108])
+@pytest.mark.parametrize("T", [1, 3, 845])
+def test_cols_padded_n1_with_c_strided(gpu, n1, T):
+    """n1 not a multiple of 16: zero-padded row tiles, whose rows must neither reach the
+    absmax nor be stored, at a single token, a few tokens and several tokens per
+    workgroup, with a row stride larger than the row."""
+    import torch
+    wl = replace(S.WORKLOADS["ffn_n11008"], n1=n1)
+    inp = S.make(wl, T=T)
+    plan, X = K.make_plan(inp)
+    assert plan.kernel == f"fused_mfma_bf16_cols_{n1}x128_c", plan.kernel
+    n = inp.wl.n
+    wide = torch.zeros((T, n + 64), dtype=torch.bfloat16, device=gpu)
+    wide[:, 32:32 + n] = X
+    Xs = wide[:, 32:32 + n]
     codes, scales, y = K.run(plan, Xs)
     c2, s2 = K.run(plan, X, y_debug=False)
     assert torch.equal(codes, c2) and torch.equal(scales, s2)
