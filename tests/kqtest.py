@@ -5,6 +5,7 @@ import math
 import numpy as np
 
 from kronecker_factored_transforms_amd import binding as B
+from kronecker_factored_transforms_amd import synth as S
 from oracle import kq_oracle as O
 
 TOL = {"bf16": 2e-3, "fp32": 1e-5}   # rel-L2 of the transformed tensor vs the fp64 oracle
@@ -88,4 +89,31 @@ def check_against_oracle(inp, codes, scales, y, clip, token_ids=None, scale_dtyp
     assert rel <= TOL[inp.wl.dtype], f"rel-L2 {rel:.3e} > {TOL[inp.wl.dtype]:.0e}"
     assert_quant_bit_exact(codes, scales, y, clip, sd)
     assert clip == float(O.clip_ratio(inp.alpha)) or (math.isinf(inp.alpha) and clip in (0.0, 1.0))
+    return rel
+
+
+def check_plan_against_oracle(inp, plan, codes, scales, y):
+    """Any plan's outputs for inp.X: a Kronecker plan (within the dtype's tolerance of the
+    fp64 oracle) or a per-row plan (identity left factor, one step per row of n2 values,
+    within 1e-5), with INT4 or INT8 codes bit-exact against the oracle quantizer applied
+    to the GPU's own y. Arguments are torch tensors."""
+    import torch
+    n1, n2 = inp.wl.n1, inp.wl.n2
+    T = inp.X.shape[0]
+    y = y.cpu().numpy()
+    sd = "fp16" if plan.scale_dtype == torch.float16 else "fp32"
+    if plan.per_row:
+        Y = O.transform(inp.X, S.to_bf16_bits(np.eye(n1)), inp.P2, None, inp.wl.dtype)
+        tol, rows = 1e-5, y.reshape(T * n1, n2)
+    else:
+        Y = O.transform(inp.X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
+        tol, rows = TOL[inp.wl.dtype], y
+    rel = rel_l2(y, Y)
+    assert rel <= tol, f"rel-L2 {rel:.3e} > {tol:.0e}"
+    q, s = O.quantize_per_token(np.ascontiguousarray(rows, dtype=np.float32),
+                                np.float32(plan.clip), sd, bits=plan.bits)
+    packed = (O.pack_int4(q) if plan.bits == 4 else O.pack_int8(q)).reshape(T, -1)
+    assert np.array_equal(codes.cpu().numpy(), packed), "codes differ"
+    assert np.array_equal(np_scales(scales).reshape(-1).view(np.uint8), s.view(np.uint8)), \
+        "scales differ"
     return rel
