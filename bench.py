@@ -230,6 +230,9 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
+    # fingerprints of the synthetic inputs, so that runs can be matched to the same data
+    sha = {k: (hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest() if v is not None
+               else None) for k, v in (("X", inp.X), ("P1", inp.P1), ("P2", inp.P2), ("c", inp.c))}
     X0 = dev_tensor(inp.X)
     c = torch.from_numpy(inp.c).to(dev) if inp.c is not None else None
     flags = {"default": 0, "reg1": B.KQ_FLAG_SPLIT_REG1, "reg2": B.KQ_FLAG_SPLIT_REG2,
@@ -342,6 +345,7 @@ def main():
             "alpha": inp.alpha, "kernel": kname, "buffer_sets": nsets,
             "scales_per_token": wl.n1 if wl.per_row else 1, "code_bits": args.bits,
         },
+        "inputs_sha256": sha,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved_gbs,

@@ -1239,6 +1239,12 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
 // least four (then several tokens share a workgroup).
 constexpr int cols_waves(int n2) { return n2 / 32 > kWaves ? n2 / 32 : kWaves; }
 
+// Two workgroups per CU for n2 = 128 and n1 >= 80 (see ColsCfg::TWO), otherwise one.
+constexpr bool cols_two(int n1, int n2, bool has_c) {
+  return n2 == 128 && (n1 + 15) / 16 * 16 >= 80;
+}
+constexpr int cols_min_blocks(int n1, int n2, bool has_c) { return cols_two(n1, n2, has_c) ? 2 : 1; }
+
 template <int N1, int N2, bool HAS_C>
 struct ColsCfg {
   static_assert(N1 >= 16 && N1 <= 128, "n1 in [16, 128]");
@@ -1257,31 +1263,45 @@ struct ColsCfg {
   static constexpr int KK = (N1P + 31) / 32;        // stage-2 reduction steps of 32
   static constexpr bool KHALF = (N1P % 32) != 0;    // last step holds 16 rows + 16 zeros
   static constexpr int CH = N2 / 8;                 // 16-byte chunks per V row
-  // row layout in LDS: an XOR swizzle of the chunks when CH is a power of two, else rows
+  static constexpr int VPLANES = HAS_C ? 2 : 1;     // hi (+ lo) bf16 planes of x*c
+  static constexpr int P1_BYTES = KK * MT * 1024;   // n1 x n1 bf16, zero-padded to 32-steps
+  // Two workgroups per CU (n2 = 128, n1 >= 80): with P2, P1 and the tile in LDS a single
+  // workgroup of 4 waves fills the CU and runs its phases (loads, tile store, stage 1,
+  // stage 2, quantizer, barriers) one after the other. Here each wave keeps its 32-column
+  // block of P2 in registers and c is re-read from L2 for every tile instead of living in
+  // registers; where the tile's planes and P1 would still exceed half of the LDS, the tile
+  // passes through LDS in KH = 2 column halves (stage 1 reduces over each half in turn).
+  // Two workgroups then share the CU and overlap each other's phases.
+  static constexpr bool TWO = cols_two(N1, N2, HAS_C);
+  static constexpr int KH = TWO && N1P * CH * 16 * VPLANES + P1_BYTES + 64 > 80 * 1024 ? 2 : 1;
+  static constexpr int CHK = CH / KH;               // chunks per row of one column part
+  static constexpr int KSH = KS / KH;               // stage-1 steps per column part
+  // row layout in LDS: an XOR swizzle of the chunks when CHK is a power of two, else rows
   // padded by one chunk; either way the 16 rows of one A-operand read hit 16 different
   // bank groups
-  static constexpr bool POW2 = (CH & (CH - 1)) == 0;
-  static constexpr int ROW_CHUNKS = POW2 ? CH : CH + 1;
-  static constexpr int TOK_CHUNKS = N1 * CH;
+  static constexpr bool POW2 = (CHK & (CHK - 1)) == 0;
+  static constexpr int ROW_CHUNKS = POW2 ? CHK : CHK + 1;
+  static constexpr int TOK_CHUNKS = N1 * CHK;       // chunks of one column part of a token
   static constexpr int CPT = (TPI * TOK_CHUNKS + THREADS - 1) / THREADS;  // chunks per thread
   static constexpr bool EVEN = CPT * THREADS == TPI * TOK_CHUNKS;        // no idle slots
   static constexpr int V_BYTES = N1P * ROW_CHUNKS * 16;
+  static constexpr int VBUF = TPI * V_BYTES * VPLANES;
+  static_assert(!TWO || VBUF + P1_BYTES + 64 <= 80 * 1024, "two workgroups per CU");
+  static_assert(KS % KH == 0, "column parts");
   // P2 operands: shared in LDS while they fit, else read from the plan's copy in global
   // memory, which stays in the L2 caches
-  static constexpr bool P2_LDS = N2 <= 128;
+  static constexpr bool P2_LDS = N2 <= 128 && !TWO;
   static constexpr int P2_BYTES = P2_LDS ? N2 * N2 * 2 : 16;
-  static constexpr int P1_BYTES = KK * MT * 1024;   // n1 x n1 bf16, zero-padded to 32-steps
-  static constexpr int VPLANES = HAS_C ? 2 : 1;     // hi (+ lo) bf16 planes of x*c
-  static_assert(!HAS_C || P2_LDS, "column kernel with c: n2 <= 128");
-  static constexpr int VBUF = TPI * V_BYTES * VPLANES;
+  static_assert(!HAS_C || N2 <= 128, "column kernel with c: n2 <= 128");
   // Large n2 (P2 outside LDS): each wave keeps its 32-column block of P2 in registers and
   // the next token's tile arrives by DMA in a second LDS buffer, when two tiles and P1 fit
-  static constexpr bool DMA = !P2_LDS && 2 * VBUF + P1_BYTES + 64 <= 160 * 1024;
+  static constexpr bool DMA = N2 > 128 && 2 * VBUF + P1_BYTES + 64 <= 160 * 1024;
+  static constexpr bool P2REG = DMA || TWO;          // P2 block of the wave in registers
   static constexpr int VBUFS = DMA ? 2 : 1;
   static constexpr int SLOTS = N1 * ROW_CHUNKS;      // 16-byte LDS slots of one tile
   static constexpr int DMA_INSTR = (SLOTS + 63) / 64;
-  static_assert(!DMA || (TPI == 1 && SLOTS % 64 == 0), "tile DMA: whole instructions");
-  static_assert(!PADDED || P2_LDS, "padded n1: n2 <= 128");
+  static_assert(!DMA || (TPI == 1 && SLOTS % 64 == 0 && KH == 1), "tile DMA: whole instructions");
+  static_assert(!PADDED || N2 <= 128, "padded n1: n2 <= 128");
 };
 
 // byte offset of 16-byte chunk `cc` of row `r` of a token tile in LDS
@@ -1292,7 +1312,7 @@ __device__ __forceinline__ int vchunk_off(int r, int cc) {
 }
 
 template <int N1, int N2, bool HAS_C, bool YDBG = false>
-__global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
+__global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2, HAS_C)) void kq_cols_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
     const float *__restrict__ cvec, float clip, int scale_fp16,
@@ -1332,12 +1352,13 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
     const int q = c_ok[i] ? q0 : 0;
     c_ts[i] = q / C::TOK_CHUNKS;
     const int qq = q % C::TOK_CHUNKS;
-    c_row[i] = qq / C::CH;
-    c_cc[i] = qq % C::CH;
+    c_row[i] = qq / C::CHK;
+    c_cc[i] = qq % C::CHK;
   }
-  // per-channel scale of this thread's chunks, kept in registers
-  float creg[HAS_C ? C::CPT : 1][8];
-  if constexpr (HAS_C) {
+  // per-channel scale of this thread's chunks, kept in registers (re-read from L2 for each
+  // tile in the two-workgroup mode)
+  float creg[HAS_C && !C::TWO ? C::CPT : 1][8];
+  if constexpr (HAS_C && !C::TWO) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
@@ -1347,26 +1368,35 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
     }
   }
 
+  // loads of column part h (chunks h CHK .. h CHK + CHK - 1 of every row) of group grp
   uint4 pre[C::CPT];
-  auto issue_loads = [&](int64_t grp) {
+  auto issue_loads = [&](int64_t grp, int h) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int64_t t = grp * C::TPI + c_ts[i];
       if (c_ok[i] && t < T) {
-        pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + c_row[i] * N2 + c_cc[i] * 8);
+        pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + c_row[i] * N2 + (h * C::CHK + c_cc[i]) * 8);
       } else {
         pre[i] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
   };
-  auto store_lds = [&]() {
+  auto store_lds = [&](int h) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       if (!c_ok[i]) continue;
-      const int off = c_ts[i] * C::V_BYTES + vchunk_off<C::CH>(c_row[i], c_cc[i]);
+      const int off = c_ts[i] * C::V_BYTES + vchunk_off<C::CHK>(c_row[i], c_cc[i]);
       if constexpr (HAS_C) {
         uint4 hi, lo;
-        split_scaled(pre[i], creg[i], hi, lo);
+        if constexpr (C::TWO) {
+          const float4 *cp =
+              reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + (h * C::CHK + c_cc[i]) * 8);
+          const float4 a = cp[0], b = cp[1];
+          const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          split_scaled(pre[i], cl, hi, lo);
+        } else {
+          split_scaled(pre[i], creg[i], hi, lo);
+        }
         *reinterpret_cast<uint4 *>(s_v + off) = hi;
         *reinterpret_cast<uint4 *>(s_v + C::TPI * C::V_BYTES + off) = lo;
       } else {
@@ -1391,8 +1421,8 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
       dma16<true>(base, voff, __builtin_amdgcn_readfirstlane(lds_addr(s_v + b * C::VBUF + j * 1024)));
     }
   };
-  bf16x8 p2w[C::DMA ? C::KS : 1][2];
-  if constexpr (C::DMA) {
+  bf16x8 p2w[C::P2REG ? C::KS : 1][2];
+  if constexpr (C::P2REG) {
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       p2w[ks][0] = p2op[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
@@ -1405,7 +1435,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
     if (grp < ngroups) dma_tile(grp, 0);
     wait_and_fence<kWaitVm0>();  // the first tile and P2's registers have landed
   } else {
-    if (grp < ngroups) issue_loads(grp);
+    if (grp < ngroups) issue_loads(grp, 0);
   }
   lds_barrier();  // factors (and the first DMA tile) visible
 
@@ -1414,64 +1444,76 @@ __global__ __launch_bounds__(cols_waves(N2) * 64) void kq_cols_kernel(
 
   for (int it = 0; grp < ngroups; grp += gridDim.x, ++it) {
     const int64_t nxt = grp + gridDim.x;
-    const unsigned char *vt;
-    if constexpr (C::DMA) {
-      // the other buffer was last read in the previous iteration, before its final barrier
-      if (nxt < ngroups) dma_tile(nxt, (it + 1) & 1);
-      vt = s_v + (it & 1) * C::VBUF;
-    } else {
-      store_lds();
-      lds_barrier();
-      if (nxt < ngroups) issue_loads(nxt);  // in flight while this group computes
-      vt = s_v + ts * C::V_BYTES;
-    }
     const int64_t tok = grp * C::TPI + ts;
 
     // ---- stage 1: Z[:, block] = V P2[:, block]  (M = n1 rows, K = n2, N = 32) ----
     f32x4 zacc[C::MT][2];
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) zacc[mt][0] = zacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // (n2 = 256: a rolled loop, so that only one step's operands are in registers)
-#pragma unroll(C::P2_LDS || C::DMA ? C::KS : 1)
-    for (int ks = 0; ks < C::KS; ++ks) {
-      bf16x8 b0, b1;
-      if constexpr (C::P2_LDS) {
-        b0 = sp2[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
-        b1 = sp2[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
-      } else if constexpr (C::DMA) {
-        b0 = p2w[ks][0];
-        b1 = p2w[ks][1];
-      } else {  // from the plan's copy in global memory (L2-resident, shared by all CUs)
-        b0 = p2op[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
-        b1 = p2op[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
-      }
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
-        const int off = vchunk_off<C::CH>(mt * 16 + lr, ks * 4 + g);
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vt + off);
-        zacc[mt][0] = mfma(a, b0, zacc[mt][0]);
-        zacc[mt][1] = mfma(a, b1, zacc[mt][1]);
-        if constexpr (HAS_C) {
-          const bf16x8 al = *reinterpret_cast<const bf16x8 *>(vt + C::TPI * C::V_BYTES + off);
-          zacc[mt][0] = mfma(al, b0, zacc[mt][0]);
-          zacc[mt][1] = mfma(al, b1, zacc[mt][1]);
+    for (int h = 0; h < C::KH; ++h) {  // column parts of the tile
+      const unsigned char *vt;
+      if constexpr (C::DMA) {
+        // the other buffer was last read in the previous iteration, before its final barrier
+        if (nxt < ngroups) dma_tile(nxt, (it + 1) & 1);
+        vt = s_v + (it & 1) * C::VBUF;
+      } else {
+        store_lds(h);
+        lds_barrier();
+        // the next part, or the next group's first part, is in flight while this one computes
+        if (h + 1 < C::KH) issue_loads(grp, h + 1);
+        else if (nxt < ngroups) issue_loads(nxt, 0);
+        vt = s_v + ts * C::V_BYTES;
+      }
+      // (n2 = 256: a rolled loop, so that only one step's operands are in registers)
+#pragma unroll(C::P2_LDS || C::P2REG ? C::KSH : 1)
+      for (int ks = h * C::KSH; ks < (h + 1) * C::KSH; ++ks) {
+        bf16x8 b0, b1;
+        if constexpr (C::P2_LDS) {
+          b0 = sp2[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
+          b1 = sp2[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
+        } else if constexpr (C::P2REG) {
+          b0 = p2w[ks][0];
+          b1 = p2w[ks][1];
+        } else {  // from the plan's copy in global memory (L2-resident, shared by all CUs)
+          b0 = p2op[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
+          b1 = p2op[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
+        }
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+          const int off = vchunk_off<C::CHK>(mt * 16 + lr, (ks - h * C::KSH) * 4 + g);
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vt + off);
+          zacc[mt][0] = mfma(a, b0, zacc[mt][0]);
+          zacc[mt][1] = mfma(a, b1, zacc[mt][1]);
+          if constexpr (HAS_C) {
+            const bf16x8 al = *reinterpret_cast<const bf16x8 *>(vt + C::TPI * C::V_BYTES + off);
+            zacc[mt][0] = mfma(al, b0, zacc[mt][0]);
+            zacc[mt][1] = mfma(al, b1, zacc[mt][1]);
+          }
         }
       }
+      if (h + 1 < C::KH) lds_barrier();  // every wave is done with this part's planes
     }
 
     // ---- stage 2: Y^T[block, :] = Z[:, block]^T P1  (M = 32, K = n1, N = n1) ----
     // The stage-1 accumulators of row tiles (2kk, 2kk+1) form the A operand of step kk;
     // an odd number of row tiles pads the last step with zeros (and P1 with zero rows),
     // so that every accumulator chain uses the same MFMA opcode.
+    // (Z is packed to bf16 first, so that its fp32 accumulators are dead before Y's are live)
+    bf16x8 za[C::KK][2];
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const bool pad = C::KHALF && kk == C::KK - 1;
+      za[kk][0] = pack8(zacc[2 * kk][0], pad ? zero : zacc[(2 * kk + 1) % C::MT][0]);
+      za[kk][1] = pack8(zacc[2 * kk][1], pad ? zero : zacc[(2 * kk + 1) % C::MT][1]);
+    }
     f32x4 yacc[2][C::MT];
 #pragma unroll
     for (int nt = 0; nt < C::MT; ++nt) yacc[0][nt] = yacc[1][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const bool pad = C::KHALF && kk == C::KK - 1;
-      const bf16x8 za0 = pack8(zacc[2 * kk][0], pad ? zero : zacc[(2 * kk + 1) % C::MT][0]);
-      const bf16x8 za1 = pack8(zacc[2 * kk][1], pad ? zero : zacc[(2 * kk + 1) % C::MT][1]);
+      const bf16x8 za0 = za[kk][0], za1 = za[kk][1];
 #pragma unroll
       for (int nt = 0; nt < C::MT; ++nt) {
         const bf16x8 b = sp1[(kk * C::MT + nt) * 64 + lane];
