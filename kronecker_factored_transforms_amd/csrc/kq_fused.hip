@@ -37,6 +37,7 @@
 #include "kq_device.h"
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 namespace {
@@ -105,6 +106,8 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b) {
 // x (8 bf16) * c (8 fp32) in fp32, split into hi = bf16(x*c) and lo = bf16(x*c - hi):
 // hi + lo carries ~16 significant bits, so one extra MFMA pass over lo keeps the
 // per-channel scale from adding a second bf16 rounding to the transform.
+// Per pair of values: 2 unpacks, 2 multiplies, one paired RNE conversion for hi, 2 unpacks
+// of hi, 2 subtractions, one paired conversion for lo (5 VALU per value).
 __device__ __forceinline__ void split_scaled(const uint4 &raw, const float *c, uint4 &hi,
                                              uint4 &lo) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -113,13 +116,15 @@ __device__ __forceinline__ void split_scaled(const uint4 &raw, const float *c, u
   for (int e = 0; e < 4; ++e) {
     const float s0 = __fmul_rn(__uint_as_float(w[e] << 16), c[2 * e]);
     const float s1 = __fmul_rn(__uint_as_float(w[e] & 0xFFFF0000u), c[2 * e + 1]);
-    const __bf16 h0 = (__bf16)s0, h1 = (__bf16)s1;
-    const __bf16 l0 = (__bf16)__fsub_rn(s0, (float)h0);
-    const __bf16 l1 = (__bf16)__fsub_rn(s1, (float)h1);
-    h[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    l[e] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    const bf16x2_t hv = {(__bf16)s0, (__bf16)s1};  // v_cvt_pk_bf16_f32
+    h[e] = __builtin_bit_cast(uint32_t, hv);
+    // opaque to the optimizer, so that hi's fp32 values are unpacked from this word
+    // instead of converting s0 a second time
+    asm("" : "+v"(h[e]));
+    const float r0 = __fsub_rn(s0, __uint_as_float(h[e] << 16));
+    const float r1 = __fsub_rn(s1, __uint_as_float(h[e] & 0xFFFF0000u));
+    const bf16x2_t lv = {(__bf16)r0, (__bf16)r1};
+    l[e] = __builtin_bit_cast(uint32_t, lv);
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
@@ -1368,16 +1373,17 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2, HAS_C)
     }
   }
 
-  // loads of column part h (chunks h CHK .. h CHK + CHK - 1 of every row) of group grp
-  uint4 pre[C::CPT];
+  // loads of column part h (chunks h CHK .. h CHK + CHK - 1 of every row) of group grp,
+  // into that part's own registers
+  uint4 pre[C::KH][C::CPT];
   auto issue_loads = [&](int64_t grp, int h) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int64_t t = grp * C::TPI + c_ts[i];
       if (c_ok[i] && t < T) {
-        pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + c_row[i] * N2 + (h * C::CHK + c_cc[i]) * 8);
+        pre[h][i] = *reinterpret_cast<const uint4 *>(X + t * ldx + c_row[i] * N2 + (h * C::CHK + c_cc[i]) * 8);
       } else {
-        pre[i] = make_uint4(0u, 0u, 0u, 0u);
+        pre[h][i] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
   };
@@ -1393,14 +1399,14 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2, HAS_C)
               reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + (h * C::CHK + c_cc[i]) * 8);
           const float4 a = cp[0], b = cp[1];
           const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          split_scaled(pre[i], cl, hi, lo);
+          split_scaled(pre[h][i], cl, hi, lo);
         } else {
-          split_scaled(pre[i], creg[i], hi, lo);
+          split_scaled(pre[h][i], creg[i], hi, lo);
         }
         *reinterpret_cast<uint4 *>(s_v + off) = hi;
         *reinterpret_cast<uint4 *>(s_v + C::TPI * C::V_BYTES + off) = lo;
       } else {
-        *reinterpret_cast<uint4 *>(s_v + off) = pre[i];
+        *reinterpret_cast<uint4 *>(s_v + off) = pre[h][i];
       }
     }
   };
@@ -1435,7 +1441,9 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2, HAS_C)
     if (grp < ngroups) dma_tile(grp, 0);
     wait_and_fence<kWaitVm0>();  // the first tile and P2's registers have landed
   } else {
-    if (grp < ngroups) issue_loads(grp, 0);
+    if (grp < ngroups)
+#pragma unroll
+      for (int h = 0; h < C::KH; ++h) issue_loads(grp, h);
   }
   lds_barrier();  // factors (and the first DMA tile) visible
 
@@ -1460,9 +1468,9 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2, HAS_C)
       } else {
         store_lds(h);
         lds_barrier();
-        // the next part, or the next group's first part, is in flight while this one computes
-        if (h + 1 < C::KH) issue_loads(grp, h + 1);
-        else if (nxt < ngroups) issue_loads(nxt, 0);
+        // this part's registers are free: the next group's same part is in flight for a
+        // whole group's computation
+        if (nxt < ngroups) issue_loads(nxt, h);
         vt = s_v + ts * C::V_BYTES;
       }
       // (n2 = 256: a rolled loop, so that only one step's operands are in registers)
