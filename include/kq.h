@@ -76,8 +76,8 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
  * a call must have T * n1 < 2^31 rows (else KQ_ERR_UNSUPPORTED). */
 #define KQ_FLAG_PER_ROW 0x400u
 
-/* KQ_FLAG_INT8: INT8 codes instead of INT4 ("FlatQuant" page, mixed-precision settings
- * such as W4A8): step s32 = fp32(fp32(clip * a) / 127), q = clamp(rint(fp32(y * inv)),
+/* KQ_FLAG_INT8: INT8 codes instead of INT4 ("FlatQuant" page, How we know: beyond dense
+ * W4A4 -- mixed precision, where some layers run at W8A8): step s32 = fp32(fp32(clip * a) / 127), q = clamp(rint(fp32(y * inv)),
  * -128, 127), one two's-complement byte per value, so `codes` holds T x n bytes (row
  * stride n). bf16 plans of the stream kernel's shapes: n2 in {64, 128} with n1 in
  * {16, 32, 48, 64}, without c, or n2 = 64 with c; and per-row plans (KQ_FLAG_PER_ROW, one
