@@ -77,10 +77,12 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
 #define KQ_FLAG_PER_ROW 0x400u
 
 /* KQ_FLAG_INT8: INT8 codes instead of INT4 ("FlatQuant" page, How we know: beyond dense
- * W4A4 -- mixed precision, where some layers run at W8A8): step s32 = fp32(fp32(clip * a) / 127), q = clamp(rint(fp32(y * inv)),
- * -128, 127), one two's-complement byte per value, so `codes` holds T x n bytes (row
- * stride n). bf16 plans of the stream kernel's shapes: n2 in {64, 128} with n1 in
- * {16, 32, 48, 64}, without c, or n2 = 64 with c; and per-row plans (KQ_FLAG_PER_ROW, one
+ * W4A4 -- mixed precision, where some layers run at W8A8): step
+ * s32 = fp32(fp32(clip * a) / 127), q = clamp(rint(fp32(y * inv)), -128, 127), one
+ * two's-complement byte per value, so `codes` holds T x n bytes (row stride n). bf16 plans of the stream kernel's shapes: n2 in {64, 128} with n1 in
+ * {16, 32, 48, 64}, without c, or n2 = 64 with c; of the column kernel's shapes: n2 = 128
+ * with n1 in {80, 86, 96, 108, 112, 128}, with or without c, 64 x 128 with c, and n1 = 128
+ * with n2 in {160, 192, 224, 256} without c; and per-row plans (KQ_FLAG_PER_ROW, one
  * step per row of n2 values) with n2 in {64, 128} (KQ_ERR_UNSUPPORTED otherwise); not with
  * KQ_FLAG_FORCE_GENERIC. */
 #define KQ_FLAG_INT8 0x800u

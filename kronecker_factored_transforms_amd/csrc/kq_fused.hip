@@ -1316,7 +1316,8 @@ __device__ __forceinline__ int vchunk_off(int r, int cc) {
   else return (r * (CH + 1) + cc) * 16;
 }
 
-template <int N1, int N2, bool HAS_C, bool YDBG = false>
+// BITS = 4: INT4 codes (8 per dword); BITS = 8: INT8 codes (one byte per value)
+template <int N1, int N2, bool HAS_C, bool YDBG = false, int BITS = 4>
 __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2, HAS_C)) void kq_cols_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
@@ -1544,20 +1545,29 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2, HAS_C)
     float amax = 0.f;
 #pragma unroll
     for (int w = 0; w < C::W; ++w) amax = fmaxf(amax, s_red[ts * C::W + w]);
-    const TokenScale sc = token_scale(amax, clip, scale_fp16);
+    const TokenScale sc = token_scale(amax, clip, scale_fp16, BITS == 4 ? 7.0f : 127.0f);
 
     if (tok < T) {
       // lane holds Y[j = nt*16 + lr][wt*32 + 8g + 4h + r]: 8 consecutive codes -> 1 dword
-      // a uniform row base plus a 32-bit lane offset (nothing 64-bit per lane to keep)
-      uint8_t *crow = codes + tok * (int64_t)(n / 2);
-      const uint32_t loff = (uint32_t)(lr * (N2 / 2) + wt * 16 + g * 4);
+      // (INT4) or 2 dwords (INT8); a uniform row base plus a 32-bit lane offset (nothing
+      // 64-bit per lane to keep)
+      constexpr int RB = N2 * BITS / 8;  // code bytes per row of Y
+      uint8_t *crow = codes + tok * (int64_t)(n * BITS / 8);
+      const uint32_t loff = (uint32_t)(lr * RB + (wt * 32 + g * 8) * BITS / 8);
 #pragma unroll
       for (int nt = 0; nt < C::MT; ++nt) {
         const int j = nt * 16 + lr;
         if (C::PADDED && j >= N1) continue;  // padded rows of Y are not stored
-        const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
-                             yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
-        *reinterpret_cast<uint32_t *>(crow + (loff + (uint32_t)(nt * 16 * (N2 / 2)))) = quant8(yv, sc.inv);
+        uint8_t *dst = crow + (loff + (uint32_t)(nt * 16 * RB));
+        if constexpr (BITS == 8) {
+          const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], sc.inv),
+                             quant4x8(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3], sc.inv)};
+          *reinterpret_cast<u32x2_t *>(dst) = w;
+        } else {
+          const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
+                               yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
+          *reinterpret_cast<uint32_t *>(dst) = quant8(yv, sc.inv);
+        }
         if constexpr (YDBG) {
           float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wt * 32 + g * 8);
           yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
@@ -1587,14 +1597,15 @@ hipError_t launch_reg(const kq_plan *p, const void *X, int64_t T, int64_t ldx, u
   return hipGetLastError();
 }
 
-template <int N1, int N2, bool HAS_C>
+template <int N1, int N2, bool HAS_C, int BITS = 4>
 hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
                        void *scales, float *y_debug, hipStream_t stream) {
   using C = ColsCfg<N1, N2, HAS_C>;
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
   // the debug output has its own instantiation, so that the timed kernel keeps its registers
-  auto k = y_debug ? &kq_cols_kernel<N1, N2, HAS_C, true> : &kq_cols_kernel<N1, N2, HAS_C, false>;
+  auto k = y_debug ? &kq_cols_kernel<N1, N2, HAS_C, true, BITS>
+                   : &kq_cols_kernel<N1, N2, HAS_C, false, BITS>;
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
@@ -1681,6 +1692,10 @@ hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
   kq_fused_variant{A, B, HC, KQ_SPLIT_COLS, 4, 32, ColsCfg<A, B, HC>::THREADS, &launch_cols<A, B, HC>, \
                    reinterpret_cast<const void *>(&kq_cols_kernel<A, B, HC>),          \
                    "fused_mfma_bf16_cols_" #A "x" #B SUF}
+#define KQ_COLS8(A, B, HC, SUF)                                                        \
+  kq_fused_variant{A, B, HC, KQ_SPLIT_COLS, 8, 32, ColsCfg<A, B, HC>::THREADS, &launch_cols<A, B, HC, 8>, \
+                   reinterpret_cast<const void *>(&kq_cols_kernel<A, B, HC, false, 8>), \
+                   "fused_mfma_bf16_cols_" #A "x" #B SUF "_int8"}
 #define KQ_ALL1(A, B)                                                                  \
   KQ_REG(A, B, 1, false, ""), KQ_REG(A, B, 1, true, "_c"), KQ_COLS(A, B, false, ""),    \
       KQ_COLS(A, B, true, "_c")
@@ -1726,6 +1741,17 @@ const kq_fused_variant kVariants[] = {
     KQ_STREAM8(48, 128, false, ""), KQ_STREAM8(64, 128, false, ""),
     KQ_STREAM8(16, 64, true, "_c"), KQ_STREAM8(32, 64, true, "_c"), KQ_STREAM8(48, 64, true, "_c"),
     KQ_STREAM8(64, 64, true, "_c"),
+    // INT8 codes on the column kernel: the shapes where it is the default (n1 > 64, or
+    // 64 x 128 with c), e.g. FFN down-projection inputs kept at 8 bits
+    KQ_COLS8(64, 128, true, "_c"),
+    KQ_COLS8(80, 128, false, ""),  KQ_COLS8(80, 128, true, "_c"),
+    KQ_COLS8(96, 128, false, ""),  KQ_COLS8(96, 128, true, "_c"),
+    KQ_COLS8(112, 128, false, ""), KQ_COLS8(112, 128, true, "_c"),
+    KQ_COLS8(86, 128, false, ""),  KQ_COLS8(86, 128, true, "_c"),
+    KQ_COLS8(108, 128, false, ""), KQ_COLS8(108, 128, true, "_c"),
+    KQ_COLS8(128, 128, false, ""), KQ_COLS8(128, 128, true, "_c"),
+    KQ_COLS8(128, 160, false, ""), KQ_COLS8(128, 192, false, ""),
+    KQ_COLS8(128, 224, false, ""), KQ_COLS8(128, 256, false, ""),
     KQ_STREAM(16, 128), KQ_STREAM(32, 128), KQ_STREAM(48, 128),
     KQ_PAIR(16, 64), KQ_PAIR(32, 64), KQ_PAIR(48, 64), KQ_PAIR(64, 64),
     KQ_PAIR(16, 128), KQ_PAIR(32, 128), KQ_PAIR(48, 128), KQ_PAIR(64, 128),

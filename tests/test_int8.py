@@ -67,11 +67,60 @@ def test_int8_full_size_sampled(gpu):
 
 
 def test_int8_unsupported_shapes(gpu):
-    inp = S.make("down_proj_n14336", T=4)
+    # n2 = 32 has only the register kernels, which have no INT8 epilogue
+    wl = replace(S.WORKLOADS["hidden_n8192"], n1=16, n2=32, n_outliers=2, pivot_channels=0)
+    inp = S.make(wl, T=4)
     X, P1, P2, c = K.device_inputs(inp)
     with pytest.raises(B.KqError) as e:
-        B.kq_create(112, 128, "bf16", "fp16", P1, P2, c, 1.0, None, B.KQ_FLAG_INT8)
+        B.kq_create(16, 32, "bf16", "fp16", P1, P2, None, 1.0, None, B.KQ_FLAG_INT8)
     assert e.value.status == B.KQ_ERR_UNSUPPORTED
+
+
+COLS_SHAPES = [(112, 128, True), (86, 128, True), (108, 128, False), (96, 128, True),
+               (128, 128, True), (64, 128, True), (80, 128, False), (128, 224, False),
+               (128, 160, False), (128, 256, False)]
+
+
+@pytest.mark.parametrize("n1,n2,with_c", COLS_SHAPES)
+@pytest.mark.parametrize("T", [1, 203])
+def test_int8_cols_parity(gpu, n1, n2, with_c, T):
+    """INT8 codes from the column kernel (two workgroups per CU, column halves, padded
+    n1, P2 in registers or L2 for n2 > 128), e.g. down-projection inputs kept at 8 bits."""
+    import torch
+    base = S.WORKLOADS["down_proj_n14336"] if with_c else S.WORKLOADS["hidden_n8192"]
+    wl = replace(base, n1=n1, n2=n2, n_outliers=4, pivot_channels=0)
+    inp = S.make(wl, T=T)
+    plan, X = _plan(inp)
+    assert plan.kernel == f"fused_mfma_bf16_cols_{n1}x{n2}{'_c' if with_c else ''}_int8", plan.kernel
+    codes, scales, y = K.run(plan, X, y_debug=True)
+    codes2, scales2 = K.run(plan, X, y_debug=False)
+    assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
+    assert tuple(codes.shape) == (T, n1 * n2)
+    _check(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+@pytest.mark.parametrize("name", ["down_proj_n14336", "down_proj_n28672"])
+def test_int8_cols_strided_and_full_size_sampled(gpu, name):
+    """Full-size INT8 run in the bench's launch configuration, sampled tokens checked
+    against the oracle; the same codes through a row stride larger than the row."""
+    import torch
+    inp = S.make(name)
+    plan, X = _plan(inp)
+    codes, scales = K.run(plan, X, y_debug=False)
+    n = inp.wl.n
+    T = 3 * 256 + 77
+    wide = torch.zeros((T, n + 64), dtype=torch.bfloat16, device=gpu)
+    wide[:, 32:32 + n] = X[:T]
+    c2, s2 = K.run(plan, wide[:, 32:32 + n], y_debug=False)
+    assert torch.equal(c2, codes[:T]) and torch.equal(s2, scales[:T])
+    rng = np.random.default_rng(9)
+    ids = np.unique(np.concatenate([[0, inp.wl.T - 1], rng.integers(0, inp.wl.T, 100)]))
+    sub = S.make(name, token_ids=ids)
+    Xs = K.torch_from(sub.X, "bf16").to("cuda:0")
+    cs, ss, ys = K.run(plan, Xs, y_debug=True)
+    idx = torch.from_numpy(ids).cuda()
+    assert torch.equal(codes[idx], cs) and torch.equal(scales[idx], ss)
+    _check(sub, cs.cpu().numpy(), K.np_scales(ss), ys.cpu().numpy(), plan.clip)
 
 
 @pytest.mark.parametrize("n1,n2,T", [(8, 128, 777), (3, 64, 41), (1, 128, 5), (32, 128, 129)])

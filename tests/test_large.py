@@ -36,6 +36,8 @@ CASES = {
     "cols_c_112x128": (W["down_proj_n14336"], 0, 4, False, 0),
     "cols_c_86x128": (W["ffn_n11008"], 0, 4, False, 64),
     "cols_128x224": (W["down_proj_n28672"], 0, 4, False, 0),
+    "cols_c_112x128_int8": (W["down_proj_n14336"], 0, 8, False, 64),
+    "cols_128x224_int8": (W["down_proj_n28672"], 0, 8, False, 0),
     "cols_128x256": (replace(W["down_proj_n28672"], n2=256), 0, 4, False, 64),
     "rows": (W["kv_h8_d128"], 0, 4, True, 0),
     "rows_strided": (W["kv_h8_d128"], 0, 4, True, 64),
