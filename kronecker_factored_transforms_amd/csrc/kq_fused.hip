@@ -765,10 +765,27 @@ struct PairCfg {
   static constexpr int kWaitHalf = 0x0F70 | (HALF_LOADS & 15) | ((HALF_LOADS >> 4) << 14);
 };
 
-template <int N1, int N2>
+// lane's LPL consecutive codes of each of its rows: LPL / 2 bytes (INT4) or LPL bytes (INT8)
+template <int N1, int N2, int BITS = 4>
 __device__ __forceinline__ void store_codes_half(uint8_t *codes, int64_t tok, int wave,
-                                                 const uint32_t (*w)[N2 / 64], int lr, int g) {
+                                                 const uint32_t (*w)[BITS == 4 ? N2 / 64 : N2 / 32],
+                                                 int lr, int g) {
   using C = PairCfg<N1, N2>;
+  if constexpr (BITS == 8) {
+    uint8_t *crow = codes + tok * (int64_t)(N1 * N2) + wave * C::CB + g * C::LPL;
+#pragma unroll
+    for (int nt = 0; nt < C::MT; ++nt) {
+      uint8_t *dst = crow + (nt * 16 + lr) * N2;
+      if constexpr (N2 == 128) {
+        const u32x4_t v = {w[nt][0], w[nt][1], w[nt][2], w[nt][3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
+      } else {
+        const u32x2_t v = {w[nt][0], w[nt][1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(dst));
+      }
+    }
+    return;
+  }
   uint8_t *crow = codes + tok * (int64_t)(N1 * N2 / 2) + wave * (C::CB / 2) + g * (C::LPL / 2);
 #pragma unroll
   for (int nt = 0; nt < C::MT; ++nt) {
@@ -782,7 +799,7 @@ __device__ __forceinline__ void store_codes_half(uint8_t *codes, int64_t tok, in
   }
 }
 
-template <int N1, int N2, bool YDBG>
+template <int N1, int N2, bool YDBG, int BITS = 4>
 __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
@@ -831,7 +848,8 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
   wait_and_fence<kWaitVm0>();
   if (tok + G < T) dma_half(tok + G, 1);
 
-  uint32_t pend[C::MT][C::NH / 2];  // codes of the previous token, stored one step late
+  // codes of the previous token, stored one step late (8 or 4 values per dword)
+  uint32_t pend[C::MT][BITS == 4 ? C::NH / 2 : C::NH];
   TokenScale pend_s{0.f, (_Float16)0.f, 0.f};
   int64_t pend_tok = -1;
 
@@ -845,7 +863,7 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     if (pend_tok >= 0) {
-      store_codes_half<N1, N2>(codes, pend_tok, wave, pend, lr, g);
+      store_codes_half<N1, N2, BITS>(codes, pend_tok, wave, pend, lr, g);
       if (wave == 0 && lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
     }
     const unsigned char *tile = s_tile[b];
@@ -908,8 +926,10 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
     const float amax = fmaxf(m, s_max[wave ^ 1]);
     if (tok + 2 * G < T) dma_half(tok + 2 * G, b);  // both waves are done with buffer b
 
-    const TokenScale ts = token_scale(amax, clip, scale_fp16);
-    if (__builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, ts.s32) ? 1 : 0)) {
+    const TokenScale ts = token_scale(amax, clip, scale_fp16, BITS == 4 ? 7.0f : 127.0f);
+    if constexpr (BITS == 8) {
+      quant_tile8<C::MT, C::NH>(yacc, ts.inv, pend);
+    } else if (__builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, ts.s32) ? 1 : 0)) {
       quant_tile<true, C::MT, C::NH>(yacc, ts.inv, pend);
     } else {
       quant_tile<false, C::MT, C::NH>(yacc, ts.inv, pend);
@@ -928,7 +948,7 @@ __global__ __launch_bounds__(128, 2) void kq_pair_kernel(
     }
   }
   if (pend_tok >= 0) {
-    store_codes_half<N1, N2>(codes, pend_tok, wave, pend, lr, g);
+    store_codes_half<N1, N2, BITS>(codes, pend_tok, wave, pend, lr, g);
     if (wave == 0 && lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
   }
 }
@@ -1245,10 +1265,8 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
 constexpr int cols_waves(int n2) { return n2 / 32 > kWaves ? n2 / 32 : kWaves; }
 
 // Two workgroups per CU for n2 = 128 and n1 >= 80 (see ColsCfg::TWO), otherwise one.
-constexpr bool cols_two(int n1, int n2, bool has_c) {
-  return n2 == 128 && (n1 + 15) / 16 * 16 >= 80;
-}
-constexpr int cols_min_blocks(int n1, int n2, bool has_c) { return cols_two(n1, n2, has_c) ? 2 : 1; }
+constexpr bool cols_two(int n1, int n2) { return n2 == 128 && (n1 + 15) / 16 * 16 >= 80; }
+constexpr int cols_min_blocks(int n1, int n2) { return cols_two(n1, n2) ? 2 : 1; }
 
 template <int N1, int N2, bool HAS_C>
 struct ColsCfg {
@@ -1277,7 +1295,7 @@ struct ColsCfg {
   // registers; where the tile's planes and P1 would still exceed half of the LDS, the tile
   // passes through LDS in KH = 2 column halves (stage 1 reduces over each half in turn).
   // Two workgroups then share the CU and overlap each other's phases.
-  static constexpr bool TWO = cols_two(N1, N2, HAS_C);
+  static constexpr bool TWO = cols_two(N1, N2);
   static constexpr int KH = TWO && N1P * CH * 16 * VPLANES + P1_BYTES + 64 > 80 * 1024 ? 2 : 1;
   static constexpr int CHK = CH / KH;               // chunks per row of one column part
   static constexpr int KSH = KS / KH;               // stage-1 steps per column part
@@ -1318,7 +1336,7 @@ __device__ __forceinline__ int vchunk_off(int r, int cc) {
 
 // BITS = 4: INT4 codes (8 per dword); BITS = 8: INT8 codes (one byte per value)
 template <int N1, int N2, bool HAS_C, bool YDBG = false, int BITS = 4>
-__global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2, HAS_C)) void kq_cols_kernel(
+__global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2)) void kq_cols_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
     const float *__restrict__ cvec, float clip, int scale_fp16,
@@ -1631,12 +1649,12 @@ hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx
   return hipGetLastError();
 }
 
-template <int N1, int N2>
+template <int N1, int N2, int BITS = 4>
 hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
                        void *scales, float *y_debug, hipStream_t stream) {
   using C = PairCfg<N1, N2>;
   const int grid = (int)(T < (int64_t)p->grid_cap ? T : (int64_t)p->grid_cap);
-  auto k = y_debug ? &kq_pair_kernel<N1, N2, true> : &kq_pair_kernel<N1, N2, false>;
+  auto k = y_debug ? &kq_pair_kernel<N1, N2, true, BITS> : &kq_pair_kernel<N1, N2, false, BITS>;
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
@@ -1650,6 +1668,11 @@ hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
                    &launch_pair<A, B>,                                                 \
                    reinterpret_cast<const void *>(&kq_pair_kernel<A, B, false>),       \
                    "fused_mfma_bf16_pair_" #A "x" #B}
+#define KQ_PAIR8(A, B)                                                                 \
+  kq_fused_variant{A, B, false, KQ_SPLIT_PAIR, 8, (B) / 2, PairCfg<A, B>::THREADS,          \
+                   &launch_pair<A, B, 8>,                                              \
+                   reinterpret_cast<const void *>(&kq_pair_kernel<A, B, false, 8>),    \
+                   "fused_mfma_bf16_pair_" #A "x" #B "_int8"}
 template <int N2, int BITS = 4>
 hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
                        void *scales, float *y_debug, hipStream_t stream) {
@@ -1755,6 +1778,8 @@ const kq_fused_variant kVariants[] = {
     KQ_STREAM(16, 128), KQ_STREAM(32, 128), KQ_STREAM(48, 128),
     KQ_PAIR(16, 64), KQ_PAIR(32, 64), KQ_PAIR(48, 64), KQ_PAIR(64, 64),
     KQ_PAIR(16, 128), KQ_PAIR(32, 128), KQ_PAIR(48, 128), KQ_PAIR(64, 128),
+    KQ_PAIR8(16, 64), KQ_PAIR8(32, 64), KQ_PAIR8(48, 64), KQ_PAIR8(64, 64),
+    KQ_PAIR8(16, 128), KQ_PAIR8(32, 128), KQ_PAIR8(48, 128), KQ_PAIR8(64, 128),
 };
 
 }  // namespace

@@ -43,12 +43,35 @@ def test_int8_parity(gpu, n1, n2, with_c, T):
     wl = replace(base, n1=n1, n2=n2, n_outliers=4, pivot_channels=0)
     inp = S.make(wl, T=T)
     plan, X = _plan(inp)
-    assert plan.kernel.endswith("_int8") and plan.kernel_for(T) == plan.kernel
+    # small batches of the stream shapes without c run on the pair split
+    small = f"fused_mfma_bf16_pair_{n1}x{n2}_int8" if not with_c else plan.kernel
+    assert plan.kernel.endswith("_int8") and plan.kernel_for(T) == small
     codes, scales, y = K.run(plan, X, y_debug=True)
     codes2, scales2 = K.run(plan, X, y_debug=False)
     assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
     assert tuple(codes.shape) == (T, n1 * n2)
     _check(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+@pytest.mark.parametrize("n1,n2", [(64, 128), (16, 64), (48, 128)])
+@pytest.mark.parametrize("T", [1, 77, 1500])
+def test_int8_pair_split(gpu, n1, n2, T):
+    """INT8 codes from the pair split (two waves per token), forced with its flag at any
+    T, and the same codes from the default plan, which runs it below about four tokens
+    per CU and the stream kernel above."""
+    import torch
+    wl = replace(S.WORKLOADS["hidden_n8192"], n1=n1, n2=n2, n_outliers=4, pivot_channels=0)
+    inp = S.make(wl, T=T)
+    X, P1, P2, c = K.device_inputs(inp)
+    pair = B.Plan(P1, P2, None, inp.alpha, inp.wl.scale_dtype, bits=8, flags=B.KQ_FLAG_SPLIT_PAIR)
+    assert pair.kernel == f"fused_mfma_bf16_pair_{n1}x{n2}_int8"
+    codes, scales, y = K.run(pair, X, y_debug=True)
+    codes2, scales2 = K.run(pair, X, y_debug=False)
+    assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
+    _check(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), pair.clip)
+    dflt, _ = _plan(inp)
+    c3, s3 = K.run(dflt, X, y_debug=False)
+    assert torch.equal(codes, c3) and torch.equal(scales, s3)
 
 
 def test_int8_full_size_sampled(gpu):
