@@ -1260,9 +1260,13 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
 // ------------------------------------------------------------------------------------
 // column kernel: W = n2/32 waves per token
 // ------------------------------------------------------------------------------------
-// Waves per workgroup of the column kernel: one per 32 output columns of a token, at
-// least four (then several tokens share a workgroup).
-constexpr int cols_waves(int n2) { return n2 / 32 > kWaves ? n2 / 32 : kWaves; }
+// Waves per workgroup of the column kernel: one per 32 output columns of a token (n2p is
+// n2 rounded up to a multiple of 32); where that is fewer than four, as many whole tokens
+// as fill four waves share a workgroup.
+constexpr int cols_waves(int n2p) {
+  return n2p / 32 >= kWaves ? n2p / 32 : (n2p / 32) * (kWaves / (n2p / 32));
+}
+constexpr int cols_n2p(int n2) { return (n2 + 31) / 32 * 32; }
 
 // Two workgroups per CU for n2 = 128 and n1 >= 80 (see ColsCfg::TWO), otherwise one.
 constexpr bool cols_two(int n1, int n2) { return n2 == 128 && (n1 + 15) / 16 * 16 >= 80; }
@@ -1271,9 +1275,14 @@ constexpr int cols_min_blocks(int n1, int n2) { return cols_two(n1, n2) ? 2 : 1;
 template <int N1, int N2, bool HAS_C>
 struct ColsCfg {
   static_assert(N1 >= 16 && N1 <= 128, "n1 in [16, 128]");
-  static_assert(N2 % 32 == 0 && N2 >= 32 && N2 <= 256, "n2 must be a multiple of 32 up to 256");
-  static constexpr int W = N2 / 32;                 // waves per token
-  static constexpr int WAVES = cols_waves(N2);      // waves per workgroup
+  static_assert(N2 % 16 == 0 && N2 >= 32 && N2 <= 256, "n2 must be a multiple of 16 in [32, 256]");
+  // n2 that is not a multiple of 32 is padded with zero columns to N2P: P2's padded rows
+  // and columns are zero (in the plan's operand copy), so the padded columns of V add
+  // nothing to Z and the padded columns of Y are zero; they are not stored
+  static constexpr int N2P = cols_n2p(N2);
+  static constexpr bool PADC = N2P != N2;
+  static constexpr int W = N2P / 32;                // waves per token
+  static constexpr int WAVES = cols_waves(N2P);     // waves per workgroup
   static constexpr int THREADS = WAVES * 64;
   static constexpr int TPI = WAVES / W;             // tokens per workgroup iteration
   // n1 that is not a multiple of 16 is padded to whole row tiles: the padded rows of V
@@ -1282,10 +1291,11 @@ struct ColsCfg {
   static constexpr bool PADDED = (N1 % 16) != 0;
   static constexpr int MT = (N1 + 15) / 16;         // 16-row tiles of V / Z
   static constexpr int N1P = MT * 16;
-  static constexpr int KS = N2 / 32;                // stage-1 reduction steps
+  static constexpr int KS = N2P / 32;               // stage-1 reduction steps
   static constexpr int KK = (N1P + 31) / 32;        // stage-2 reduction steps of 32
   static constexpr bool KHALF = (N1P % 32) != 0;    // last step holds 16 rows + 16 zeros
-  static constexpr int CH = N2 / 8;                 // 16-byte chunks per V row
+  static constexpr int CH = N2 / 8;                 // 16-byte chunks per row of X
+  static constexpr int CHP = N2P / 8;               // chunks per row of the tile in LDS
   static constexpr int VPLANES = HAS_C ? 2 : 1;     // hi (+ lo) bf16 planes of x*c
   static constexpr int P1_BYTES = KK * MT * 1024;   // n1 x n1 bf16, zero-padded to 32-steps
   // Two workgroups per CU (n2 = 128, n1 >= 80): with P2, P1 and the tile in LDS a single
@@ -1297,13 +1307,15 @@ struct ColsCfg {
   // Two workgroups then share the CU and overlap each other's phases.
   static constexpr bool TWO = cols_two(N1, N2);
   static constexpr int KH = TWO && N1P * CH * 16 * VPLANES + P1_BYTES + 64 > 80 * 1024 ? 2 : 1;
+  static_assert(KH == 1 || !PADC, "column parts of a padded row");
   static constexpr int CHK = CH / KH;               // chunks per row of one column part
+  static constexpr int CHL = CHP / KH;              // the same in LDS (with padded columns)
   static constexpr int KSH = KS / KH;               // stage-1 steps per column part
-  // row layout in LDS: an XOR swizzle of the chunks when CHK is a power of two, else rows
+  // row layout in LDS: an XOR swizzle of the chunks when CHL is a power of two, else rows
   // padded by one chunk; either way the 16 rows of one A-operand read hit 16 different
   // bank groups
-  static constexpr bool POW2 = (CHK & (CHK - 1)) == 0;
-  static constexpr int ROW_CHUNKS = POW2 ? CHK : CHK + 1;
+  static constexpr bool POW2 = (CHL & (CHL - 1)) == 0;
+  static constexpr int ROW_CHUNKS = POW2 ? CHL : CHL + 1;
   static constexpr int TOK_CHUNKS = N1 * CHK;       // chunks of one column part of a token
   static constexpr int CPT = (TPI * TOK_CHUNKS + THREADS - 1) / THREADS;  // chunks per thread
   static constexpr bool EVEN = CPT * THREADS == TPI * TOK_CHUNKS;        // no idle slots
@@ -1313,12 +1325,12 @@ struct ColsCfg {
   static_assert(KS % KH == 0, "column parts");
   // P2 operands: shared in LDS while they fit, else read from the plan's copy in global
   // memory, which stays in the L2 caches
-  static constexpr bool P2_LDS = N2 <= 128 && !TWO;
-  static constexpr int P2_BYTES = P2_LDS ? N2 * N2 * 2 : 16;
+  static constexpr bool P2_LDS = N2P <= 128 && !TWO;
+  static constexpr int P2_BYTES = P2_LDS ? N2P * N2P * 2 : 16;
   static_assert(!HAS_C || N2 <= 128, "column kernel with c: n2 <= 128");
   // Large n2 (P2 outside LDS): each wave keeps its 32-column block of P2 in registers and
   // the next token's tile arrives by DMA in a second LDS buffer, when two tiles and P1 fit
-  static constexpr bool DMA = N2 > 128 && 2 * VBUF + P1_BYTES + 64 <= 160 * 1024;
+  static constexpr bool DMA = N2P > 128 && 2 * VBUF + P1_BYTES + 64 <= 160 * 1024;
   static constexpr bool P2REG = DMA || TWO;          // P2 block of the wave in registers
   static constexpr int VBUFS = DMA ? 2 : 1;
   static constexpr int SLOTS = N1 * ROW_CHUNKS;      // 16-byte LDS slots of one tile
@@ -1336,7 +1348,7 @@ __device__ __forceinline__ int vchunk_off(int r, int cc) {
 
 // BITS = 4: INT4 codes (8 per dword); BITS = 8: INT8 codes (one byte per value)
 template <int N1, int N2, bool HAS_C, bool YDBG = false, int BITS = 4>
-__global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2)) void kq_cols_kernel(
+__global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, N2)) void kq_cols_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
     const float *__restrict__ cvec, float clip, int scale_fp16,
@@ -1365,6 +1377,16 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2)) void 
       *reinterpret_cast<uint4 *>(s_v + (q / PAD_UNITS) * C::V_BYTES + N1 * C::ROW_CHUNKS * 16 +
                                  (q % PAD_UNITS) * 16) = make_uint4(0u, 0u, 0u, 0u);
   }
+  if constexpr (C::PADC && !C::DMA) {  // chunks CH .. CHP of every row stay zero
+    constexpr int PC = C::CHP - C::CH, PER_PLANE = N1 * PC;
+    for (int q = tid; q < C::TPI * C::VPLANES * PER_PLANE; q += C::THREADS) {
+      const int pl = q / PER_PLANE, r = (q % PER_PLANE) / PC, cc = C::CH + q % PC;
+      *reinterpret_cast<uint4 *>(s_v + pl * C::V_BYTES + vchunk_off<C::CHL>(r, cc)) =
+          make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // (with the tile DMA, the padded chunks of a row receive a copy of its first chunk:
+  // finite values that meet P2's zero rows)
 
   // per-thread chunk coordinates (fixed for the whole kernel)
   int c_ts[C::CPT], c_row[C::CPT], c_cc[C::CPT];
@@ -1410,7 +1432,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2)) void 
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       if (!c_ok[i]) continue;
-      const int off = c_ts[i] * C::V_BYTES + vchunk_off<C::CHK>(c_row[i], c_cc[i]);
+      const int off = c_ts[i] * C::V_BYTES + vchunk_off<C::CHL>(c_row[i], c_cc[i]);
       if constexpr (HAS_C) {
         uint4 hi, lo;
         if constexpr (C::TWO) {
@@ -1508,7 +1530,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2)) void 
         }
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) {
-          const int off = vchunk_off<C::CHK>(mt * 16 + lr, (ks - h * C::KSH) * 4 + g);
+          const int off = vchunk_off<C::CHL>(mt * 16 + lr, (ks - h * C::KSH) * 4 + g);
           const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vt + off);
           zacc[mt][0] = mfma(a, b0, zacc[mt][0]);
           zacc[mt][1] = mfma(a, b1, zacc[mt][1]);
@@ -1576,6 +1598,7 @@ __global__ __launch_bounds__(cols_waves(N2) * 64, cols_min_blocks(N1, N2)) void 
       for (int nt = 0; nt < C::MT; ++nt) {
         const int j = nt * 16 + lr;
         if (C::PADDED && j >= N1) continue;  // padded rows of Y are not stored
+        if (C::PADC && wt * 32 + g * 8 >= N2) continue;  // nor its padded columns
         uint8_t *dst = crow + (loff + (uint32_t)(nt * 16 * RB));
         if constexpr (BITS == 8) {
           const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], sc.inv),
@@ -1752,6 +1775,12 @@ const kq_fused_variant kVariants[] = {
     // hidden sizes whose larger factor exceeds 128 (e.g. 28672 -> 128 x 224)
     KQ_COLS(128, 160, false, ""),  KQ_COLS(128, 192, false, ""),
     KQ_COLS(128, 224, false, ""),  KQ_COLS(128, 256, false, ""),
+    // n2 an odd multiple of 16, padded to a multiple of 32: the factors that minimise
+    // n1 + n2 for 1536 (32 x 48), 5120 (64 x 80), 7168 (64 x 112) and 18432 (128 x 144)
+    KQ_COLS(32, 48, false, ""),    KQ_COLS(32, 48, true, "_c"),
+    KQ_COLS(64, 80, false, ""),    KQ_COLS(64, 80, true, "_c"),
+    KQ_COLS(64, 112, false, ""),   KQ_COLS(64, 112, true, "_c"),
+    KQ_COLS(128, 144, false, ""),
     // the other splits, selectable with KQ_FLAG_SPLIT_*
     KQ_ALL1(16, 32), KQ_ALL1(32, 32), KQ_ALL(16, 64), KQ_ALL(32, 64), KQ_ALL(48, 64),
     KQ_ALL(64, 64), KQ_ALL(16, 128), KQ_ALL(32, 128), KQ_ALL(48, 128), KQ_ALL(64, 128),
@@ -1775,6 +1804,10 @@ const kq_fused_variant kVariants[] = {
     KQ_COLS8(128, 128, false, ""), KQ_COLS8(128, 128, true, "_c"),
     KQ_COLS8(128, 160, false, ""), KQ_COLS8(128, 192, false, ""),
     KQ_COLS8(128, 224, false, ""), KQ_COLS8(128, 256, false, ""),
+    KQ_COLS8(32, 48, false, ""),   KQ_COLS8(32, 48, true, "_c"),
+    KQ_COLS8(64, 80, false, ""),   KQ_COLS8(64, 80, true, "_c"),
+    KQ_COLS8(64, 112, false, ""),  KQ_COLS8(64, 112, true, "_c"),
+    KQ_COLS8(128, 144, false, ""),
     KQ_STREAM(16, 128), KQ_STREAM(32, 128), KQ_STREAM(48, 128),
     KQ_PAIR(16, 64), KQ_PAIR(32, 64), KQ_PAIR(48, 64), KQ_PAIR(64, 64),
     KQ_PAIR(16, 128), KQ_PAIR(32, 128), KQ_PAIR(48, 128), KQ_PAIR(64, 128),
@@ -1826,7 +1859,11 @@ size_t kq_fused_p1op_elems(int n1) {
   const int mt = (n1 + 15) / 16;  // n1 padded to whole 16-row tiles
   return (size_t)((mt * 16 + 31) / 32) * mt * 512;
 }
-size_t kq_fused_p2op_elems(int n2) { return (size_t)n2 * (size_t)n2; }
+// n2 that is not a multiple of 32 is padded with zero rows and columns to the next one
+size_t kq_fused_p2op_elems(int n2) {
+  const size_t n2p = (size_t)(n2 + 31) / 32 * 32;
+  return n2p * n2p;
+}
 
 // P2 as stage-1 B operands, in blocks of `cb` output columns (one block per wave that
 // shares a token): [block wb][step ks][tile a][lane L][slot v] =
@@ -1834,8 +1871,10 @@ size_t kq_fused_p2op_elems(int n2) { return (size_t)n2 * (size_t)n2; }
 // Reduction slot (g, v) of step ks carries row 32 ks + 8 g + v. The 16 columns of tile a
 // are spread so that, after stage 2, lane group g holds the cb/4 consecutive output
 // columns cb wb + (cb/4) g + [0, cb/4) of a row of Y, i.e. cb/8 packed code bytes.
+// Rows and columns from n2 up to the next multiple of 32 are zero.
 void kq_fused_arrange_p2(const uint16_t *P2, int n2, int cb, uint16_t *out) {
-  const int KS = n2 / 32, NB = n2 / cb, NT = cb / 16;
+  const int n2p = (n2 + 31) / 32 * 32;
+  const int KS = n2p / 32, NB = n2p / cb, NT = cb / 16;
   size_t o = 0;
   for (int wb = 0; wb < NB; ++wb)
     for (int ks = 0; ks < KS; ++ks)
@@ -1843,7 +1882,8 @@ void kq_fused_arrange_p2(const uint16_t *P2, int n2, int cb, uint16_t *out) {
         for (int L = 0; L < 64; ++L)
           for (int v = 0; v < 8; ++v) {
             const int g = L / 16, x = L % 16, b = x / 4, r = x % 4;
-            out[o++] = P2[(size_t)(32 * ks + 8 * g + v) * n2 + cb * wb + (cb / 4) * b + 4 * a + r];
+            const int i = 32 * ks + 8 * g + v, j = cb * wb + (cb / 4) * b + 4 * a + r;
+            out[o++] = i < n2 && j < n2 ? P2[(size_t)i * n2 + j] : (uint16_t)0;
           }
 }
 

@@ -101,6 +101,15 @@ WORKLOADS = {
         "ffn_n11008", 8, T=8192, n1=86, n2=128, dtype="bf16", x_kind="silu_gate",
         p_kind="near_identity", p_eps=0.05, c_kind="loguniform", c_lo=0.25, c_hi=4.0,
         alpha=None),
+    # DeepSeek-V3-class hidden size 7168 with the factors that minimise n1 + n2 (64 x 112:
+    # n2 is an odd multiple of 16), heavy-tailed activations
+    "hidden_n7168": Workload(
+        "hidden_n7168", 9, T=16384, n1=64, n2=112, dtype="bf16", x_kind="student_t3",
+        n_outliers=8, outlier_scale=30.0, p_kind="orthogonal", alpha=3.0),
+    # DeepSeek-V3-class dense FFN down-projection input, 18432 = 128 x 144
+    "ffn_n18432": Workload(
+        "ffn_n18432", 10, T=4096, n1=128, n2=144, dtype="bf16", x_kind="silu_gate",
+        p_kind="orthogonal", alpha=3.0),
     # a larger factor than 128: the 70B-class FFN down-projection input, 28672 = 128 x 224
     "down_proj_n28672": Workload(
         "down_proj_n28672", 6, T=4096, n1=128, n2=224, dtype="bf16", x_kind="silu_gate",

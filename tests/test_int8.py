@@ -101,7 +101,8 @@ def test_int8_unsupported_shapes(gpu):
 
 COLS_SHAPES = [(112, 128, True), (86, 128, True), (108, 128, False), (96, 128, True),
                (128, 128, True), (64, 128, True), (80, 128, False), (128, 224, False),
-               (128, 160, False), (128, 256, False)]
+               (128, 160, False), (128, 256, False), (64, 112, True), (128, 144, False),
+               (32, 48, True)]
 
 
 @pytest.mark.parametrize("n1,n2,with_c", COLS_SHAPES)

@@ -34,6 +34,8 @@ SMALL = [
     ("prefill_n8192_t65536", 777),
     ("down_proj_n28672", 203),
     ("ffn_n11008", 301),
+    ("hidden_n7168", 333),
+    ("ffn_n18432", 277),
 ]
 
 
@@ -51,7 +53,7 @@ def test_parity_against_full_oracle(gpu, name, T):
 
 
 FULL = ["attn_n4096", "hidden_n8192", "down_proj_n14336", "decode_n8192_t64",
-        "prefill_n8192_t65536", "down_proj_n28672", "ffn_n11008"]
+        "prefill_n8192_t65536", "down_proj_n28672", "ffn_n11008", "hidden_n7168", "ffn_n18432"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -18,6 +18,8 @@ def test_workload_shapes():
     assert shapes["down_proj_n28672"] == (4096, 128, 224, "bf16")
     assert shapes["kv_h8_d128"] == (65536, 8, 128, "bf16")
     assert shapes["ffn_n11008"] == (8192, 86, 128, "bf16")
+    assert shapes["hidden_n7168"] == (16384, 64, 112, "bf16")
+    assert shapes["ffn_n18432"] == (4096, 128, 144, "bf16")
 
 
 def test_same_seed_same_bytes_and_token_subsets_agree():

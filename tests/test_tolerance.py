@@ -19,7 +19,7 @@ from oracle import kq_oracle as O
 
 GATE = 2e-3
 BF16_WORKLOADS = ["attn_n4096", "hidden_n8192", "down_proj_n14336", "decode_n8192_t64",
-                  "down_proj_n28672", "ffn_n11008"]
+                  "down_proj_n28672", "ffn_n11008", "hidden_n7168", "ffn_n18432"]
 
 
 def _bf16(a64):

@@ -20,12 +20,16 @@ SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (3
           (48, 128, True), (16, 64, True), (48, 64, False), (32, 32, True), (16, 32, False),
           (112, 128, False), (112, 128, True), (96, 128, False), (128, 128, True), (80, 128, False),
           (128, 160, False), (128, 224, False), (128, 256, False), (128, 224, True),
-          (86, 128, False), (86, 128, True), (108, 128, False), (108, 128, True)]
+          (86, 128, False), (86, 128, True), (108, 128, False), (108, 128, True),
+          (32, 48, False), (32, 48, True), (64, 80, False), (64, 80, True), (64, 112, False),
+          (64, 112, True), (128, 144, False)]
 
 
 def _available(n1, n2, split, with_c=False):
     if n2 > 128:  # only the column kernel, without c (P2 operands read from L2)
         return split == "cols" and not with_c
+    if n2 % 32:  # n2 padded to a multiple of 32: only the column kernel
+        return split == "cols"
     if split == "deep":
         return (n1, n2, with_c) in DEEP_SHAPES
     if split == "stream":
@@ -97,6 +101,27 @@ def test_cols_padded_n1_with_c_strided(gpu, n1, T):
     wide[:, 32:32 + n] = X
     Xs = wide[:, 32:32 + n]
     codes, scales, y = K.run(plan, Xs)
+    c2, s2 = K.run(plan, X, y_debug=False)
+    assert torch.equal(codes, c2) and torch.equal(scales, s2)
+    K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+@pytest.mark.parametrize("n1,n2,with_c", [(64, 112, True), (64, 80, False), (128, 144, False)])
+def test_cols_padded_n2_strided(gpu, n1, n2, with_c):
+    """n2 an odd multiple of 16: zero-padded columns of the tile (in LDS, or filled by the
+    tile DMA for n2 > 128) and of P2, whose columns of Y must neither reach the absmax nor
+    be stored; several tokens per workgroup and a row stride larger than the row."""
+    import torch
+    base = S.WORKLOADS["down_proj_n14336"] if with_c else S.WORKLOADS["hidden_n8192"]
+    wl = replace(base, n1=n1, n2=n2, n_outliers=4, pivot_channels=0)
+    T = 3 * 256 + 77
+    inp = S.make(wl, T=T)
+    plan, X = K.make_plan(inp)
+    assert plan.kernel == f"fused_mfma_bf16_cols_{n1}x{n2}{'_c' if with_c else ''}", plan.kernel
+    n = inp.wl.n
+    wide = torch.zeros((T, n + 64), dtype=torch.bfloat16, device=gpu)
+    wide[:, 32:32 + n] = X
+    codes, scales, y = K.run(plan, wide[:, 32:32 + n])
     c2, s2 = K.run(plan, X, y_debug=False)
     assert torch.equal(codes, c2) and torch.equal(scales, s2)
     K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
