@@ -514,14 +514,25 @@ __device__ __forceinline__ void store_codes8(uint8_t *codes, int64_t tok,
   }
 }
 
-template <int N1, int N2>
+// N2R: the real row length when the tile is laid out for N2 = 128 and rows hold only
+// N2R = 112 values (lane group 3 then holds 16 real and 16 padding columns; rows of codes
+// are 56 bytes, so the stores are split to 8-byte aligned halves)
+template <int N1, int N2, int N2R = N2>
 __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t tok, const uint32_t (*w)[N2 / 32],
                                             int lr, int g) {
-  uint8_t *crow = codes + tok * (int64_t)(N1 * N2 / 2);
+  static_assert(N2R == N2 || (N2 == 128 && N2R == 112), "padded stream rows: 112 of 128");
+  uint8_t *crow = codes + tok * (int64_t)(N1 * N2R / 2);
 #pragma unroll
   for (int nt = 0; nt < N1 / 16; ++nt) {
-    uint8_t *dst = crow + (nt * 16 + lr) * (N2 / 2) + g * (N2 / 8);
-    if constexpr (N2 == 128) {
+    uint8_t *dst = crow + (nt * 16 + lr) * (N2R / 2) + g * (N2 / 8);
+    if constexpr (N2R != N2) {
+      const u32x2_t v0 = {w[nt][0], w[nt][1]};
+      __builtin_nontemporal_store(v0, reinterpret_cast<u32x2_t *>(dst));
+      if (g < 3) {
+        const u32x2_t v1 = {w[nt][2], w[nt][3]};
+        __builtin_nontemporal_store(v1, reinterpret_cast<u32x2_t *>(dst + 8));
+      }
+    } else if constexpr (N2 == 128) {
       const u32x4_t v = {w[nt][0], w[nt][1], w[nt][2], w[nt][3]};
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
     } else {
@@ -531,14 +542,18 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t tok, const u
   }
 }
 
-template <int N1, int N2, bool HAS_C, bool YDBG, int BITS = 4>
+// N2R < N2: rows of X (and of Y and the codes) hold N2R values; the tile in LDS keeps the
+// N2 layout, its padding pieces meet P2's zero rows (see dma_tile) and padded columns of
+// Y are zero and not stored
+template <int N1, int N2, bool HAS_C, bool YDBG, int BITS = 4, int N2R = N2>
 __global__ __launch_bounds__(512) void kq_stream_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
     const float *__restrict__ cvec, float clip, int scale_fp16, int clip_allows_no_clamp,
     uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
   using C = StreamCfg<N1, N2, HAS_C>;
-  constexpr int n = N1 * N2;
+  static_assert(N2R == N2 || (N2 == 128 && N2R == 112 && !HAS_C && BITS == 4), "padded rows");
+  constexpr int n = N1 * N2R;
   // P2 operands, then (with c) c as 16-byte units of 4 channels: unit u of row R at
   // R * 4 N2 + ((u ^ (R % 16)) * 16), so that the 16 rows of one A-operand read hit 16
   // different bank groups
@@ -567,14 +582,17 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 #pragma unroll
     for (int j = 0; j < SWP; ++j) {
       const int R = j * C::RPI + r0;
-      voff[j] = (uint32_t)((r0 * N2 + ((pos0 ^ C::swz(R)) * 8)) * 2);
+      // rows of X hold N2R values: a padding piece (>= N2R / 8) reads the row's first
+      // piece instead, finite values that meet P2's zero rows
+      const int piece = pos0 ^ C::swz(R);
+      voff[j] = (uint32_t)((r0 * N2R + ((piece < N2R / 8 ? piece : 0) * 8)) * 2);
     }
   }
   auto dma_tile = [&](int64_t tok) {
     const unsigned char *xt = reinterpret_cast<const unsigned char *>(X + tok * ldx);
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j)  // swz(R + SWP RPI) == swz(R)
-      dma16_nt(xt + j * 1024, voff[j % SWP], lds_addr(slot + j * 1024));
+      dma16_nt(xt + j * (C::RPI * N2R * 2), voff[j % SWP], lds_addr(slot + j * 1024));
   };
 
   const int64_t stride = (int64_t)gridDim.x * C::WAVES;
@@ -607,7 +625,7 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
   TokenScale pend_s{0.f, (_Float16)0.f, 0.f};
   int64_t pend_tok = -1;
   auto store_pending = [&]() {
-    if constexpr (BITS == 4) store_codes<N1, N2>(codes, pend_tok, pend, lr, g);
+    if constexpr (BITS == 4) store_codes<N1, N2, N2R>(codes, pend_tok, pend, lr, g);
     else store_codes8<N1, N2>(codes, pend_tok, pend, lr, g);
     if (lane == 0) store_scale(scales, pend_tok, pend_s, scale_fp16);
   };
@@ -724,10 +742,11 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
     if constexpr (YDBG) {
 #pragma unroll
       for (int nt = 0; nt < C::MT; ++nt) {
-        float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + (nt * 16 + lr) * N2 + g * C::LPL);
+        float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + (nt * 16 + lr) * N2R + g * C::LPL);
 #pragma unroll
         for (int m2 = 0; m2 < C::NT; ++m2)
-          yp[m2] = make_float4(yacc[m2][nt][0], yacc[m2][nt][1], yacc[m2][nt][2], yacc[m2][nt][3]);
+          if (g * C::LPL + 4 * m2 < N2R)  // padded columns are not written
+            yp[m2] = make_float4(yacc[m2][nt][0], yacc[m2][nt][1], yacc[m2][nt][2], yacc[m2][nt][3]);
       }
     }
   }
@@ -1654,7 +1673,7 @@ hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
   return hipGetLastError();
 }
 
-template <int N1, int N2, bool HAS_C, int BITS = 4>
+template <int N1, int N2, bool HAS_C, int BITS = 4, int N2R = N2>
 hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
                          void *scales, float *y_debug, hipStream_t stream) {
   using C = StreamCfg<N1, N2, HAS_C>;
@@ -1662,8 +1681,8 @@ hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
   // the debug output has its own instantiation so that the timed kernel keeps its
   // registers; both compute Y with the same per-accumulator MFMA order
-  auto k = y_debug ? &kq_stream_kernel<N1, N2, HAS_C, true, BITS>
-                   : &kq_stream_kernel<N1, N2, HAS_C, false, BITS>;
+  auto k = y_debug ? &kq_stream_kernel<N1, N2, HAS_C, true, BITS, N2R>
+                   : &kq_stream_kernel<N1, N2, HAS_C, false, BITS, N2R>;
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
@@ -1721,6 +1740,12 @@ hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
                    &launch_stream<A, B, HC, 8>,                                        \
                    reinterpret_cast<const void *>(&kq_stream_kernel<A, B, HC, false, 8>), \
                    "fused_mfma_bf16_stream_" #A "x" #B SUF "_int8"}
+// rows of 112 values in the 128-column layout (hidden 7168 = 64 x 112)
+#define KQ_STREAM_P(A, B, BR)                                                          \
+  kq_fused_variant{A, BR, false, KQ_SPLIT_STREAM, 4, (B), StreamCfg<A, B>::THREADS,         \
+                   &launch_stream<A, B, false, 4, BR>,                                 \
+                   reinterpret_cast<const void *>(&kq_stream_kernel<A, B, false, false, 4, BR>), \
+                   "fused_mfma_bf16_stream_" #A "x" #BR}
 #define KQ_STREAM_C(A, B)                                                              \
   kq_fused_variant{A, B, true, KQ_SPLIT_STREAM, 4, (B), StreamCfg<A, B, true>::THREADS,     \
                    &launch_stream<A, B, true>,                                         \
@@ -1779,7 +1804,7 @@ const kq_fused_variant kVariants[] = {
     // n1 + n2 for 1536 (32 x 48), 5120 (64 x 80), 7168 (64 x 112) and 18432 (128 x 144)
     KQ_COLS(32, 48, false, ""),    KQ_COLS(32, 48, true, "_c"),
     KQ_COLS(64, 80, false, ""),    KQ_COLS(64, 80, true, "_c"),
-    KQ_COLS(64, 112, false, ""),   KQ_COLS(64, 112, true, "_c"),
+    KQ_STREAM_P(64, 128, 112),     KQ_COLS(64, 112, false, ""),   KQ_COLS(64, 112, true, "_c"),
     KQ_COLS(128, 144, false, ""),
     // the other splits, selectable with KQ_FLAG_SPLIT_*
     KQ_ALL1(16, 32), KQ_ALL1(32, 32), KQ_ALL(16, 64), KQ_ALL(32, 64), KQ_ALL(48, 64),

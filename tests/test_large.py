@@ -36,7 +36,8 @@ CASES = {
     "cols_c_112x128": (W["down_proj_n14336"], 0, 4, False, 0),
     "cols_c_86x128": (W["ffn_n11008"], 0, 4, False, 64),
     "cols_128x224": (W["down_proj_n28672"], 0, 4, False, 0),
-    "cols_64x112_padded_n2": (W["hidden_n7168"], 0, 4, False, 64),
+    "stream_64x112_padded_n2": (W["hidden_n7168"], 0, 4, False, 64),
+    "cols_64x112_padded_n2": (W["hidden_n7168"], B.KQ_FLAG_SPLIT_COLS, 4, False, 0),
     "cols_128x144_padded_n2": (W["ffn_n18432"], 0, 4, False, 0),
     "cols_c_112x128_int8": (W["down_proj_n14336"], 0, 8, False, 64),
     "cols_128x224_int8": (W["down_proj_n28672"], 0, 8, False, 0),

@@ -28,8 +28,9 @@ SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (3
 def _available(n1, n2, split, with_c=False):
     if n2 > 128:  # only the column kernel, without c (P2 operands read from L2)
         return split == "cols" and not with_c
-    if n2 % 32:  # n2 padded to a multiple of 32: only the column kernel
-        return split == "cols"
+    if n2 % 32:  # n2 padded to a multiple of 32: the column kernel, and 64 x 112 rows in
+        # the stream kernel's 128-column layout
+        return split == "cols" or (split == "stream" and (n1, n2, with_c) == (64, 112, False))
     if split == "deep":
         return (n1, n2, with_c) in DEEP_SHAPES
     if split == "stream":
@@ -125,3 +126,27 @@ def test_cols_padded_n2_strided(gpu, n1, n2, with_c):
     c2, s2 = K.run(plan, X, y_debug=False)
     assert torch.equal(codes, c2) and torch.equal(scales, s2)
     K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+
+
+@pytest.mark.gpu
+def test_stream_rows_of_112_values():
+    """hidden 7168 = 64 x 112 runs on the stream kernel in its 128-column layout: the tile
+    DMA fetches 14 real pieces per row (the 2 padding pieces re-read the first one and meet
+    P2's zero rows), the codes of the padded columns are not stored. Several tokens per
+    wave, a row stride larger than the row, and identity with the column kernel."""
+    import torch
+    gpu = "cuda:0"
+    inp = S.make("hidden_n7168", T=5000)
+    plan, X = K.make_plan(inp)
+    assert plan.kernel == "fused_mfma_bf16_stream_64x112" and plan.kernel_for(5000) == plan.kernel
+    assert plan.kernel_for(64) == "fused_mfma_bf16_cols_64x112"  # small batches
+    n = inp.wl.n
+    wide = torch.zeros((5000, n + 64), dtype=torch.bfloat16, device=gpu)
+    wide[:, 32:32 + n] = X
+    codes, scales, y = K.run(plan, wide[:, 32:32 + n])
+    c2, s2 = K.run(plan, X, y_debug=False)
+    assert torch.equal(codes, c2) and torch.equal(scales, s2)
+    K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
+    cols, _ = K.make_plan(inp, flags=B.KQ_FLAG_SPLIT_COLS)
+    c3, s3 = K.run(cols, X, y_debug=False)
+    assert torch.equal(codes, c3) and torch.equal(scales, s3)
