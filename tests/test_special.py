@@ -213,3 +213,30 @@ def test_small_batches_switch_to_the_pair_split(gpu):
         assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
         K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(),
                                plan.clip)
+
+
+@pytest.mark.parametrize("name,small", [("attn_n4096", "fused_mfma_bf16_cols_64x64_c"),
+                                        ("hidden_n7168", "fused_mfma_bf16_cols_64x112")])
+def test_small_batches_without_a_pair_split_use_the_column_split(gpu, name, small):
+    """Stream plans with no pair variant (with c, or rows of 112 values) switch to the
+    column split for small batches; both sides of the switch match the oracle, and the
+    same tokens give the same codes on both sides."""
+    import torch
+    inp = S.make(name, T=8)
+    plan, _ = K.make_plan(inp)
+    assert plan.kernel.startswith("fused_mfma_bf16_stream_"), plan.kernel
+    assert plan.kernel_for(8) == small and plan.kernel_for(1 << 20) == plan.kernel
+    lo, hi = 1, 1 << 20
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if plan.kernel_for(mid) == plan.kernel:
+            hi = mid
+        else:
+            lo = mid + 1
+    inp = S.make(name, T=lo)
+    plan, X = K.make_plan(inp)
+    big_codes, big_scales, y = K.run(plan, X, y_debug=True)
+    K.check_against_oracle(inp, big_codes.cpu().numpy(), K.np_scales(big_scales), y.cpu().numpy(),
+                           plan.clip)
+    c_small, s_small = K.run(plan, X[: lo - 1], y_debug=False)
+    assert torch.equal(c_small, big_codes[: lo - 1]) and torch.equal(s_small, big_scales[: lo - 1])
