@@ -1773,24 +1773,30 @@ hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
 #define KQ_ALL(A, B)                                                                   \
   KQ_ALL1(A, B), KQ_REG(A, B, 2, false, ""), KQ_REG(A, B, 2, true, "_c")
 
-// Every work split that is built. The first match for a shape is its default: the
-// register kernels where their registers fit without spilling (two waves per token
-// where n2 >= 64, which leaves room to prefetch the next token), the stream kernel for
-// 64x128 (and for 64x64 with a per-channel scale: measured on MI355X, 2048 tokens in
-// 10.1 us vs 15.5 us for two waves per token), else the column kernel. Plans of the
-// stream kernel without c switch to the pair kernel for small batches (kq_api.hip).
+// Every work split that is built. The first match for a shape is its default, chosen by
+// measurement on MI355X (T = 16384 and 65536, inputs rotated past the caches):
+// - the stream kernel (one wave per token, next token in LDS by DMA) for n1 >= 32 with
+//   n2 = 64 (with or without c) and for n2 = 128 without c: e.g. 64x64 31.8 us against
+//   49.1 us for two waves per token with the token in registers, 32x64 with c 21.0 vs
+//   44.8 us, 48x128 48.6 vs 74.6 us;
+// - one wave per token with the token in registers for n1 = 16 with n2 = 64 (12.2 us at
+//   16384 tokens, 33.3 us at 65536) and for 16..48 x 128 with c (16x128: 31.5 vs 44.5 us
+//   for the column kernel);
+// - the column kernel for 64 x 128 with c and everything larger.
+// Stream plans switch to the pair kernel (or, where there is none, the column kernel) for
+// small batches (kq_api.hip).
 const kq_fused_variant kVariants[] = {
     // defaults
     KQ_REG(16, 32, 1, false, ""),  KQ_REG(16, 32, 1, true, "_c"),
     KQ_REG(32, 32, 1, false, ""),  KQ_REG(32, 32, 1, true, "_c"),
-    KQ_REG(16, 64, 2, false, ""),  KQ_REG(16, 64, 2, true, "_c"),
-    KQ_REG(32, 64, 2, false, ""),  KQ_REG(32, 64, 2, true, "_c"),
-    KQ_REG(48, 64, 2, false, ""),  KQ_REG(48, 64, 2, true, "_c"),
-    KQ_REG(64, 64, 2, false, ""),  KQ_STREAM_C(64, 64),
-    KQ_REG(16, 128, 2, false, ""), KQ_COLS(16, 128, true, "_c"),
-    KQ_REG(32, 128, 2, false, ""), KQ_COLS(32, 128, true, "_c"),
-    KQ_REG(48, 128, 2, false, ""), KQ_COLS(48, 128, true, "_c"),
-    KQ_STREAM(64, 128), KQ_COLS(64, 128, true, "_c"),
+    KQ_REG(16, 64, 1, false, ""),  KQ_REG(16, 64, 1, true, "_c"),
+    KQ_STREAM(32, 64),             KQ_STREAM_C(32, 64),
+    KQ_STREAM(48, 64),             KQ_STREAM_C(48, 64),
+    KQ_STREAM(64, 64),             KQ_STREAM_C(64, 64),
+    KQ_STREAM(16, 128),            KQ_REG(16, 128, 1, true, "_c"),
+    KQ_STREAM(32, 128),            KQ_REG(32, 128, 1, true, "_c"),
+    KQ_STREAM(48, 128),            KQ_REG(48, 128, 1, true, "_c"),
+    KQ_STREAM(64, 128),            KQ_COLS(64, 128, true, "_c"),
     KQ_COLS(80, 128, false, ""),   KQ_COLS(80, 128, true, "_c"),
     KQ_COLS(96, 128, false, ""),   KQ_COLS(96, 128, true, "_c"),
     KQ_COLS(112, 128, false, ""),  KQ_COLS(112, 128, true, "_c"),
