@@ -1,4 +1,5 @@
-// Fused Kronecker-factored transform + per-token INT4 quantization, bf16 MFMA, gfx950.
+// Fused Kronecker-factored transform + per-token INT4 (or INT8) quantization, bf16 MFMA,
+// gfx950.
 //
 // Per token (n = n1*n2):  V = x (*c) viewed n1 x n2 row-major;  Z = V P2;  Y = P1^T Z;
 // absmax -> clip -> fp16 step -> RTN -> clamp [-8, 7] -> two nibbles per byte.
@@ -8,7 +9,7 @@
 //
 // What is kept from the page's fused design: both factors stay on chip for the kernel's
 // lifetime, the token tile never leaves the CU between the two contractions, and only
-// the packed INT4 tile (+ one scale per token) is written to HBM. What is different on
+// the packed codes (+ one scale per token) are written to HBM. What is different on
 // gfx950: the two contractions run on 16x16x32 bf16 MFMA with fp32 accumulation and
 // the intermediate Z is handed from stage 1 to stage 2 in registers (no LDS round trip):
 // the stage-1 accumulator layout (4 consecutive rows of one column per lane) is exactly
@@ -16,15 +17,17 @@
 // is absorbed by storing P1 pre-permuted in the plan. Quantization runs on the stage-2
 // accumulators with a wave reduction for the absmax.
 //
-// Two work splits:
-//  * wave kernel (n1 <= 64): one wave owns a whole token. It loads the token straight
-//    from HBM into MFMA A-operand registers (16 rows x 64 contiguous bytes per load),
-//    reads P1/P2 operands from LDS (shared, read-only, loaded once per workgroup), and
-//    never synchronizes with other waves inside the token loop.
-//  * column kernel (larger n1): a token is shared by W = n2/32 waves of a workgroup,
-//    each owning 32 output columns (a column block of Y needs only the same column block
-//    of Z, which needs all of V and 32 columns of P2). The token tile is staged in LDS
-//    (XOR-swizzled 16-byte chunks) and the absmax is combined across the W waves.
+// Work splits (each a kernel below; the plan picks one per shape, see the variant table):
+//  * register kernel: 1 or 2 waves per token, the token loaded straight from HBM into
+//    MFMA A-operand registers ("deep": one wave per SIMD, next token prefetched);
+//  * stream kernel: one wave per token, the next token brought into an LDS slot by DMA
+//    while the current one is computed (also rows of 112 values in the 128 layout);
+//  * pair kernel: two waves per token, one column half each (small batches);
+//  * rows kernel: identity left factor, one step per row of V (per-head transforms);
+//  * column kernel: a token shared by n2/32 waves of a workgroup, each owning 32 output
+//    columns, the tile staged in LDS (larger factors, n1 not a multiple of 16, n2 an odd
+//    multiple of 16, and the shapes with a per-channel scale beyond the stream kernel's).
+// The stream, pair, column and rows kernels also write INT8 codes (one byte per value).
 //
 // MFMA operand layouts used below (wave64, 16x16x32 bf16; lane L, g = L/16):
 //   A (16 x 32):  lane L holds row L%16, 8 reduction slots (g, v), v = 0..7
@@ -1277,7 +1280,7 @@ __global__ __launch_bounds__(512) void kq_rows_kernel(
 }
 
 // ------------------------------------------------------------------------------------
-// column kernel: W = n2/32 waves per token
+// column kernel: W = n2p/32 waves per token (n2p: n2 rounded up to a multiple of 32)
 // ------------------------------------------------------------------------------------
 // Waves per workgroup of the column kernel: one per 32 output columns of a token (n2p is
 // n2 rounded up to a multiple of 32); where that is fewer than four, as many whole tokens
