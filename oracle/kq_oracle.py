@@ -48,6 +48,15 @@ once here and relied on by every function below):
   R10 Element 2m goes in the low nibble of byte m, element 2m+1 in the high nibble,
       each as a 4-bit two's-complement value, in row-major Y order (index j*n2 + l).
 
+Beyond the INT4 path the module also defines, with the same conventions:
+  - INT8 codes (quantize_per_token(..., bits=8), pack_int8): divisor 127, clamp to
+    [-128, 127], one two's-complement byte per value [FQ How we know: beyond dense W4A4,
+    mixed precision at W8A8];
+  - the weight side and the consumer (weight_factors, int4_gemm): the rows of W take the
+    factors P1^-T and P2^-T so that (X P)(P^-1 W^T) = X W^T, and the INT4 x INT4 product
+    is the integer dot product times both scales [FQ Learning the affine transformation;
+    HR Technical Summary].
+
 Every function below is pinned by tests that do not re-type its formula (brute-force
 definition loops, library Kronecker products, closed forms for identity/permutation
 factors, orthogonal norm and inverse invariants, exact power-of-two cases against
