@@ -240,3 +240,44 @@ def test_small_batches_without_a_pair_split_use_the_column_split(gpu, name, smal
                            plan.clip)
     c_small, s_small = K.run(plan, X[: lo - 1], y_debug=False)
     assert torch.equal(c_small, big_codes[: lo - 1]) and torch.equal(s_small, big_scales[: lo - 1])
+
+
+# The kernels behind the padded and widened shapes, through the same edge cases: fp32
+# steps, clip 0 (every code and step zero), a token of zeros among others, and T = 0.
+EDGE_CASES = [
+    ("hidden_n7168", 4, "fused_mfma_bf16_stream_64x112"),
+    ("ffn_n11008", 4, "fused_mfma_bf16_cols_86x128_c"),
+    ("ffn_n18432", 4, "fused_mfma_bf16_cols_128x144"),
+    ("down_proj_n14336", 8, "fused_mfma_bf16_cols_112x128_c_int8"),
+    ("hidden_n8192", 8, "fused_mfma_bf16_stream_64x128_int8"),
+]
+
+
+@pytest.mark.parametrize("name,bits,kernel", EDGE_CASES)
+@pytest.mark.parametrize("case", ["fp32_scales", "clip_zero", "zero_token"])
+def test_widened_kernels_edge_cases(gpu, name, bits, kernel, case):
+    import torch
+    wl = S.WORKLOADS[name]
+    if case == "clip_zero":
+        wl = replace(wl, alpha=-math.inf)
+    T = 1100  # at or above the small-batch switch, so the named kernel runs
+    inp = S.make(wl, T=T)
+    if case == "zero_token":
+        X0 = inp.X.copy()
+        X0[[0, 517, T - 1]] = 0
+        inp.X = X0
+    X, P1, P2, c = K.device_inputs(inp)
+    sd = "fp32" if case == "fp32_scales" else inp.wl.scale_dtype
+    plan = B.Plan(P1, P2, c, inp.alpha, sd, bits=bits)
+    assert plan.kernel_for(T) == kernel, plan.kernel_for(T)
+    codes, scales, y = K.run(plan, X, y_debug=True)
+    K.check_plan_against_oracle(inp, plan, codes, scales, y)
+    s = K.np_scales(scales)
+    cn = codes.cpu().numpy()
+    if case == "clip_zero":
+        assert np.all(s == 0) and np.all(cn == 0)
+    if case == "zero_token":
+        assert np.all(s[[0, 517, T - 1]] == 0) and np.all(cn[[0, 517, T - 1]] == 0)
+    e = torch.empty((0, inp.wl.n), dtype=torch.bfloat16, device=gpu)
+    c0, s0 = plan(e)
+    assert c0.shape == (0, inp.wl.n * bits // 8) and s0.shape == (0,)
