@@ -166,3 +166,44 @@ def test_host_tensors_are_refused_before_any_call():
     with pytest.raises(ValueError):
         B._ptr(torch.zeros(4))
     assert B._ptr(None) is None and B._ptr(0x1000) == 0x1000
+
+
+C_CONSUMER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "kq.h"
+
+int main(void) {
+  int n1 = 0, n2 = 0;
+  kq_plan *plan = (kq_plan *)1;
+  if (kq_choose_factors(8192, &n1, &n2) != KQ_OK || n1 != 64 || n2 != 128) return 1;
+  if (strlen(kq_status_string(KQ_ERR_UNSUPPORTED)) == 0) return 2;
+  if (kq_version() <= 0) return 3;
+  /* rejected on the host, before any HIP call: n1 * n2 odd */
+  if (kq_create(&plan, 3, 3, KQ_BF16, KQ_FP16, (const void *)16, (const void *)16, NULL,
+                1.0f, NULL) != KQ_ERR_INVALID_ARG || plan != NULL) return 4;
+  if (kq_destroy(NULL) != KQ_OK) return 5;
+  printf("ok %d %d\n", n1, n2);
+  return 0;
+}
+"""
+
+
+def test_a_c99_program_builds_against_the_header_and_links_the_library(L, tmp_path):
+    """The boundary is usable from plain C: a C99 program including only kq.h compiles
+    with -Wall -Wextra -pedantic, links libkq.so and runs its host-only calls."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(B.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                        "-L", libdir, "-lkq", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok 64 128", (r.returncode, r.stdout, r.stderr)
