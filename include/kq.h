@@ -82,8 +82,8 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
  * two's-complement byte per value, so `codes` holds T x n bytes (row stride n). bf16 plans of the stream kernel's shapes: n2 in {64, 128} with n1 in
  * {16, 32, 48, 64}, without c, or n2 = 64 with c; of the column kernel's shapes: n2 = 128
  * with n1 in {80, 86, 96, 108, 112, 128}, with or without c, 64 x 128 with c, n1 = 128
- * with n2 in {144, 160, 192, 224, 256} without c, and 32 x 48, 64 x 80, 64 x 112 with or
- * without c; and per-row plans (KQ_FLAG_PER_ROW, one
+ * with n2 in {144, 160, 192, 224, 256} without c, and 32 x 48, 56 x 64, 64 x 80, 64 x 104,
+ * 64 x 112 with or without c; and per-row plans (KQ_FLAG_PER_ROW, one
  * step per row of n2 values) with n2 in {64, 128} (KQ_ERR_UNSUPPORTED otherwise); not with
  * KQ_FLAG_FORCE_GENERIC. */
 #define KQ_FLAG_INT8 0x800u
@@ -124,9 +124,10 @@ kq_status kq_create(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype sc
  *     n1 in {86, 108} (hidden sizes 11008 and 13824; P1 is zero-padded to whole 16-row
  *     tiles inside the plan, results are unchanged). Without c
  *     also n1 = 128 with n2 in {160, 192, 224, 256} (hidden sizes 20480 ... 32768, e.g.
- *     28672 = 128 x 224). n2 an odd multiple of 16, padded with zero columns inside the
- *     plan: 32 x 48 and 64 x 80 and 64 x 112 with or without c, 128 x 144 without c (the
- *     factors kq_choose_factors gives for 1536, 5120, 7168 and 18432).
+ *     28672 = 128 x 224). n2 not a multiple of 32, padded with zero columns inside the
+ *     plan: 32 x 48, 64 x 80, 64 x 104 and 64 x 112 with or without c, 128 x 144 without
+ *     c (the factors kq_choose_factors gives for 1536, 5120, 6656, 7168 and 18432); and
+ *     56 x 64 with or without c (3584, n1 padded).
  *   fp32 (and bf16 shapes not listed above): the generic fp32 kernel, n <= 16384.
  */
 

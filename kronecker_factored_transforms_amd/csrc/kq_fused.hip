@@ -1297,7 +1297,7 @@ constexpr int cols_min_blocks(int n1, int n2) { return cols_two(n1, n2) ? 2 : 1;
 template <int N1, int N2, bool HAS_C>
 struct ColsCfg {
   static_assert(N1 >= 16 && N1 <= 128, "n1 in [16, 128]");
-  static_assert(N2 % 16 == 0 && N2 >= 32 && N2 <= 256, "n2 must be a multiple of 16 in [32, 256]");
+  static_assert(N2 % 8 == 0 && N2 >= 32 && N2 <= 256, "n2 must be a multiple of 8 in [32, 256]");
   // n2 that is not a multiple of 32 is padded with zero columns to N2P: P2's padded rows
   // and columns are zero (in the plan's operand copy), so the padded columns of V add
   // nothing to Z and the padded columns of Y are zero; they are not stored
@@ -1809,12 +1809,15 @@ const kq_fused_variant kVariants[] = {
     // hidden sizes whose larger factor exceeds 128 (e.g. 28672 -> 128 x 224)
     KQ_COLS(128, 160, false, ""),  KQ_COLS(128, 192, false, ""),
     KQ_COLS(128, 224, false, ""),  KQ_COLS(128, 256, false, ""),
-    // n2 an odd multiple of 16, padded to a multiple of 32: the factors that minimise
-    // n1 + n2 for 1536 (32 x 48), 5120 (64 x 80), 7168 (64 x 112) and 18432 (128 x 144)
+    // n2 not a multiple of 32, padded to one: the factors that minimise n1 + n2 for 1536
+    // (32 x 48), 5120 (64 x 80), 7168 (64 x 112), 18432 (128 x 144), 6656 (64 x 104, n2 an
+    // odd multiple of 8), and 3584 (56 x 64, n1 padded)
     KQ_COLS(32, 48, false, ""),    KQ_COLS(32, 48, true, "_c"),
     KQ_COLS(64, 80, false, ""),    KQ_COLS(64, 80, true, "_c"),
     KQ_STREAM_P(64, 128, 112),     KQ_COLS(64, 112, false, ""),   KQ_COLS(64, 112, true, "_c"),
     KQ_COLS(128, 144, false, ""),
+    KQ_COLS(56, 64, false, ""),    KQ_COLS(56, 64, true, "_c"),
+    KQ_COLS(64, 104, false, ""),   KQ_COLS(64, 104, true, "_c"),
     // the other splits, selectable with KQ_FLAG_SPLIT_*
     KQ_ALL1(16, 32), KQ_ALL1(32, 32), KQ_ALL(16, 64), KQ_ALL(32, 64), KQ_ALL(48, 64),
     KQ_ALL(64, 64), KQ_ALL(16, 128), KQ_ALL(32, 128), KQ_ALL(48, 128), KQ_ALL(64, 128),

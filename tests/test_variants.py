@@ -22,12 +22,15 @@ SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (3
           (128, 160, False), (128, 224, False), (128, 256, False), (128, 224, True),
           (86, 128, False), (86, 128, True), (108, 128, False), (108, 128, True),
           (32, 48, False), (32, 48, True), (64, 80, False), (64, 80, True), (64, 112, False),
-          (64, 112, True), (128, 144, False)]
+          (64, 112, True), (128, 144, False), (56, 64, False), (56, 64, True), (64, 104, False),
+          (64, 104, True)]
 
 
 def _available(n1, n2, split, with_c=False):
     if n2 > 128:  # only the column kernel, without c (P2 operands read from L2)
         return split == "cols" and not with_c
+    if n1 % 16:  # n1 padded to whole row tiles: only the column kernel
+        return split == "cols"
     if n2 % 32:  # n2 padded to a multiple of 32: the column kernel, and 64 x 112 rows in
         # the stream kernel's 128-column layout
         return split == "cols" or (split == "stream" and (n1, n2, with_c) == (64, 112, False))
@@ -107,7 +110,8 @@ def test_cols_padded_n1_with_c_strided(gpu, n1, T):
     K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip)
 
 
-@pytest.mark.parametrize("n1,n2,with_c", [(64, 112, True), (64, 80, False), (128, 144, False)])
+@pytest.mark.parametrize("n1,n2,with_c", [(64, 112, True), (64, 80, False), (128, 144, False),
+                                          (64, 104, True), (56, 64, True)])
 def test_cols_padded_n2_strided(gpu, n1, n2, with_c):
     """n2 an odd multiple of 16: zero-padded columns of the tile (in LDS, or filled by the
     tile DMA for n2 > 128) and of P2, whose columns of Y must neither reach the absmax nor
