@@ -171,6 +171,24 @@ def test_argument_errors(gpu):
     with pytest.raises(B.KqError) as e:      # T < 0
         B.kq_transform_quant(plan.handle, X, -1, n, codes, scales)
     assert e.value.status == B.KQ_ERR_INVALID_ARG
+    # every case below is refused on the host, before anything is launched
+    cbytes = torch.empty((8 * n // 2 + 16,), dtype=torch.uint8, device=gpu)
+    sbytes = torch.empty((32,), dtype=torch.uint8, device=gpu)
+    ybuf = torch.empty((8 * n + 4,), dtype=torch.float32, device=gpu)
+    bad = [
+        ((X, 8, n + 1, codes, scales, None), B.KQ_ERR_ALIGNMENT),                    # row pitch not 16 B
+        ((X, 8, n, cbytes.data_ptr() + 1, scales, None), B.KQ_ERR_ALIGNMENT),       # codes
+        ((X, 8, n, codes, sbytes.data_ptr() + 1, None), B.KQ_ERR_ALIGNMENT),        # fp16 steps
+        ((X, 8, n, codes, scales, ybuf.data_ptr() + 4), B.KQ_ERR_ALIGNMENT),        # y_debug
+        ((X, (1 << 40) // n + 1, n, codes, scales, None), B.KQ_ERR_INVALID_ARG),    # T * n > 2^40
+        ((0, 8, n, codes, scales, None), B.KQ_ERR_INVALID_ARG),                     # null X
+        ((X, 8, n, 0, scales, None), B.KQ_ERR_INVALID_ARG),                         # null codes
+    ]
+    for args, status in bad:
+        with pytest.raises(B.KqError) as e:
+            B.kq_transform_quant(plan.handle, *args)
+        assert e.value.status == status, args[1:3]
+    B.kq_transform_quant(plan.handle, 0, 0, n, 0, 0)  # T = 0: nothing to do, no pointer read
     with pytest.raises(B.KqError) as e:
         B.Plan(K.torch_from(inp.P1, "bf16").to(gpu), K.torch_from(inp.P2, "bf16").to(gpu),
                alpha=float("nan"))
