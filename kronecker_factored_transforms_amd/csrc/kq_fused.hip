@@ -501,7 +501,10 @@ __device__ __forceinline__ void quant_tile8(const f32x4 (&yacc)[NT][MT], float i
       w[nt][m2] = quant4x8(yacc[m2][nt][0], yacc[m2][nt][1], yacc[m2][nt][2], yacc[m2][nt][3], inv);
 }
 
-// INT8 code rows: lane stores 4 NT bytes (its LPL consecutive columns) of row 16 nt + lr
+// INT8 code rows: lane stores 4 NT bytes (its LPL consecutive columns) of row 16 nt + lr.
+// Each store instruction fills half of every 32-byte piece of a row and the next one the
+// other half; plain stores let L2 merge the halves before they go to HBM (non-temporal
+// stores wrote 14 % more bytes than the codes hold).
 template <int N1, int N2>
 __device__ __forceinline__ void store_codes8(uint8_t *codes, int64_t tok,
                                              const uint32_t (*w)[N2 / 16], int lr, int g) {
@@ -512,7 +515,7 @@ __device__ __forceinline__ void store_codes8(uint8_t *codes, int64_t tok,
 #pragma unroll
     for (int q = 0; q < N2 / 64; ++q) {
       const u32x4_t v = {w[nt][4 * q], w[nt][4 * q + 1], w[nt][4 * q + 2], w[nt][4 * q + 3]};
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst + 16 * q));
+      *reinterpret_cast<u32x4_t *>(dst + 16 * q) = v;
     }
   }
 }
