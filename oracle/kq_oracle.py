@@ -44,7 +44,10 @@ once here and relied on by every function below):
       fp32); codes are computed with the *stored* scale: inv = fp32(1 / s),
       q = clamp(rint(fp32(y * inv)), -8, 7). Every step is one IEEE-rounded fp32 op.
   R9  A token whose stored scale is 0 (all-zero token, clip 0, or underflow) gets all
-      codes 0. Non-finite inputs are outside the contract.
+      codes 0. A stored fp32 step so small that fp32(1 / s) overflows (s <= 2^-128) is an
+      underflow too: it is stored as 0 and its codes are 0 (an fp16 step never reaches
+      that range: its smallest nonzero value is 2^-24). Non-finite inputs are outside the
+      contract.
   R10 Element 2m goes in the low nibble of byte m, element 2m+1 in the high nibble,
       each as a 4-bit two's-complement value, in row-major Y order (index j*n2 + l).
 
@@ -259,7 +262,7 @@ def quantize_per_token(Y32, clip, scale_dtype: str = "fp16", bits: int = 4):
         a   = max_k |y_k|                          (exact)
         s32 = fp32( fp32(clip * a) / M )
         s   = fp16_rne(s32)   (or s32 when scale_dtype == "fp32")
-        s == 0 -> all codes 0
+        s == 0, or fp32(1 / s) not finite (then s is stored as 0) -> all codes 0
         inv = fp32(1 / s);  q = clamp(rint(fp32(y * inv)), -M - 1, M)
     Returns (q int8 [T, n], scales float16|float32 [T]).
     """
@@ -287,6 +290,12 @@ def quantize_per_token(Y32, clip, scale_dtype: str = "fp16", bits: int = 4):
         s_f = s_store.astype(np.float32)
         zero = s_f == np.float32(0.0)
         inv = (np.float32(1.0) / np.where(zero, np.float32(1.0), s_f)).astype(np.float32)
+        # reading R9: a step whose reciprocal overflows fp32 counts as underflowed
+        tiny = ~np.isfinite(inv)
+        if tiny.any():
+            s_store = np.where(tiny, np.zeros_like(s_store), s_store)
+            zero = zero | tiny
+            inv = np.where(tiny, np.float32(0.0), inv).astype(np.float32)
         v = (y * inv[:, None]).astype(np.float32)
         q = np.rint(v)
         q = np.clip(q, -M - 1, M)

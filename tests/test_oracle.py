@@ -291,6 +291,28 @@ def test_zero_and_degenerate_tokens():
     assert np.all(s == 0) and np.all(q == 0)
 
 
+def test_fp32_step_whose_reciprocal_overflows_is_an_underflow():
+    """Reading R9: with fp32 steps, a token whose step s = fp32(a / 7) is at most 2^-128
+    (fp32(1 / s) = inf) is stored with step 0 and all-zero codes, like a zero token; a step
+    just above that range still quantizes normally and keeps the half-step error bound."""
+    y = np.zeros((4, 8), np.float32)
+    y[0, :3] = [1e-38, 3e-39, 0.0]                                # s32 = 1.43e-39
+    y[1, :2] = [7 * np.float32(2.0 ** -128), np.float32(2.0 ** -128)]  # s32 = 2^-128
+    y[2, :2] = [7 * np.float32(2.0 ** -127), -np.float32(2.0 ** -126)]  # s32 = 2^-127
+    y[3, :2] = [np.float32(2.0 ** -120), -np.float32(2.0 ** -121)]      # s32 ~ 1.1e-37
+    q, s = O.quantize_per_token(y, 1.0, "fp32")
+    for t in (0, 1):
+        assert s[t] == 0 and np.all(q[t] == 0)
+    assert s[2] == np.float32(2.0 ** -127) and q[2, 0] == 7 and q[2, 1] == -2
+    assert s[3] > 0 and q[3, 0] == 7 and q[3, 1] in (-3, -4)
+    for t in (2, 3):
+        err = np.abs(y[t].astype(np.float64) - q[t] * np.float64(s[t]))
+        assert np.all(err <= np.float64(s[t]) / 2)
+    # fp16 steps never reach that range: the same tokens give step 0 by fp16 underflow
+    q16, s16 = O.quantize_per_token(y, 1.0, "fp16")
+    assert np.all(s16 == 0) and np.all(q16 == 0)
+
+
 def test_pack_nibble_order_and_roundtrip():
     assert O.pack_int4(np.array([[1, -1]])).tolist() == [[0xF1]]
     assert O.pack_int4(np.array([[-8, 7]])).tolist() == [[0x78]]
