@@ -38,11 +38,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# every source that decides what a launch reads and writes: the kernels, the device helpers
+# (DMA and its cache policy), and the host code that picks the kernel and sizes its grid
+KERNEL_SOURCES = ("kq_api.hip", "kq_internal.h", "kq_device.h", "kq_fused.hip", "kq_generic.hip",
+                  "kq_large.hip")
+
+
 def kernel_source_sha256() -> str:
     h = hashlib.sha256()
-    for f in ("kq_fused.hip", "kq_generic.hip"):
-        with open(os.path.join(ROOT, "kronecker_factored_transforms_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in KERNEL_SOURCES:
+        path = os.path.join(ROOT, "kronecker_factored_transforms_amd", "csrc", f)
+        if os.path.exists(path):
+            with open(path, "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
@@ -172,6 +180,182 @@ def bench_int4_gemm(args, torch, B, dev):
     }), flush=True)
 
 
+# Workloads timed beside the headline in the default run: the other gated and reported
+# configurations (the 65536-token prefill carries the second 60 % gate; the with-c
+# down-projection and attention inputs; the 64-token decode batch, eager and replayed from a
+# HIP graph).
+EXTRA_WORKLOADS = ("prefill_n8192_t65536", "down_proj_n14336", "attn_n4096", "decode_n8192_t64")
+GRAPH_CALLS = 100  # calls captured per graph for the decode timing
+
+
+def measure(torch, B, S, dev, name, args, tokens=None, split_flags=0, bits=4, min_warm_ms=0.0,
+            graph=False, keep_inputs=False):
+    """Time one workload: `args.warmup` untimed steps (more, up to `min_warm_ms` of GPU time,
+    when asked), then exactly `args.steps` steps bracketed by device synchronizations; the
+    kernel's average duration is the HIP event span on the launch stream over those steps."""
+    import numpy as np
+
+    wl = S.WORKLOADS[name]
+    t_gen = time.perf_counter()
+    inp = S.make(wl, T=tokens)
+    if tokens is not None:
+        wl = S.with_tokens(wl, tokens)
+    log(f"[bench] generated {wl.name}: T={wl.T} n={wl.n} ({wl.n1}x{wl.n2}) {wl.dtype} "
+        f"in {time.perf_counter() - t_gen:.1f}s")
+
+    def dev_tensor(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    sha = {k: (hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest() if v is not None
+               else None) for k, v in (("X", inp.X), ("P1", inp.P1), ("P2", inp.P2), ("c", inp.c))}
+    X0 = dev_tensor(inp.X)
+    c = torch.from_numpy(inp.c).to(dev) if inp.c is not None else None
+    if wl.per_row:  # identity left factor, one step per row of V
+        plan = B.Plan(None, dev_tensor(inp.P2), None, inp.alpha, wl.scale_dtype, flags=split_flags,
+                      n1=wl.n1, bits=bits)
+    else:
+        plan = B.Plan(dev_tensor(inp.P1), dev_tensor(inp.P2), c, inp.alpha, wl.scale_dtype,
+                      flags=split_flags, bits=bits)
+    T, n = wl.T, wl.n
+    nscales = T * wl.n1 if wl.per_row else T
+    esize = 2 if wl.dtype == "bf16" else 4
+    code_bytes = n * bits // 8  # per token
+    ws_bytes = plan.workspace_bytes(T)
+    set_bytes = T * n * esize + T * code_bytes + nscales * 2
+    nsets = max(2, math.ceil(args.rotate_mib * 2 ** 20 / set_bytes))
+    Xs = [X0] + [X0.clone() for _ in range(nsets - 1)]
+    outs = [(torch.empty((T, code_bytes), dtype=torch.uint8, device=dev),
+             torch.empty((nscales,), dtype=plan.scale_dtype, device=dev)) for _ in range(nsets)]
+    # the intermediate of the two-kernel designs for large factors: allocated once, outside
+    # the timed region (the library itself never allocates in a call)
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
+    stream = torch.cuda.current_stream()
+    handle, sh = plan.handle, int(stream.cuda_stream)
+    kname = plan.kernel_for(T)
+    log(f"[bench] {wl.name}: kernel={kname} clip={plan.clip:.6f} buffer sets={nsets} "
+        f"({nsets * set_bytes / 2**20:.0f} MiB)" + (f", workspace {ws_bytes / 2**20:.1f} MiB" if ws_bytes else ""))
+
+    def step(i, sh=sh):
+        X = Xs[i % nsets]
+        codes, scales = outs[i % nsets]
+        B.kq_transform_quant_ws(handle, X, T, n, codes, scales, None, ws, ws_bytes, sh)
+
+    K = args.steps
+    # events are created before the warmup: creating them between the warmup and the
+    # timed region would leave the GPU idle for milliseconds, and the launches right
+    # after such a pause run measurably slower while the clocks ramp back up
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K if args.per_launch_events else 0)]
+    span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    w0 = torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    nwarm = 0
+    for _ in range(args.warmup):
+        step(nwarm)
+        nwarm += 1
+    span[0].record(stream)
+    torch.cuda.synchronize()
+    while min_warm_ms > 0 and w0.elapsed_time(span[0]) < min_warm_ms:
+        for _ in range(16):
+            step(nwarm)
+            nwarm += 1
+        span[0].record(stream)
+        torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, bracketed by synchronizations (the throughput)
+    t0 = time.perf_counter()
+    span[0].record(stream)
+    for i in range(K):
+        step(i)
+    span[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    gpu_span_ms = span[0].elapsed_time(span[1]) / K
+    k_avg_s = gpu_span_ms / 1e3
+    per_launch = None
+    if args.per_launch_events:
+        # diagnostic only: an event pair around every launch; the event packets add a few
+        # microseconds to each measured interval and space the launches apart
+        for i in range(K):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        kernel_ms = sorted(a.elapsed_time(b) for a, b in ev)
+        per_launch = {"mean_us": sum(kernel_ms) / K * 1e3, "median_us": kernel_ms[K // 2] * 1e3,
+                      "p10_us": kernel_ms[K // 10] * 1e3, "p90_us": kernel_ms[(9 * K) // 10] * 1e3,
+                      "min_us": kernel_ms[0] * 1e3, "max_us": kernel_ms[-1] * 1e3}
+    graph_us = None
+    if graph:
+        # the same calls captured once in a HIP graph and replayed: no host enqueue cost per
+        # call (what a serving loop that captures its decode step sees)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                csh = int(torch.cuda.current_stream().cuda_stream)
+                for i in range(GRAPH_CALLS):
+                    step(i, csh)
+        torch.cuda.synchronize()
+        reps = max(4, K // GRAPH_CALLS + 1)
+        for _ in range(2):
+            g.replay()
+        gs = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        torch.cuda.synchronize()
+        gs[0].record(stream)
+        for _ in range(reps):
+            g.replay()
+        gs[1].record(stream)
+        torch.cuda.synchronize()
+        graph_us = gs[0].elapsed_time(gs[1]) * 1e3 / (reps * GRAPH_CALLS)
+        del g
+
+    flop_tok = 2 * n * (wl.n1 + wl.n2)
+    byte_tok = esize * n + code_bytes
+    tokens_per_s = T / (ms_per_step / 1e3)
+    achieved_gbs = T * byte_tok / k_avg_s / 1e9
+    achieved_tflops = T * flop_tok / k_avg_s / 1e12
+    traffic = traffic_from_profile(wl.name, kname)
+    log(f"[bench] {wl.name}: {K} steps: {ms_per_step * 1e3:.2f} us/step wall, {gpu_span_ms * 1e3:.2f} "
+        f"us/launch on the stream: {achieved_gbs:.0f} GB/s ({achieved_gbs / PEAK_HBM_GBS:.3f} of HBM), "
+        f"{achieved_tflops:.1f} TFLOP/s" + (f"; graph replay {graph_us:.2f} us/call" if graph else "")
+        + (f"; per-launch events: {per_launch}" if per_launch else ""))
+    res = {
+        "workload": wl.name, "T": T, "n": n, "n1": wl.n1, "n2": wl.n2, "x_dtype": wl.dtype,
+        "scale_dtype": wl.scale_dtype, "per_channel_c": inp.c is not None, "alpha": inp.alpha,
+        "kernel": kname, "buffer_sets": nsets, "scales_per_token": wl.n1 if wl.per_row else 1,
+        "code_bits": bits, "workspace_bytes": ws_bytes, "warmup_steps_run": nwarm,
+        "tokens_per_s": tokens_per_s, "ms_per_step": ms_per_step,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic,
+            "kernel_avg_us": k_avg_s * 1e6,
+            "kernel_avg_source": "HIP event span of the timed region on the launch stream / steps",
+            "algorithmic_bytes_per_launch": T * byte_tok,
+        },
+        "mfma": {"achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": achieved_tflops / PEAK_BF16_TFLOPS,
+                 "algorithmic_flop_per_launch": T * flop_tok},
+        "inputs_sha256": sha,
+    }
+    if graph_us is not None:
+        res["graph_replay_us_per_call"] = graph_us
+        res["eager_us_per_call"] = ms_per_step * 1e3
+    if per_launch:
+        res["per_launch_events_us"] = per_launch
+    plan.close()
+    if not keep_inputs:
+        del Xs, outs, X0, ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        inp = None
+    return res, inp
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,10 +368,15 @@ def main():
                     help="minimum total size of the rotated input+output buffer sets")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--split", choices=["default", "reg1", "reg2", "cols", "deep", "stream", "pair", "generic"],
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --workload (the default run also times " + ", ".join(EXTRA_WORKLOADS) + ")")
+    ap.add_argument("--split", choices=["default", "reg1", "reg2", "cols", "deep", "stream", "pair",
+                                        "generic", "twostage", "ptile"],
                     default="default", help="work split of the fused kernel (default: the plan's)")
     ap.add_argument("--per-launch-events", action="store_true",
                     help="also time every launch with its own event pair (diagnostic)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also replay the calls from a captured HIP graph (per-call time)")
     ap.add_argument("--bits", type=int, choices=[4, 8], default=4,
                     help="code width: 4 (packed nibbles, the default) or 8 (one byte per value)")
     ap.add_argument("--int4-gemm", type=int, nargs=3, metavar=("T", "N", "K"), default=None,
@@ -204,7 +393,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from kronecker_factored_transforms_amd import binding as B
@@ -217,48 +405,11 @@ def main():
     if args.int4_gemm:
         bench_int4_gemm(args, torch, B, dev)
         return
-    wl = S.WORKLOADS[args.workload]
-    t_gen = time.perf_counter()
-    inp = S.make(wl, T=args.tokens)
-    if args.tokens is not None:
-        wl = S.with_tokens(wl, args.tokens)
-    log(f"[bench] generated {wl.name}: T={wl.T} n={wl.n} ({wl.n1}x{wl.n2}) {wl.dtype} "
-        f"in {time.perf_counter() - t_gen:.1f}s")
-
-    def dev_tensor(a):
-        if wl.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
-
-    # fingerprints of the synthetic inputs, so that runs can be matched to the same data
-    sha = {k: (hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest() if v is not None
-               else None) for k, v in (("X", inp.X), ("P1", inp.P1), ("P2", inp.P2), ("c", inp.c))}
-    X0 = dev_tensor(inp.X)
-    c = torch.from_numpy(inp.c).to(dev) if inp.c is not None else None
     flags = {"default": 0, "reg1": B.KQ_FLAG_SPLIT_REG1, "reg2": B.KQ_FLAG_SPLIT_REG2,
              "cols": B.KQ_FLAG_SPLIT_COLS, "deep": B.KQ_FLAG_SPLIT_DEEP,
              "stream": B.KQ_FLAG_SPLIT_STREAM, "pair": B.KQ_FLAG_SPLIT_PAIR,
-             "generic": B.KQ_FLAG_FORCE_GENERIC}[args.split]
-    if wl.per_row:  # identity left factor, one step per row of V
-        plan = B.Plan(None, dev_tensor(inp.P2), None, inp.alpha, wl.scale_dtype, flags=flags,
-                      n1=wl.n1, bits=args.bits)
-    else:
-        plan = B.Plan(dev_tensor(inp.P1), dev_tensor(inp.P2), c, inp.alpha, wl.scale_dtype,
-                      flags=flags, bits=args.bits)
-    T, n = wl.T, wl.n
-    nscales = T * wl.n1 if wl.per_row else T
-    esize = 2 if wl.dtype == "bf16" else 4
-    code_bytes = n * args.bits // 8  # per token
-    set_bytes = T * n * esize + T * code_bytes + nscales * 2
-    nsets = max(2, math.ceil(args.rotate_mib * 2 ** 20 / set_bytes))
-    Xs = [X0] + [X0.clone() for _ in range(nsets - 1)]
-    outs = [(torch.empty((T, code_bytes), dtype=torch.uint8, device=dev),
-             torch.empty((nscales,), dtype=plan.scale_dtype, device=dev)) for _ in range(nsets)]
-    stream = torch.cuda.current_stream()
-    handle, sh = plan.handle, int(stream.cuda_stream)
-    kname = plan.kernel_for(T)
-    log(f"[bench] kernel={kname} clip={plan.clip:.6f} buffer sets={nsets} "
-        f"({nsets * set_bytes / 2**20:.0f} MiB)")
+             "generic": B.KQ_FLAG_FORCE_GENERIC, "twostage": B.KQ_FLAG_SPLIT_TWOSTAGE,
+             "ptile": B.KQ_FLAG_SPLIT_PTILE}[args.split]
 
     if args.copy_probe:
         a = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
@@ -266,108 +417,56 @@ def main():
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
         log("[bench] copy probe: 3 x 512 MiB device-to-device copies")
 
-    def step(i):
-        X = Xs[i % nsets]
-        codes, scales = outs[i % nsets]
-        B.kq_transform_quant(handle, X, T, n, codes, scales, None, sh)
+    head, inp = measure(torch, B, S, dev, args.workload, args, tokens=args.tokens,
+                        split_flags=flags, bits=args.bits, graph=args.graph, keep_inputs=True)
 
-    K = args.steps
-    # events are created before the warmup: creating them between the warmup and the
-    # timed region would leave the GPU idle for milliseconds, and the launches right
-    # after such a pause run measurably slower while the clocks ramp back up
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K if args.per_launch_events else 0)]
-    span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region 1: K back-to-back steps, bracketed by synchronizations (the throughput)
-    t0 = time.perf_counter()
-    span[0].record(stream)
-    for i in range(K):
-        step(i)
-    span[1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    gpu_span_ms = span[0].elapsed_time(span[1]) / K
-    # average launch duration: the HIP event span of the timed region on the launch stream
-    # over K back-to-back launches (each launch waits for the previous one)
-    k_avg_s = gpu_span_ms / 1e3
-    per_launch = None
-    if args.per_launch_events:
-        # diagnostic only: an event pair around every launch; the event packets add a few
-        # microseconds to each measured interval and space the launches apart
-        for i in range(K):
-            ev[i][0].record(stream)
-            step(i)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        kernel_ms = sorted(a.elapsed_time(b) for a, b in ev)
-        per_launch = {"mean_us": sum(kernel_ms) / K * 1e3, "median_us": kernel_ms[K // 2] * 1e3,
-                      "p10_us": kernel_ms[K // 10] * 1e3, "p90_us": kernel_ms[(9 * K) // 10] * 1e3,
-                      "min_us": kernel_ms[0] * 1e3, "max_us": kernel_ms[-1] * 1e3}
-
-    flop_tok = 2 * n * (wl.n1 + wl.n2)
-    byte_tok = esize * n + code_bytes
-    tokens_per_s = T / (ms_per_step / 1e3)
-    achieved_gbs = T * byte_tok / k_avg_s / 1e9
-    achieved_tflops = T * flop_tok / k_avg_s / 1e12
-    traffic = traffic_from_profile(wl.name, kname)
-    log(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step wall, {gpu_span_ms * 1e3:.2f} us/launch "
-        f"on the stream: {achieved_gbs:.0f} GB/s, {achieved_tflops:.1f} TFLOP/s"
-        + (f"; per-launch events: {per_launch}" if per_launch else ""))
+    extras = {}
+    run_extra = (not args.no_extra and args.workload == "hidden_n8192" and args.tokens is None
+                 and args.split == "default" and args.bits == 4)
+    if run_extra:
+        for name in EXTRA_WORKLOADS:
+            # these follow a pause for input generation: warm the clocks for at least 20 ms of
+            # launches (beyond the --warmup steps) before their timed region
+            extras[name], _ = measure(torch, B, S, dev, name, args, min_warm_ms=20.0,
+                                      graph=name.startswith("decode"))
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds, args.bits)
         log(f"[bench] cpu oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} cores")
 
+    cfg = {k: head[k] for k in ("workload", "T", "n", "n1", "n2", "x_dtype", "scale_dtype",
+                                "per_channel_c", "alpha", "kernel", "buffer_sets",
+                                "scales_per_token", "code_bits")}
     out = {
         "metric": "tokens/s + % of roofline (HBM GB/s or MFMA TFLOP/s), n=8192 64x128 transform+INT4",
-        "value": tokens_per_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": head["x_dtype"],
         "data": "synthetic",
-        "config": {
-            "workload": wl.name, "T": T, "n": n, "n1": wl.n1, "n2": wl.n2, "x_dtype": wl.dtype,
-            "scale_dtype": wl.scale_dtype, "per_channel_c": inp.c is not None,
-            "alpha": inp.alpha, "kernel": kname, "buffer_sets": nsets,
-            "scales_per_token": wl.n1 if wl.per_row else 1, "code_bits": args.bits,
-        },
-        "inputs_sha256": sha,
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved_gbs,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": achieved_gbs / PEAK_HBM_GBS,
-            "traffic": traffic,
-            "kernel_avg_us": k_avg_s * 1e6,
-            "kernel_avg_source": "HIP event span of the timed region on the launch stream / steps",
-            "algorithmic_bytes_per_launch": T * byte_tok,
-        },
-        "mfma": {
-            "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved_tflops / PEAK_BF16_TFLOPS,
-            "algorithmic_flop_per_launch": T * flop_tok,
-        },
+        "config": cfg,
+        "inputs_sha256": head["inputs_sha256"],
+        "roofline": head["roofline"],
+        "mfma": head["mfma"],
         "cpu_baseline": cpu,
     }
-    if per_launch:  # diagnostic: an event pair around every launch (adds a few us each)
-        out["per_launch_events_us"] = per_launch
+    if "per_launch_events_us" in head:
+        out["per_launch_events_us"] = head["per_launch_events_us"]
+    if "graph_replay_us_per_call" in head:
+        out["graph_replay_us_per_call"] = head["graph_replay_us_per_call"]
+    if extras:
+        out["configs"] = extras
     print(json.dumps(out), flush=True)
-    plan.close()
 
 
 if __name__ == "__main__":

@@ -32,6 +32,7 @@
 #ifndef KQ_H
 #define KQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -46,7 +47,9 @@ typedef enum kq_status {
   KQ_ERR_UNSUPPORTED = 2,   /* valid, but this build has no kernel for it     */
   KQ_ERR_ALIGNMENT = 3,     /* a pointer or leading dimension is misaligned   */
   KQ_ERR_OUT_OF_MEMORY = 4, /* host or device allocation failed (kq_create)   */
-  KQ_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed      */
+  KQ_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed      */
+  KQ_ERR_WORKSPACE = 6      /* the call needs a device workspace larger than   */
+                            /* the one given (see kq_workspace_size)           */
 } kq_status;
 
 typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
@@ -65,6 +68,18 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
 #define KQ_FLAG_SPLIT_PAIR 0x200u   /* MFMA: two waves per token (one column half each),  */
                                     /* operands in registers, tokens double-buffered in   */
                                     /* LDS by DMA (no per-channel scale)                  */
+/* The two designs for factors too large for one CU's on-chip memory ("FlatQuant" page,
+ * Deep Dive: The fused kernel, Figure 8(b) and 8(c); Where It Breaks: on-chip memory
+ * overflow). Both pass an intermediate through a device workspace that the caller gives
+ * to kq_transform_quant_ws (kq_workspace_size says how large). */
+#define KQ_FLAG_SPLIT_TWOSTAGE 0x1000u /* Figure 8(c): stage 1 (x c) P2 writes Z (bf16) to    */
+                                       /* the workspace; stage 2 P1^T Z + quantization      */
+                                       /* reads it back                                     */
+#define KQ_FLAG_SPLIT_PTILE 0x2000u    /* Figure 8(b): Z stays on chip, P1 is applied one    */
+                                       /* tile of its output (non-reduction) dimension at a */
+                                       /* time, each tile of Y goes to the workspace (fp32) */
+                                       /* with the token's absmax, and a second kernel      */
+                                       /* quantizes it                                      */
 
 /* KQ_FLAG_PER_ROW: the left factor is the identity (pass P1 = NULL) and every row of V
  * (n2 values, e.g. one attention head of a token) gets its own step, so `scales` holds
@@ -159,6 +174,30 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
  */
 kq_status kq_transform_quant(const kq_plan *plan, const void *X, int64_t T, int64_t ldx,
                              uint8_t *codes, void *scales, float *y_debug, void *stream);
+
+/*
+ * kq_workspace_size -- device workspace (bytes) that a call of T tokens on `plan` needs:
+ * 0 for the single-kernel designs; for the two-kernel designs (KQ_FLAG_SPLIT_TWOSTAGE,
+ * KQ_FLAG_SPLIT_PTILE, and the plans of large factors that default to one of them) the
+ * intermediate the two kernels pass through global memory. Writes *bytes. Errors:
+ * INVALID_ARG (NULL plan or bytes, T < 0, T beyond 2^40 / n).
+ */
+kq_status kq_workspace_size(const kq_plan *plan, int64_t T, size_t *bytes);
+
+/*
+ * kq_transform_quant_ws -- kq_transform_quant with a caller-owned device workspace.
+ *   workspace        device, at least kq_workspace_size(plan, T) bytes, 256-byte aligned;
+ *                    may be NULL (with workspace_bytes 0) when that size is 0. Its contents
+ *                    on entry do not matter; the call overwrites them. Calls that share a
+ *                    workspace must be ordered (same stream), or they race on it.
+ *   workspace_bytes  its size in bytes.
+ * Everything else as kq_transform_quant, which is this call with (NULL, 0).
+ * Errors: as kq_transform_quant, plus WORKSPACE (workspace missing or smaller than
+ * needed) and ALIGNMENT (workspace not 256-byte aligned).
+ */
+kq_status kq_transform_quant_ws(const kq_plan *plan, const void *X, int64_t T, int64_t ldx,
+                                uint8_t *codes, void *scales, float *y_debug, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * kq_int4_gemm -- the INT4 x INT4 consumer of two kq_transform_quant outputs, on the int8

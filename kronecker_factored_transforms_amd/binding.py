@@ -13,7 +13,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkq.so")
 
-KQ_OK, KQ_ERR_INVALID_ARG, KQ_ERR_UNSUPPORTED, KQ_ERR_ALIGNMENT, KQ_ERR_OUT_OF_MEMORY, KQ_ERR_HIP = range(6)
+(KQ_OK, KQ_ERR_INVALID_ARG, KQ_ERR_UNSUPPORTED, KQ_ERR_ALIGNMENT, KQ_ERR_OUT_OF_MEMORY, KQ_ERR_HIP,
+ KQ_ERR_WORKSPACE) = range(7)
 KQ_BF16, KQ_FP32, KQ_FP16 = 0, 1, 2
 KQ_FLAG_FORCE_GENERIC = 0x1
 KQ_FLAG_SPLIT_REG1 = 0x10
@@ -24,12 +25,14 @@ KQ_FLAG_SPLIT_STREAM = 0x100
 KQ_FLAG_SPLIT_PAIR = 0x200
 KQ_FLAG_PER_ROW = 0x400
 KQ_FLAG_INT8 = 0x800
+KQ_FLAG_SPLIT_TWOSTAGE = 0x1000
+KQ_FLAG_SPLIT_PTILE = 0x2000
 
 # every symbol declared in include/kq.h
 EXPORTS = (
     "kq_choose_factors", "kq_create", "kq_create_ex", "kq_transform_quant", "kq_destroy",
     "kq_plan_clip_ratio", "kq_plan_kernel_name", "kq_plan_kernel_name_for", "kq_status_string",
-    "kq_version", "kq_int4_gemm",
+    "kq_version", "kq_int4_gemm", "kq_workspace_size", "kq_transform_quant_ws",
 )
 
 _lib = None
@@ -59,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.kq_create_ex.restype = i32
     L.kq_transform_quant.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
     L.kq_transform_quant.restype = i32
+    L.kq_transform_quant_ws.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.kq_transform_quant_ws.restype = i32
+    L.kq_workspace_size.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_size_t)]
+    L.kq_workspace_size.restype = i32
     L.kq_destroy.argtypes = [vp]
     L.kq_destroy.restype = i32
     L.kq_plan_clip_ratio.argtypes = [vp]
@@ -140,6 +147,20 @@ def kq_transform_quant(plan, X, T, ldx, codes, scales, y_debug=None, stream=None
     st = lib().kq_transform_quant(plan, _ptr(X), int(T), int(ldx), _ptr(codes), _ptr(scales),
                                   _ptr(y_debug), _stream(stream))
     _check(st, "kq_transform_quant")
+
+
+def kq_transform_quant_ws(plan, X, T, ldx, codes, scales, y_debug, workspace, workspace_bytes,
+                          stream=None) -> None:
+    st = lib().kq_transform_quant_ws(plan, _ptr(X), int(T), int(ldx), _ptr(codes), _ptr(scales),
+                                     _ptr(y_debug), _ptr(workspace), int(workspace_bytes),
+                                     _stream(stream))
+    _check(st, "kq_transform_quant_ws")
+
+
+def kq_workspace_size(plan, T: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().kq_workspace_size(plan, int(T), ctypes.byref(b)), "kq_workspace_size")
+    return int(b.value)
 
 
 def kq_destroy(plan) -> None:
@@ -225,19 +246,43 @@ class Plan:
         self.clip = kq_plan_clip_ratio(self.handle)
         self.kernel = kq_plan_kernel_name(self.handle)
 
-    def __call__(self, X, y_debug=False, out=None, stream=None):
+    def workspace_bytes(self, T: int) -> int:
+        """Device workspace a call of T tokens needs (0 for the single-kernel designs)."""
+        return kq_workspace_size(self.handle, T)
+
+    def __call__(self, X, y_debug=False, out=None, stream=None, workspace=None):
+        """workspace: a uint8 device tensor of at least workspace_bytes(T) bytes for the
+        two-kernel designs; allocated here with torch when not given."""
         import torch
         if X.dtype != self.x_dtype or X.dim() != 2 or X.shape[1] != self.n or X.stride(1) != 1:
             raise ValueError("X must be [T, n] of the plan's dtype with unit column stride")
         T = X.shape[0]
+        code_shape = (T, self.n * self.bits // 8)
+        scale_shape = (T, self.n1) if self.per_row else (T,)
         if out is None:
-            codes = torch.empty((T, self.n * self.bits // 8), dtype=torch.uint8, device=X.device)
-            scales = torch.empty((T, self.n1) if self.per_row else (T,), dtype=self.scale_dtype,
-                                 device=X.device)
+            codes = torch.empty(code_shape, dtype=torch.uint8, device=X.device)
+            scales = torch.empty(scale_shape, dtype=self.scale_dtype, device=X.device)
         else:
             codes, scales = out
+            # the C ABI cannot see buffer sizes: a short buffer here would be written past
+            # its end by the kernels
+            if (codes.dtype != torch.uint8 or tuple(codes.shape) != code_shape
+                    or not codes.is_contiguous() or codes.device != X.device):
+                raise ValueError(f"codes must be a contiguous uint8 tensor of shape {code_shape} "
+                                 f"on {X.device}")
+            if (scales.dtype != self.scale_dtype or tuple(scales.shape) != scale_shape
+                    or not scales.is_contiguous() or scales.device != X.device):
+                raise ValueError(f"scales must be a contiguous {self.scale_dtype} tensor of shape "
+                                 f"{scale_shape} on {X.device}")
         y = torch.empty((T, self.n), dtype=torch.float32, device=X.device) if y_debug else None
-        kq_transform_quant(self.handle, X, T, X.stride(0) if T else self.n, codes, scales, y, stream)
+        need = self.workspace_bytes(T) if T else 0
+        if need and workspace is None:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=X.device)
+        if workspace is not None and (workspace.dtype != torch.uint8 or workspace.numel() < need
+                                      or workspace.device != X.device):
+            raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes on {X.device}")
+        kq_transform_quant_ws(self.handle, X, T, X.stride(0) if T else self.n, codes, scales, y,
+                              workspace, workspace.numel() if workspace is not None else 0, stream)
         return (codes, scales, y) if y_debug else (codes, scales)
 
     def kernel_for(self, T: int) -> str:

@@ -68,7 +68,7 @@ kq_status upload(void **dst, const void *src, size_t bytes, hipStream_t s) {
 
 extern "C" {
 
-int kq_version(void) { return 10000; }
+int kq_version(void) { return 10100; }
 
 const char *kq_status_string(kq_status s) {
   switch (s) {
@@ -78,6 +78,7 @@ const char *kq_status_string(kq_status s) {
     case KQ_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
     case KQ_ERR_OUT_OF_MEMORY: return "out of memory";
     case KQ_ERR_HIP: return "HIP runtime error";
+    case KQ_ERR_WORKSPACE: return "the call needs a larger device workspace";
   }
   return "unknown status";
 }
@@ -335,8 +336,20 @@ kq_status kq_create(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype sc
   return kq_create_ex(out, n1, n2, x_dtype, scale_dtype, P1, P2, c, alpha, stream, 0u);
 }
 
+kq_status kq_workspace_size(const kq_plan *p, int64_t T, size_t *bytes) {
+  if (!p || !bytes || T < 0 || (p->n && T > ((int64_t)1 << 40) / p->n)) return KQ_ERR_INVALID_ARG;
+  *bytes = kq_ws_bytes(p, T);
+  return KQ_OK;
+}
+
 kq_status kq_transform_quant(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
                              uint8_t *codes, void *scales, float *y_debug, void *stream) {
+  return kq_transform_quant_ws(p, X, T, ldx, codes, scales, y_debug, nullptr, 0, stream);
+}
+
+kq_status kq_transform_quant_ws(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
+                                uint8_t *codes, void *scales, float *y_debug, void *workspace,
+                                size_t workspace_bytes, void *stream) {
   if (!p || T < 0) return KQ_ERR_INVALID_ARG;
   if (T == 0) return KQ_OK;
   if (!X || !codes || !scales) return KQ_ERR_INVALID_ARG;
@@ -348,6 +361,13 @@ kq_status kq_transform_quant(const kq_plan *p, const void *X, int64_t T, int64_t
   if (y_debug && !is_aligned(y_debug, 16)) return KQ_ERR_ALIGNMENT;
   if (T > ((int64_t)1 << 40) / p->n) return KQ_ERR_INVALID_ARG;
   if (p->per_row && T * p->n1 >= ((int64_t)1 << 31)) return KQ_ERR_UNSUPPORTED;
+  const size_t need = kq_ws_bytes(p, T);
+  if (need) {  // the two-kernel designs pass an intermediate through this workspace
+    if (!workspace || workspace_bytes < need) return KQ_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 256)) return KQ_ERR_ALIGNMENT;
+  } else {
+    workspace = nullptr;
+  }
   int dev = -1;  // the plan's buffers live on the device that was current at create time
   if (hipGetDevice(&dev) != hipSuccess || dev != p->device) return KQ_ERR_INVALID_ARG;
   hipError_t e;
@@ -355,9 +375,10 @@ kq_status kq_transform_quant(const kq_plan *p, const void *X, int64_t T, int64_t
     kq_plan v = *p;  // the same plan seen through the small-batch variant's operands
     v.p2op = p->small_p2op;
     v.grid_cap = p->small_grid_cap;
-    e = p->small_launch(&v, X, T, ldx, codes, scales, y_debug, static_cast<hipStream_t>(stream));
+    e = p->small_launch(&v, X, T, ldx, codes, scales, y_debug, nullptr,
+                        static_cast<hipStream_t>(stream));
   } else {
-    e = p->launch(p, X, T, ldx, codes, scales, y_debug, static_cast<hipStream_t>(stream));
+    e = p->launch(p, X, T, ldx, codes, scales, y_debug, workspace, static_cast<hipStream_t>(stream));
   }
   return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }

@@ -38,164 +38,13 @@
 
 #include "kq_internal.h"
 #include "kq_device.h"
+#include "kq_common.h"
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-
-// ------------------------------------------------------------------------------------
-// shared helpers
-// ------------------------------------------------------------------------------------
-
-// Workgroup barrier that orders LDS only. __syncthreads() also fences global memory,
-// which makes every wave wait for its in-flight prefetch loads at each barrier; these
-// kernels only exchange data through LDS, so the release/acquire is restricted to it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-// Max over the wave of a non-negative value, returned wave-uniform: within each row of 16
-// lanes with DPP (quad swaps, half-row and row mirrors), then the four row maxima read
-// into scalars. No LDS round trips.
-// Maxima of absolute values (x >= 0, never NaN: the in-lane maxima start from 0 and
-// fmaxf drops NaN operands). For such x the float order is the order of the bit patterns
-// as unsigned integers, so the cross-lane steps use the integer max, which takes its DPP
-// operand directly (every DPP pattern used here reads a valid lane: no "old" value).
-__device__ __forceinline__ float max_nn(float a, float b) {
-  const uint32_t x = __float_as_uint(a), y = __float_as_uint(b);
-  return __uint_as_float(x > y ? x : y);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_read(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_step(float v) {
-  return max_nn(v, dpp_read<CTRL>(v));
-}
-__device__ __forceinline__ float wave_max_uniform(float v) {
-  v = dpp_step<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_step<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_step<0x141>(v);  // row_half_mirror
-  v = dpp_step<0x140>(v);  // row_mirror: every lane of a row holds the row max
-  const int i = __float_as_int(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(i, 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(i, 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(i, 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(i, 48));
-  return max_nn(max_nn(r0, r1), max_nn(r2, r3));
-}
-
-__device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b) {
-  bf16x8 r;
-  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
-  r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
-  return r;
-}
-
-// x (8 bf16) * c (8 fp32) in fp32, split into hi = bf16(x*c) and lo = bf16(x*c - hi):
-// hi + lo carries ~16 significant bits, so one extra MFMA pass over lo keeps the
-// per-channel scale from adding a second bf16 rounding to the transform.
-// Per pair of values: 2 unpacks, 2 multiplies, one paired RNE conversion for hi, 2 unpacks
-// of hi, 2 subtractions, one paired conversion for lo (5 VALU per value).
-__device__ __forceinline__ void split_scaled(const uint4 &raw, const float *c, uint4 &hi,
-                                             uint4 &lo) {
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float s0 = __fmul_rn(__uint_as_float(w[e] << 16), c[2 * e]);
-    const float s1 = __fmul_rn(__uint_as_float(w[e] & 0xFFFF0000u), c[2 * e + 1]);
-    const bf16x2_t hv = {(__bf16)s0, (__bf16)s1};  // v_cvt_pk_bf16_f32
-    h[e] = __builtin_bit_cast(uint32_t, hv);
-    // opaque to the optimizer, so that hi's fp32 values are unpacked from this word
-    // instead of converting s0 a second time
-    asm("" : "+v"(h[e]));
-    const float r0 = __fsub_rn(s0, __uint_as_float(h[e] << 16));
-    const float r1 = __fsub_rn(s1, __uint_as_float(h[e] & 0xFFFF0000u));
-    const bf16x2_t lv = {(__bf16)r0, (__bf16)r1};
-    l[e] = __builtin_bit_cast(uint32_t, lv);
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-// Per-token step: s32 = fp32(fp32(clip * a) / 7), stored as fp16 (RNE) or fp32; the
-// codes use the stored step, inv = fp32(1 / s) (0 when s == 0, giving all-zero codes).
-struct TokenScale {
-  float s32;
-  _Float16 s16;
-  float inv;
-};
-
-// qmax = 2^(b-1) - 1: 7 for INT4 codes, 127 for INT8 codes
-__device__ __forceinline__ TokenScale token_scale(float amax, float clip, int scale_fp16,
-                                                  float qmax = 7.0f) {
-  TokenScale t;
-  t.s32 = __fdiv_rn(__fmul_rn(clip, amax), qmax);
-  t.s16 = (_Float16)t.s32;
-  const float sf = scale_fp16 ? (float)t.s16 : t.s32;
-  t.inv = (sf == 0.f) ? 0.f : __fdiv_rn(1.0f, sf);
-  return t;
-}
-
-__device__ __forceinline__ void store_scale(void *scales, int64_t tok, const TokenScale &t,
-                                            int scale_fp16) {
-  if (scale_fp16) reinterpret_cast<_Float16 *>(scales)[tok] = t.s16;
-  else reinterpret_cast<float *>(scales)[tok] = t.s32;
-}
-
-// Quantize 8 consecutive values into one dword of 4-bit two's-complement codes (value e
-// in bits 4e..4e+3). Per value: v = fp32(y * inv); adding 1.5*2^23 + 8 in fp32 rounds v
-// to the nearest integer with ties to even (the sum's unit in the last place is 1 and
-// 1.5*2^23 + 8 is even) and leaves q + 8 in the low mantissa bits, for |v| < 2^22; the
-// integer clamp of the bit pattern is the clamp of q to [-8, 7]. The two steps are
-// separate roundings on purpose (no fused multiply-add). Codes are assembled as q + 8
-// and turned into two's complement with one xor per dword. CLAMP = false is only used
-// when every |v| < 7.5 is guaranteed (see clamp_needed), where the clamp is a no-op.
-template <bool CLAMP = true>
-__device__ __forceinline__ uint32_t quant8(const float (&y)[8], float inv) {
-  constexpr float kMagic = 12582920.0f;   // 1.5 * 2^23 + 8, bit pattern 0x4B400008
-  constexpr int kLo = 0x4B400000, kHi = 0x4B40000F;
-  uint32_t u[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float t = __fadd_rn(__fmul_rn(y[e], inv), kMagic);
-    u[e] = CLAMP ? (uint32_t)min(max(__float_as_int(t), kLo), kHi) : __float_as_uint(t);
-  }
-  // byte k of the result = u[2k] | u[2k+1] << 4 (bits above the low byte are ignored)
-  const uint32_t p0 = (u[1] << 4) | u[0], p1 = (u[3] << 4) | u[2];
-  const uint32_t p2 = (u[5] << 4) | u[4], p3 = (u[7] << 4) | u[6];
-  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);  // [p0.b0, p1.b0, 0, 0]
-  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);  // [0, 0, p2.b0, p3.b0]
-  return (lo | hi) ^ 0x88888888u;
-}
-
-// Whether the clamp to [-8, 7] can change a code. With |y| <= a, inv = fp32(1/s) and
-// s the stored step of s32 = fp32(fp32(clip a)/7): for an fp16 step in the normal
-// range (relative rounding error <= 2^-11; an fp32 step is exact) every
-// |fp32(y inv)| <= (7/clip)(1 + 2^-10) < 7.5 once clip >= 0.935 (checked on the host),
-// so rint gives |q| <= 7. A zero or overflowed step gives inv = 0 and q = 0.
-__device__ __forceinline__ bool clamp_needed(int clip_allows_no_clamp, float s32) {
-  return !(clip_allows_no_clamp && (s32 >= 6.103515625e-05f || s32 == 0.f));
-}
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ void copy_to_lds(unsigned char *dst, const void *src, int bytes,
                                             int tid, int nthreads = kThreads) {
@@ -453,8 +302,6 @@ struct StreamCfg {
 // byte written once, so both go non-temporal ("nt"), which keeps them from displacing
 // each other in the caches (measured on MI355X: read 16 KiB + write 4 KiB per token
 // streams about 12% faster than with the default policy).
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // Quantize a wave's whole Y tile (lane holds yacc[m2][nt] = 4 consecutive columns of row
 // 16 nt + lr) into packed code words w[nt][q] (8 consecutive columns each).
@@ -470,23 +317,6 @@ __device__ __forceinline__ void quant_tile(const f32x4 (&yacc)[NT][MT], float in
                            yacc[2 * q + 1][nt][2], yacc[2 * q + 1][nt][3]};
       w[nt][q] = quant8<CLAMP>(yv, inv);
     }
-}
-
-// INT8: 4 consecutive values -> one dword of two's-complement bytes (value e in byte e).
-// Adding 1.5*2^23 in fp32 rounds v = fp32(y * inv) to the nearest integer, ties to even,
-// and leaves q in the low mantissa bits (|v| < 2^22); clamping the bit pattern clamps q to
-// [-128, 127], and its low byte is then q as a two's-complement byte.
-__device__ __forceinline__ uint32_t quant4x8(float y0, float y1, float y2, float y3, float inv) {
-  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23, bit pattern 0x4B400000
-  constexpr int kLo = 0x4B400000 - 128, kHi = 0x4B400000 + 127;
-  const float y[4] = {y0, y1, y2, y3};
-  uint32_t u[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    u[e] = (uint32_t)min(max(__float_as_int(__fadd_rn(__fmul_rn(y[e], inv), kMagic)), kLo), kHi);
-  const uint32_t lo = __builtin_amdgcn_perm(u[1], u[0], 0x0C0C0400u);  // [u0.b0, u1.b0, 0, 0]
-  const uint32_t hi = __builtin_amdgcn_perm(u[3], u[2], 0x04000C0Cu);  // [0, 0, u2.b0, u3.b0]
-  return lo | hi;
 }
 
 // INT8 codes of a wave's Y tile (lane holds yacc[m2][nt] = 4 consecutive columns of row
@@ -1364,12 +1194,6 @@ struct ColsCfg {
   static_assert(!PADDED || N2 <= 128, "padded n1: n2 <= 128");
 };
 
-// byte offset of 16-byte chunk `cc` of row `r` of a token tile in LDS
-template <int CH>
-__device__ __forceinline__ int vchunk_off(int r, int cc) {
-  if constexpr ((CH & (CH - 1)) == 0) return (r * CH + (cc ^ (r & (CH - 1)))) * 16;
-  else return (r * (CH + 1) + cc) * 16;
-}
 
 // BITS = 4: INT4 codes (8 per dword); BITS = 8: INT8 codes (one byte per value)
 template <int N1, int N2, bool HAS_C, bool YDBG = false, int BITS = 4>
@@ -1652,7 +1476,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
 // ------------------------------------------------------------------------------------
 template <int N1, int N2, int WPT, bool HAS_C, bool DEEP>
 hipError_t launch_reg(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
-                      void *scales, float *y_debug, hipStream_t stream) {
+                      void *scales, float *y_debug, void *ws, hipStream_t stream) {
   using C = RegCfg<N1, N2, WPT, HAS_C, DEEP>;
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
@@ -1665,7 +1489,7 @@ hipError_t launch_reg(const kq_plan *p, const void *X, int64_t T, int64_t ldx, u
 
 template <int N1, int N2, bool HAS_C, int BITS = 4>
 hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
-                       void *scales, float *y_debug, hipStream_t stream) {
+                       void *scales, float *y_debug, void *ws, hipStream_t stream) {
   using C = ColsCfg<N1, N2, HAS_C>;
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
@@ -1681,7 +1505,7 @@ hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
 
 template <int N1, int N2, bool HAS_C, int BITS = 4, int N2R = N2>
 hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
-                         void *scales, float *y_debug, hipStream_t stream) {
+                         void *scales, float *y_debug, void *ws, hipStream_t stream) {
   using C = StreamCfg<N1, N2, HAS_C>;
   const int64_t ngroups = (T + C::WAVES - 1) / C::WAVES;
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
@@ -1699,7 +1523,7 @@ hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx
 
 template <int N1, int N2, int BITS = 4>
 hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
-                       void *scales, float *y_debug, hipStream_t stream) {
+                       void *scales, float *y_debug, void *ws, hipStream_t stream) {
   using C = PairCfg<N1, N2>;
   const int grid = (int)(T < (int64_t)p->grid_cap ? T : (int64_t)p->grid_cap);
   auto k = y_debug ? &kq_pair_kernel<N1, N2, true, BITS> : &kq_pair_kernel<N1, N2, false, BITS>;
@@ -1723,7 +1547,7 @@ hipError_t launch_pair(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
                    "fused_mfma_bf16_pair_" #A "x" #B "_int8"}
 template <int N2, int BITS = 4>
 hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
-                       void *scales, float *y_debug, hipStream_t stream) {
+                       void *scales, float *y_debug, void *ws, hipStream_t stream) {
   using C = RowsCfg<N2>;
   const int64_t ntiles = (T * p->n1 + C::ROWS - 1) / C::ROWS;
   const int64_t groups = (ntiles + C::WAVES - 1) / C::WAVES;
@@ -1821,6 +1645,12 @@ const kq_fused_variant kVariants[] = {
     KQ_COLS(128, 144, false, ""),
     KQ_COLS(56, 64, false, ""),    KQ_COLS(56, 64, true, "_c"),
     KQ_COLS(64, 104, false, ""),   KQ_COLS(64, 104, true, "_c"),
+    // 2560 (40 x 64, n1 padded to 48), 5632 (64 x 88, n2 padded to 96), 6144 (64 x 96) and
+    // 8960 (80 x 112, n2 padded to 128)
+    KQ_COLS(40, 64, false, ""),    KQ_COLS(40, 64, true, "_c"),
+    KQ_COLS(64, 88, false, ""),    KQ_COLS(64, 88, true, "_c"),
+    KQ_COLS(64, 96, false, ""),    KQ_COLS(64, 96, true, "_c"),
+    KQ_COLS(80, 112, false, ""),   KQ_COLS(80, 112, true, "_c"),
     // the other splits, selectable with KQ_FLAG_SPLIT_*
     KQ_ALL1(16, 32), KQ_ALL1(32, 32), KQ_ALL(16, 64), KQ_ALL(32, 64), KQ_ALL(48, 64),
     KQ_ALL(64, 64), KQ_ALL(16, 128), KQ_ALL(32, 128), KQ_ALL(48, 128), KQ_ALL(64, 128),
@@ -1848,6 +1678,12 @@ const kq_fused_variant kVariants[] = {
     KQ_COLS8(64, 80, false, ""),   KQ_COLS8(64, 80, true, "_c"),
     KQ_COLS8(64, 112, false, ""),  KQ_COLS8(64, 112, true, "_c"),
     KQ_COLS8(128, 144, false, ""),
+    KQ_COLS8(56, 64, false, ""),   KQ_COLS8(56, 64, true, "_c"),
+    KQ_COLS8(64, 104, false, ""),  KQ_COLS8(64, 104, true, "_c"),
+    KQ_COLS8(40, 64, false, ""),   KQ_COLS8(40, 64, true, "_c"),
+    KQ_COLS8(64, 88, false, ""),   KQ_COLS8(64, 88, true, "_c"),
+    KQ_COLS8(64, 96, false, ""),   KQ_COLS8(64, 96, true, "_c"),
+    KQ_COLS8(80, 112, false, ""),  KQ_COLS8(80, 112, true, "_c"),
     KQ_STREAM(16, 128), KQ_STREAM(32, 128), KQ_STREAM(48, 128),
     KQ_PAIR(16, 64), KQ_PAIR(32, 64), KQ_PAIR(48, 64), KQ_PAIR(64, 64),
     KQ_PAIR(16, 128), KQ_PAIR(32, 128), KQ_PAIR(48, 128), KQ_PAIR(64, 128),

@@ -81,10 +81,14 @@ __global__ __launch_bounds__(kThreads) void kq_generic_kernel(
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) amax = fmaxf(amax, s_red[w]);
 
-    const float s32 = __fdiv_rn(__fmul_rn(clip, amax), 7.0f);
+    float s32 = __fdiv_rn(__fmul_rn(clip, amax), 7.0f);
     const _Float16 s16 = (_Float16)s32;
     const float sf = scale_fp16 ? (float)s16 : s32;
-    const float inv = (sf == 0.f) ? 0.f : __fdiv_rn(1.0f, sf);
+    float inv = (sf == 0.f) ? 0.f : __fdiv_rn(1.0f, sf);
+    if (__builtin_isinf(inv)) {  // fp32 step <= 2^-128: stored as 0, codes 0 (underflow)
+      s32 = 0.f;
+      inv = 0.f;
+    }
 
     uint8_t *crow = codes + tok * (int64_t)(n / 2);
     for (int mm = tid; mm < n / 2; mm += kThreads) {
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void kq_generic_kernel(
 }
 
 hipError_t launch_generic(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
-                          void *scales, float *y_debug, hipStream_t stream) {
+                          void *scales, float *y_debug, void *ws, hipStream_t stream) {
   const int grid = (int)(T < (int64_t)p->grid_cap ? T : (int64_t)p->grid_cap);
   const size_t lds = kq_generic_lds_bytes(p->n);
   hipLaunchKernelGGL(kq_generic_kernel, dim3(grid), dim3(kThreads), lds, stream, X,

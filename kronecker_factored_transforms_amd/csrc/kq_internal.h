@@ -16,8 +16,10 @@ struct kq_plan;
 
 // Launches one kq_transform_quant on a plan of the matching variant. Arguments are
 // already validated by the host API.
+// `ws` is the call's device workspace (at least kq_ws_bytes(p, T) bytes, 256-byte aligned),
+// or nullptr for the single-kernel designs, which need none.
 typedef hipError_t (*kq_launch_fn)(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
-                                   uint8_t *codes, void *scales, float *y_debug,
+                                   uint8_t *codes, void *scales, float *y_debug, void *ws,
                                    hipStream_t stream);
 
 struct kq_plan {
@@ -48,7 +50,21 @@ struct kq_plan {
   // 1: identity left factor and one step per row of V (T * n1 scales)
   int per_row;
   int bits;             // code width: 4 or 8
+  // device workspace of the two-kernel designs for large factors: region A holds
+  // ws_a_per_token bytes per token, region B (at a 256-byte aligned offset after A) holds
+  // ws_b_per_token bytes per token; both 0 for the single-kernel designs
+  size_t ws_a_per_token;
+  size_t ws_b_per_token;
 };
+
+// Workspace of a call of T tokens: total bytes, and the offset of region B.
+inline size_t kq_ws_offset_b(const kq_plan *p, int64_t T) {
+  return ((size_t)T * p->ws_a_per_token + 255) / 256 * 256;
+}
+inline size_t kq_ws_bytes(const kq_plan *p, int64_t T) {
+  if (!p->ws_a_per_token && !p->ws_b_per_token) return 0;
+  return kq_ws_offset_b(p, T) + ((size_t)T * p->ws_b_per_token + 255) / 256 * 256;
+}
 
 // ---- fused MFMA family (kq_fused.hip) ----
 // Work splits of the fused family: 1 or 2 waves per token with the token in registers

@@ -117,3 +117,39 @@ def check_plan_against_oracle(inp, plan, codes, scales, y):
     assert np.array_equal(np_scales(scales).reshape(-1).view(np.uint8), s.view(np.uint8)), \
         "scales differ"
     return rel
+
+
+def check_all_tokens_chunked(inp, plan, codes, scales, y, chunk=4096):
+    """Every token of a full-size call against the oracle, a chunk of tokens at a time (host
+    memory stays bounded): the fp32 Y within the dtype's rel-L2 tolerance over the whole
+    tensor (and the worst per-token rel-L2 reported), codes and steps bit-exact against the
+    oracle quantizer on the GPU's own Y. Arguments are torch tensors of the whole call."""
+    import torch
+    T = int(codes.shape[0])
+    sd = "fp16" if plan.scale_dtype == torch.float16 else "fp32"
+    err2 = ref2 = 0.0
+    worst = 0.0
+    for a in range(0, T, chunk):
+        b = min(T, a + chunk)
+        yc = y[a:b].cpu().numpy()
+        Y = O.transform(inp.X[a:b], inp.P1, inp.P2, inp.c, inp.wl.dtype)
+        d = yc.astype(np.float64) - Y
+        e_tok = np.einsum("ij,ij->i", d, d)
+        r_tok = np.einsum("ij,ij->i", Y, Y)
+        err2 += float(e_tok.sum())
+        ref2 += float(r_tok.sum())
+        nz = r_tok > 0
+        if nz.any():
+            worst = max(worst, float(np.sqrt((e_tok[nz] / r_tok[nz]).max())))
+        q, s = O.quantize_per_token(np.ascontiguousarray(yc, dtype=np.float32), np.float32(plan.clip),
+                                    sd, bits=plan.bits)
+        packed = O.pack_int4(q) if plan.bits == 4 else O.pack_int8(q)
+        cc = codes[a:b].cpu().numpy()
+        if not np.array_equal(cc, packed):
+            bad = np.argwhere(cc != packed)
+            raise AssertionError(f"{len(bad)} code bytes differ; first at token {a + bad[0][0]}")
+        assert np.array_equal(np_scales(scales[a:b]).view(np.uint8), s.view(np.uint8)), \
+            f"scales differ in tokens {a}..{b}"
+    rel = float(np.sqrt(err2 / ref2)) if ref2 else float(np.sqrt(err2))
+    assert rel <= TOL[inp.wl.dtype], f"rel-L2 {rel:.3e} > {TOL[inp.wl.dtype]:.0e}"
+    return rel, worst

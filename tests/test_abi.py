@@ -44,10 +44,10 @@ def test_no_torch_types_in_the_abi():
 
 def test_status_strings_and_version(L):
     assert B.kq_status_string(0) == "ok"
-    msgs = {B.kq_status_string(s) for s in range(6)}
-    assert len(msgs) == 6
+    msgs = {B.kq_status_string(s) for s in range(7)}
+    assert len(msgs) == 7
     assert B.kq_status_string(99) == "unknown status"
-    assert B.kq_version() >= 10000
+    assert B.kq_version() >= 10100
 
 
 def _brute_factors(n):
@@ -207,3 +207,30 @@ def test_a_c99_program_builds_against_the_header_and_links_the_library(L, tmp_pa
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok 64 128", (r.returncode, r.stdout, r.stderr)
+
+
+def test_plan_call_refuses_wrong_output_buffers():
+    """Caller-provided (codes, scales) are checked before any pointer reaches the C ABI:
+    a buffer of the wrong size, dtype, layout or device would be written past its end."""
+    import torch
+    p = B.Plan.__new__(B.Plan)
+    p.handle, p.n1, p.n2, p.n, p.bits, p.per_row = None, 64, 128, 8192, 4, False
+    p.x_dtype, p.scale_dtype = torch.bfloat16, torch.float16
+    T = 5
+    X = torch.zeros((T, 8192), dtype=torch.bfloat16)
+    good_c = torch.empty((T, 4096), dtype=torch.uint8)
+    good_s = torch.empty((T,), dtype=torch.float16)
+    bad = [
+        (torch.empty((T - 1, 4096), dtype=torch.uint8), good_s),          # short codes
+        (torch.empty((T, 4096), dtype=torch.int8), good_s),               # dtype
+        (torch.empty((4096, T), dtype=torch.uint8).t(), good_s),          # not contiguous
+        (good_c, torch.empty((T - 1,), dtype=torch.float16)),             # short scales
+        (good_c, torch.empty((T,), dtype=torch.float32)),                 # scale dtype
+        (good_c, torch.empty((T, 64), dtype=torch.float16)),              # per-row shape
+    ]
+    for codes, scales in bad:
+        with pytest.raises(ValueError):
+            p(X, out=(codes, scales))
+    p.per_row = True  # a per-row plan wants T x n1 scales
+    with pytest.raises(ValueError):
+        p(X, out=(good_c, good_s))

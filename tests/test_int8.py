@@ -89,20 +89,30 @@ def test_int8_full_size_sampled(gpu):
     _check(sub, cs.cpu().numpy(), K.np_scales(ss), ys.cpu().numpy(), plan.clip)
 
 
-def test_int8_unsupported_shapes(gpu):
-    # n2 = 32 has only the register kernels, which have no INT8 epilogue
-    wl = replace(S.WORKLOADS["hidden_n8192"], n1=16, n2=32, n_outliers=2, pivot_channels=0)
+# Shapes whose default kernel is a register kernel, which has no INT8 epilogue: n2 = 32,
+# and 16..48 x 128 with a per-channel scale.
+INT8_LEFT_OUT = [(16, 32, False), (32, 32, True), (16, 128, True), (32, 128, True),
+                 (48, 128, True)]
+
+
+@pytest.mark.parametrize("n1,n2,with_c", INT8_LEFT_OUT)
+def test_int8_unsupported_shapes(gpu, n1, n2, with_c):
+    import torch
+    wl = replace(S.WORKLOADS["hidden_n8192"], n1=n1, n2=n2, n_outliers=2, pivot_channels=0)
     inp = S.make(wl, T=4)
     X, P1, P2, c = K.device_inputs(inp)
+    c = torch.ones(n1 * n2, dtype=torch.float32, device=gpu) if with_c else None
     with pytest.raises(B.KqError) as e:
-        B.kq_create(16, 32, "bf16", "fp16", P1, P2, None, 1.0, None, B.KQ_FLAG_INT8)
+        B.kq_create(n1, n2, "bf16", "fp16", P1, P2, c, 1.0, None, B.KQ_FLAG_INT8)
     assert e.value.status == B.KQ_ERR_UNSUPPORTED
 
 
 COLS_SHAPES = [(112, 128, True), (86, 128, True), (108, 128, False), (96, 128, True),
                (128, 128, True), (64, 128, True), (80, 128, False), (128, 224, False),
                (128, 160, False), (128, 256, False), (64, 112, True), (128, 144, False),
-               (32, 48, True)]
+               (32, 48, True), (56, 64, True), (56, 64, False), (64, 104, True),
+               (64, 104, False), (40, 64, True), (64, 88, False), (64, 96, True),
+               (80, 112, False)]
 
 
 @pytest.mark.parametrize("n1,n2,with_c", COLS_SHAPES)

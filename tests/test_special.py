@@ -299,3 +299,48 @@ def test_widened_kernels_edge_cases(gpu, name, bits, kernel, case):
     e = torch.empty((0, inp.wl.n), dtype=torch.bfloat16, device=gpu)
     c0, s0 = plan(e)
     assert c0.shape == (0, inp.wl.n * bits // 8) and s0.shape == (0,)
+
+
+# Reading R9 on every kernel family: with fp32 steps, a token whose absmax is 2^-126 has
+# the step fp32(2^-126 / 7) < 2^-128, whose reciprocal overflows fp32; that step counts as
+# an underflow (stored 0, codes 0). Identity factors keep Y = X exactly (normal numbers,
+# entries 0 / 1), so the tiny tokens reach the quantizer unchanged.
+TINY_STEP_CASES = [
+    ("hidden_n8192", 1100, 0, "fused_mfma_bf16_stream_64x128"),
+    ("hidden_n8192", 37, 0, "fused_mfma_bf16_pair_64x128"),
+    ("down_proj_n14336", 301, 0, "fused_mfma_bf16_cols_112x128_c"),
+    ("attn_n4096", 1100, 0, "fused_mfma_bf16_stream_64x64_c"),
+    ("hidden_n8192", 203, B.KQ_FLAG_FORCE_GENERIC, "generic_fp32_fma"),
+    ("tiny_fp32_n64", 16, 0, "generic_fp32_fma"),
+]
+
+
+@pytest.mark.parametrize("name,T,flags,kernel", TINY_STEP_CASES)
+def test_fp32_step_with_overflowing_reciprocal_is_an_underflow(gpu, name, T, flags, kernel):
+    import torch
+    wl = S.WORKLOADS[name]
+    inp = S.make(wl, T=T)
+    x = (S.bf16_bits_to_f32(inp.X) if wl.dtype == "bf16" else inp.X).astype(np.float32)
+    tiny = [0, T // 2, T - 1]
+    x[tiny] = 0
+    x[tiny, 5] = np.float32(2.0 ** -126)      # step fp32(2^-126 / 7) < 2^-128: underflow
+    x[tiny, 9] = -np.float32(2.0 ** -127)
+    x[1] = 0
+    x[1, 3] = np.float32(2.0 ** -122)         # step ~ 2^-125 > 2^-128: quantized normally
+    x[1, 4] = -np.float32(2.0 ** -124)
+    inp.X = S.to_bf16_bits(x.astype(np.float64)) if wl.dtype == "bf16" else x
+    c = None
+    if inp.c is not None:
+        c = torch.ones(wl.n, dtype=torch.float32, device=gpu)
+    dP1 = _factor_tensor(np.eye(wl.n1), wl.dtype, gpu)
+    dP2 = _factor_tensor(np.eye(wl.n2), wl.dtype, gpu)
+    plan, X = K.make_plan(inp, P1=dP1, P2=dP2, c=c, scale_dtype="fp32", flags=flags)
+    assert plan.kernel_for(T) == kernel, plan.kernel_for(T)
+    codes, scales, y = K.run(plan, X)
+    yc = y.cpu().numpy()
+    assert np.array_equal(yc, x)                   # identity factors: exact
+    K.assert_quant_bit_exact(codes.cpu().numpy(), K.np_scales(scales), yc, plan.clip, "fp32")
+    s = K.np_scales(scales)
+    cn = codes.cpu().numpy()
+    assert np.all(s[tiny] == 0) and np.all(cn[tiny] == 0)
+    assert s[1] > 0 and np.any(cn[1] != 0)

@@ -23,7 +23,8 @@ SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (3
           (86, 128, False), (86, 128, True), (108, 128, False), (108, 128, True),
           (32, 48, False), (32, 48, True), (64, 80, False), (64, 80, True), (64, 112, False),
           (64, 112, True), (128, 144, False), (56, 64, False), (56, 64, True), (64, 104, False),
-          (64, 104, True)]
+          (64, 104, True), (40, 64, False), (40, 64, True), (64, 88, False), (64, 88, True),
+          (64, 96, False), (64, 96, True), (80, 112, False), (80, 112, True)]
 
 
 def _available(n1, n2, split, with_c=False):
@@ -34,6 +35,8 @@ def _available(n1, n2, split, with_c=False):
     if n2 % 32:  # n2 padded to a multiple of 32: the column kernel, and 64 x 112 rows in
         # the stream kernel's 128-column layout
         return split == "cols" or (split == "stream" and (n1, n2, with_c) == (64, 112, False))
+    if n2 not in (32, 64, 128):  # e.g. 64 x 96: only the column kernel
+        return split == "cols"
     if split == "deep":
         return (n1, n2, with_c) in DEEP_SHAPES
     if split == "stream":
