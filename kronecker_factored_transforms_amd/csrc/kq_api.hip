@@ -172,7 +172,8 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   flags &= ~KQ_FLAG_INT8;
   const unsigned split_flags =
       flags & (KQ_FLAG_SPLIT_REG1 | KQ_FLAG_SPLIT_REG2 | KQ_FLAG_SPLIT_COLS | KQ_FLAG_SPLIT_DEEP |
-               KQ_FLAG_SPLIT_STREAM | KQ_FLAG_SPLIT_PAIR);
+               KQ_FLAG_SPLIT_STREAM | KQ_FLAG_SPLIT_PAIR | KQ_FLAG_SPLIT_TWOSTAGE |
+               KQ_FLAG_SPLIT_PTILE);
   if (flags & ~(KQ_FLAG_FORCE_GENERIC | split_flags)) return KQ_ERR_INVALID_ARG;
   if ((split_flags & (split_flags - 1)) != 0) return KQ_ERR_INVALID_ARG;  // at most one
   if (split_flags && ((flags & KQ_FLAG_FORCE_GENERIC) || x_dtype != KQ_BF16))
@@ -183,7 +184,10 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
                     : split_flags == KQ_FLAG_SPLIT_DEEP ? KQ_SPLIT_DEEP
                     : split_flags == KQ_FLAG_SPLIT_STREAM ? KQ_SPLIT_STREAM
                     : split_flags == KQ_FLAG_SPLIT_PAIR ? KQ_SPLIT_PAIR
+                    : split_flags == KQ_FLAG_SPLIT_TWOSTAGE ? KQ_SPLIT_TWOSTAGE
+                    : split_flags == KQ_FLAG_SPLIT_PTILE ? KQ_SPLIT_PTILE
                                                         : 0;
+  const bool large_split = split == KQ_SPLIT_TWOSTAGE || split == KQ_SPLIT_PTILE;
 
   // kernel choice (pure host logic, before any HIP call)
   const char *kname = nullptr;
@@ -192,7 +196,10 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   int kind = -1;
   const kq_fused_variant *fv = nullptr;
   if (x_dtype == KQ_BF16 && !(flags & KQ_FLAG_FORCE_GENERIC)) {
-    fv = kq_fused_lookup(n1, n2, c != nullptr, split, bits);
+    // single-kernel designs first; factors beyond them (or a forced two-kernel split) go
+    // to the designs of kq_large.hip
+    fv = large_split ? nullptr : kq_fused_lookup(n1, n2, c != nullptr, split, bits);
+    if (!fv && (split == 0 || large_split)) fv = kq_large_lookup(n1, n2, c != nullptr, split, bits);
     if (fv) {
       fn = fv->launch;
       kname = fv->name;
@@ -259,6 +266,18 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
         hipSuccess) {
       st = KQ_ERR_HIP;
       goto fail;
+    }
+    if (fv->kernel_symbol2) {  // two-kernel design: the second kernel's grid and the workspace
+      int per_cu2 = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu2, fv->kernel_symbol2, fv->threads2,
+                                                       0) != hipSuccess) {
+        st = KQ_ERR_HIP;
+        goto fail;
+      }
+      if (per_cu2 < 1) { st = KQ_ERR_UNSUPPORTED; goto fail; }
+      p->grid_cap2 = ncu * per_cu2;
+      p->ws_a_per_token = fv->ws_a_per_token;
+      p->ws_b_per_token = fv->ws_b_per_token;
     }
     // The stream kernel runs one wave per token and one workgroup of eight per CU: below
     // about four tokens per CU it leaves most CUs idle, and the pair kernel (two waves

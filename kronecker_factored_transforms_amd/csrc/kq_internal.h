@@ -32,6 +32,7 @@ struct kq_plan {
   const char *kname;    // static kernel variant name
   kq_launch_fn launch;
   int grid_cap;         // persistent-grid size (workgroups) for this device
+  int grid_cap2;        // the same for the second kernel of a two-kernel design
   // fused MFMA variant: operand-ordered bf16 factor copies (see kq_fused.hip)
   void *p2op;
   void *p1op;
@@ -71,8 +72,12 @@ inline size_t kq_ws_bytes(const kq_plan *p, int64_t T) {
 // ("deep": one wave per token and per SIMD, next token prefetched into registers), the
 // column kernel (n2/32 waves per token, token staged in LDS), or the stream kernel (one
 // wave per token, next token prefetched into an LDS slot by DMA).
+// The two-kernel designs for large factors (kq_large.hip): Figure 8(c) (stage 1 writes Z
+// to the workspace, stage 2 + quantizer reads it) and Figure 8(b) (P1 in tiles of its
+// output dimension, Y through the workspace, a second kernel quantizes).
 enum { KQ_SPLIT_REG1 = 1, KQ_SPLIT_REG2 = 2, KQ_SPLIT_COLS = 3, KQ_SPLIT_DEEP = 4,
-       KQ_SPLIT_STREAM = 5, KQ_SPLIT_PAIR = 6, KQ_SPLIT_ROWS = 7 };
+       KQ_SPLIT_STREAM = 5, KQ_SPLIT_PAIR = 6, KQ_SPLIT_ROWS = 7, KQ_SPLIT_TWOSTAGE = 8,
+       KQ_SPLIT_PTILE = 9 };
 
 struct kq_fused_variant {
   int n1, n2;
@@ -84,11 +89,19 @@ struct kq_fused_variant {
   kq_launch_fn launch;
   const void *kernel_symbol;
   const char *name;
+  // two-kernel designs only: the second kernel (for its occupancy) and the workspace
+  const void *kernel_symbol2;
+  int threads2;
+  size_t ws_a_per_token;
+  size_t ws_b_per_token;
 };
 
 // The variant for (n1, n2, has_c) with the given split (0: the default one) and code width,
 // or nullptr.
 const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split, int bits = 4);
+// The two-kernel designs for large factors (kq_large.hip): the variant for (n1, n2,
+// has_c) with split KQ_SPLIT_TWOSTAGE / KQ_SPLIT_PTILE (0: the shape's default), or nullptr.
+const kq_fused_variant *kq_large_lookup(int n1, int n2, bool has_c, int split, int bits);
 // The rows kernel (identity left factor, one step per row of V) for n2, or nullptr.
 const kq_fused_variant *kq_fused_lookup_rows(int n2, int bits);
 void kq_fused_arrange_p2_rows(const uint16_t *P2, int n2, uint16_t *out);

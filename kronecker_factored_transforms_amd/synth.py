@@ -114,6 +114,20 @@ WORKLOADS = {
     "down_proj_n28672": Workload(
         "down_proj_n28672", 6, T=4096, n1=128, n2=224, dtype="bf16", x_kind="silu_gate",
         p_kind="orthogonal", alpha=3.0),
+    # the same input with a per-channel scale: n2 > 128 with c has only the two-kernel
+    # designs for factors beyond the on-chip memory
+    "down_proj_n28672_c": Workload(
+        "down_proj_n28672_c", 11, T=4096, n1=128, n2=224, dtype="bf16", x_kind="silu_gate",
+        p_kind="near_identity", p_eps=0.05, c_kind="loguniform", c_lo=0.25, c_hi=4.0,
+        alpha=None),
+    # both factors above 128: a 72B-class FFN down-projection input, 29568 = 168 x 176
+    "down_proj_n29568": Workload(
+        "down_proj_n29568", 12, T=4096, n1=168, n2=176, dtype="bf16", x_kind="silu_gate",
+        p_kind="orthogonal", alpha=3.0),
+    # the largest factors built: 65536 = 256 x 256 (heavy-tailed activations)
+    "hidden_n65536": Workload(
+        "hidden_n65536", 13, T=2048, n1=256, n2=256, dtype="bf16", x_kind="student_t3",
+        n_outliers=8, outlier_scale=30.0, p_kind="orthogonal", alpha=3.0),
 }
 
 
