@@ -200,6 +200,23 @@ kq_status kq_transform_quant_ws(const kq_plan *plan, const void *X, int64_t T, i
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * kq_transform_quant_noalloc -- kq_transform_quant_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace of the two-kernel designs comes from a scratch array inside
+ * the library, KQ_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load until the
+ * process ends. The call itself allocates nothing. Arguments as kq_transform_quant.
+ * Every call of this entry point on one GPU shares that GPU's scratch: calls that may
+ * overlap on a GPU (different streams, or host threads without ordering) race on it and
+ * must be ordered by the caller. Plans of the single-kernel designs need no workspace and
+ * take any T. Errors: as kq_transform_quant_ws, with WORKSPACE when the call needs more
+ * than KQ_NOALLOC_SCRATCH_BYTES (kq_workspace_size(plan, T) says how much), UNSUPPORTED
+ * for a device ordinal of 64 or more.
+ */
+#define KQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kq_status kq_transform_quant_noalloc(const kq_plan *plan, const void *X, int64_t T, int64_t ldx,
+                                     uint8_t *codes, void *scales, float *y_debug, void *stream);
+
+/*
  * kq_int4_gemm -- the INT4 x INT4 consumer of two kq_transform_quant outputs, on the int8
  * matrix cores ("FlatQuant" page, Putting It Together: the quantized activations feed an
  * INT4 GEMM; "High-Rate Quantized Matrix Multiplication I", Technical Summary: product of

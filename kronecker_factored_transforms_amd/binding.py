@@ -33,7 +33,9 @@ EXPORTS = (
     "kq_choose_factors", "kq_create", "kq_create_ex", "kq_transform_quant", "kq_destroy",
     "kq_plan_clip_ratio", "kq_plan_kernel_name", "kq_plan_kernel_name_for", "kq_status_string",
     "kq_version", "kq_int4_gemm", "kq_workspace_size", "kq_transform_quant_ws",
+    "kq_transform_quant_noalloc",
 )
+KQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -64,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.kq_transform_quant.restype = i32
     L.kq_transform_quant_ws.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.kq_transform_quant_ws.restype = i32
+    L.kq_transform_quant_noalloc.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
+    L.kq_transform_quant_noalloc.restype = i32
     L.kq_workspace_size.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_size_t)]
     L.kq_workspace_size.restype = i32
     L.kq_destroy.argtypes = [vp]
@@ -155,6 +159,12 @@ def kq_transform_quant_ws(plan, X, T, ldx, codes, scales, y_debug, workspace, wo
                                      _ptr(y_debug), _ptr(workspace), int(workspace_bytes),
                                      _stream(stream))
     _check(st, "kq_transform_quant_ws")
+
+
+def kq_transform_quant_noalloc(plan, X, T, ldx, codes, scales, y_debug=None, stream=None) -> None:
+    st = lib().kq_transform_quant_noalloc(plan, _ptr(X), int(T), int(ldx), _ptr(codes),
+                                          _ptr(scales), _ptr(y_debug), _stream(stream))
+    _check(st, "kq_transform_quant_noalloc")
 
 
 def kq_workspace_size(plan, T: int) -> int:

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "kq_internal.h"
@@ -61,6 +63,36 @@ kq_status upload(void **dst, const void *src, size_t bytes, hipStream_t s) {
     return KQ_ERR_OUT_OF_MEMORY;
   }
   if (hipMemcpyAsync(*dst, src, bytes, hipMemcpyHostToDevice, s) != hipSuccess) return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
+// Scratch memory of kq_transform_quant_noalloc: the workspace of the two-kernel designs
+// for callers that cannot allocate. One copy per GPU, held from the library's load until
+// the process ends; every such call on a GPU shares it, so calls that overlap on one GPU
+// (different streams, or host threads without ordering) race on it. Nothing in it needs
+// to start at zero: both designs write every byte of the intermediate they read back.
+constexpr size_t kScratchBytes = KQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of each device's copy of `scratch`, looked up once per device with that
+// device current. In host code the name `scratch` is only a host-side stand-in symbol:
+// every use of the memory from the host goes through these addresses.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+kq_status scratch_address(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices) return KQ_ERR_UNSUPPORTED;
+  void *a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!a) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    a = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!a) {
+      if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return KQ_ERR_HIP;
+      g_scratch_addr[dev].store(a, std::memory_order_release);
+    }
+  }
+  *out = a;
   return KQ_OK;
 }
 
@@ -400,6 +432,24 @@ kq_status kq_transform_quant_ws(const kq_plan *p, const void *X, int64_t T, int6
     e = p->launch(p, X, T, ldx, codes, scales, y_debug, workspace, static_cast<hipStream_t>(stream));
   }
   return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
+kq_status kq_transform_quant_noalloc(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
+                                     uint8_t *codes, void *scales, float *y_debug, void *stream) {
+  if (!p || T < 0 || (p->n && T > ((int64_t)1 << 40) / p->n)) return KQ_ERR_INVALID_ARG;
+  if (T == 0) return KQ_OK;
+  const size_t need = kq_ws_bytes(p, T);
+  if (need > kScratchBytes) return KQ_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (need) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+    if (dev != p->device) return KQ_ERR_INVALID_ARG;
+    const kq_status st = scratch_address(dev, &ws);
+    if (st != KQ_OK) return st;
+  }
+  return kq_transform_quant_ws(p, X, T, ldx, codes, scales, y_debug, ws, need ? kScratchBytes : 0,
+                               stream);
 }
 
 const char *kq_plan_kernel_name_for(const kq_plan *p, int64_t T) {
