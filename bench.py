@@ -40,8 +40,8 @@ def log(*a):
 
 # every source that decides what a launch reads and writes: the kernels, the device helpers
 # (DMA and its cache policy), and the host code that picks the kernel and sizes its grid
-KERNEL_SOURCES = ("kq_api.hip", "kq_internal.h", "kq_device.h", "kq_fused.hip", "kq_generic.hip",
-                  "kq_large.hip")
+KERNEL_SOURCES = ("kq_api.hip", "kq_internal.h", "kq_device.h", "kq_common.h", "kq_fused.hip",
+                  "kq_generic.hip", "kq_large.hip", "kq_f32.hip")
 
 
 def kernel_source_sha256() -> str:

@@ -40,6 +40,13 @@ float clip_from_alpha(float alpha) {
   return (float)v;
 }
 
+// fp32 -> bf16 bit pattern, round to nearest even (finite values)
+uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 float bf16_to_f32(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;
@@ -239,6 +246,15 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
       kind = KQ_KIND_FUSED_MFMA;
     }
   }
+  if (!fn && x_dtype == KQ_FP32 && !(flags & KQ_FLAG_FORCE_GENERIC) && bits == 4) {
+    fv = kq_f32_lookup(n1, n2, c != nullptr);
+    if (fv) {
+      fn = fv->launch;
+      kname = fv->name;
+      ksym = fv->kernel_symbol;
+      kind = KQ_KIND_FUSED_F32;
+    }
+  }
   if (!fn) {
     if (split || bits == 8 || n > kq_generic_max_n()) return KQ_ERR_UNSUPPORTED;
     fn = kq_generic_launcher(&kname, &ksym);
@@ -341,6 +357,33 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
           p->small_max_T = (int64_t)4 * ncu;
         }
       }
+    }
+  } else if (kind == KQ_KIND_FUSED_F32) {
+    // each factor as bf16 hi = bf16(p) and lo = bf16(p - hi), both in the fused kernels'
+    // operand order, hi then lo in one buffer
+    const float *f1 = reinterpret_cast<const float *>(h1.data());
+    const float *f2 = reinterpret_cast<const float *>(h2.data());
+    std::vector<uint16_t> s1h(h1.size() / 4), s1l(h1.size() / 4), s2h(h2.size() / 4), s2l(h2.size() / 4);
+    for (size_t i = 0; i < s1h.size(); ++i) {
+      s1h[i] = f32_to_bf16_rne(f1[i]);
+      s1l[i] = f32_to_bf16_rne(f1[i] - bf16_to_f32(s1h[i]));
+    }
+    for (size_t i = 0; i < s2h.size(); ++i) {
+      s2h[i] = f32_to_bf16_rne(f2[i]);
+      s2l[i] = f32_to_bf16_rne(f2[i] - bf16_to_f32(s2h[i]));
+    }
+    const size_t e1 = kq_fused_p1op_elems(n1), e2 = kq_fused_p2op_elems(n2);
+    std::vector<uint16_t> a1(2 * e1), a2(2 * e2);
+    kq_fused_arrange_p1(s1h.data(), n1, a1.data());
+    kq_fused_arrange_p1(s1l.data(), n1, a1.data() + e1);
+    kq_fused_arrange_p2(s2h.data(), n2, fv->p2_block, a2.data());
+    kq_fused_arrange_p2(s2l.data(), n2, fv->p2_block, a2.data() + e2);
+    if ((st = upload(&p->p1op, a1.data(), a1.size() * 2, s)) != KQ_OK) goto fail;
+    if ((st = upload(&p->p2op, a2.data(), a2.size() * 2, s)) != KQ_OK) goto fail;
+    if (hipStreamSynchronize(s) != hipSuccess) { st = KQ_ERR_HIP; goto fail; }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ksym, fv->threads, 0) != hipSuccess) {
+      st = KQ_ERR_HIP;
+      goto fail;
     }
   } else {
     std::vector<float> f1((size_t)n1 * n1), f2((size_t)n2 * n2);

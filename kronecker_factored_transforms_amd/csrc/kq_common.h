@@ -192,4 +192,48 @@ __device__ __forceinline__ int vchunk_off(int r, int cc) {
   else return (r * (CH + 1) + cc) * 16;
 }
 
+// Quantize a wave's whole Y tile (lane holds yacc[m2][nt] = 4 consecutive columns of row
+// 16 nt + lr) into packed code words w[nt][q] (8 consecutive columns each).
+template <bool CLAMP, int MT, int NT>
+__device__ __forceinline__ void quant_tile(const f32x4 (&yacc)[NT][MT], float inv,
+                                           uint32_t (&w)[MT][NT / 2]) {
+#pragma unroll
+  for (int nt = 0; nt < MT; ++nt)
+#pragma unroll
+    for (int q = 0; q < NT / 2; ++q) {
+      const float yv[8] = {yacc[2 * q][nt][0],     yacc[2 * q][nt][1],     yacc[2 * q][nt][2],
+                           yacc[2 * q][nt][3],     yacc[2 * q + 1][nt][0], yacc[2 * q + 1][nt][1],
+                           yacc[2 * q + 1][nt][2], yacc[2 * q + 1][nt][3]};
+      w[nt][q] = quant8<CLAMP>(yv, inv);
+    }
+}
+
+// N2R: the real row length when the tile is laid out for N2 = 128 and rows hold only
+// N2R = 112 values (lane group 3 then holds 16 real and 16 padding columns; rows of codes
+// are 56 bytes, so the stores are split to 8-byte aligned halves)
+template <int N1, int N2, int N2R = N2>
+__device__ __forceinline__ void store_codes(uint8_t *codes, int64_t tok, const uint32_t (*w)[N2 / 32],
+                                            int lr, int g) {
+  static_assert(N2R == N2 || (N2 == 128 && N2R == 112), "padded stream rows: 112 of 128");
+  uint8_t *crow = codes + tok * (int64_t)(N1 * N2R / 2);
+#pragma unroll
+  for (int nt = 0; nt < N1 / 16; ++nt) {
+    uint8_t *dst = crow + (nt * 16 + lr) * (N2R / 2) + g * (N2 / 8);
+    if constexpr (N2R != N2) {
+      const u32x2_t v0 = {w[nt][0], w[nt][1]};
+      __builtin_nontemporal_store(v0, reinterpret_cast<u32x2_t *>(dst));
+      if (g < 3) {
+        const u32x2_t v1 = {w[nt][2], w[nt][3]};
+        __builtin_nontemporal_store(v1, reinterpret_cast<u32x2_t *>(dst + 8));
+      }
+    } else if constexpr (N2 == 128) {
+      const u32x4_t v = {w[nt][0], w[nt][1], w[nt][2], w[nt][3]};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
+    } else {
+      const u32x2_t v = {w[nt][0], w[nt][1]};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(dst));
+    }
+  }
+}
+
 }  // namespace

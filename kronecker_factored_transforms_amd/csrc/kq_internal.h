@@ -10,6 +10,7 @@
 enum kq_kernel_kind {
   KQ_KIND_FUSED_MFMA = 0,  // bf16 X/P, two chained bf16 MFMA contractions, fused epilogue
   KQ_KIND_GENERIC = 1,     // any supported dtype/shape, fp32 FMA contractions
+  KQ_KIND_FUSED_F32 = 2,   // fp32 X/P on bf16 MFMA (hi/lo operand pairs, three products)
 };
 
 struct kq_plan;
@@ -102,6 +103,9 @@ const kq_fused_variant *kq_fused_lookup(int n1, int n2, bool has_c, int split, i
 // The two-kernel designs for large factors (kq_large.hip): the variant for (n1, n2,
 // has_c) with split KQ_SPLIT_TWOSTAGE / KQ_SPLIT_PTILE (0: the shape's default), or nullptr.
 const kq_fused_variant *kq_large_lookup(int n1, int n2, bool has_c, int split, int bits);
+// The fp32 kernel (kq_f32.hip: fp32 values as bf16 hi/lo pairs on the bf16 MFMA) for
+// (n1, n2, has_c), or nullptr. Its plan holds P2's and P1's operands twice, hi then lo.
+const kq_fused_variant *kq_f32_lookup(int n1, int n2, bool has_c);
 // The rows kernel (identity left factor, one step per row of V) for n2, or nullptr.
 const kq_fused_variant *kq_fused_lookup_rows(int n2, int bits);
 void kq_fused_arrange_p2_rows(const uint16_t *P2, int n2, uint16_t *out);

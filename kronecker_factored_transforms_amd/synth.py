@@ -124,6 +124,10 @@ WORKLOADS = {
     "down_proj_n29568": Workload(
         "down_proj_n29568", 12, T=4096, n1=168, n2=176, dtype="bf16", x_kind="silu_gate",
         p_kind="orthogonal", alpha=3.0),
+    # fp32 activations of hidden size 4096 (64 x 64): the fp32 path on the matrix cores
+    "fp32_n4096": Workload(
+        "fp32_n4096", 14, T=2048, n1=64, n2=64, dtype="fp32", x_kind="normal",
+        n_outliers=4, outlier_scale=20.0, p_kind="orthogonal", alpha=3.0),
     # the largest factors built: 65536 = 256 x 256 (heavy-tailed activations)
     "hidden_n65536": Workload(
         "hidden_n65536", 13, T=2048, n1=256, n2=256, dtype="bf16", x_kind="student_t3",

@@ -45,7 +45,8 @@ CASES = {
     "rows": (W["kv_h8_d128"], 0, 4, True, 0),
     "rows_strided": (W["kv_h8_d128"], 0, 4, True, 64),
     "rows_int8": (W["kv_h8_d128"], 0, 8, True, 0),
-    "generic_fp32": (replace(W["tiny_fp32_n64"], n1=64, n2=64), 0, 4, False, 0),
+    "generic_fp32": (replace(W["tiny_fp32_n64"], n1=64, n2=64), B.KQ_FLAG_FORCE_GENERIC, 4, False, 0),
+    "f32x3_64x64": (replace(W["tiny_fp32_n64"], n1=64, n2=64), 0, 4, False, 64),
 }
 
 

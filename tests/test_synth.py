@@ -23,6 +23,7 @@ def test_workload_shapes():
     assert shapes["down_proj_n28672_c"] == (4096, 128, 224, "bf16")
     assert shapes["down_proj_n29568"] == (4096, 168, 176, "bf16")
     assert shapes["hidden_n65536"] == (2048, 256, 256, "bf16")
+    assert shapes["fp32_n4096"] == (2048, 64, 64, "fp32")
     assert S.WORKLOADS["down_proj_n28672_c"].c_kind == "loguniform"
     assert len({w.stream for w in S.WORKLOADS.values() if w.name not in
                 ("decode_n8192_t64", "prefill_n8192_t65536")}) == len(S.WORKLOADS) - 2
