@@ -54,6 +54,20 @@ float bf16_to_f32(uint16_t b) {
   return f;
 }
 
+// bf16 patterns -> fp16 patterns of P * 2^-f (round to nearest even) in place; returns f,
+// the smallest exponent >= 0 that keeps max |P| 2^-f below 2^15
+int to_scaled_f16(std::vector<uint16_t> &v) {
+  float mx = 0.f;
+  for (uint16_t b : v) mx = fmaxf(mx, fabsf(bf16_to_f32(b)));
+  int f = 0;
+  while (ldexpf(mx, -f) >= 32768.0f) ++f;
+  for (uint16_t &b : v) {
+    const _Float16 h = (_Float16)ldexpf(bf16_to_f32(b), -f);
+    memcpy(&b, &h, 2);
+  }
+  return f;
+}
+
 void free_plan_buffers(kq_plan *p) {
   if (!p) return;
   if (p->p1op) (void)hipFree(p->p1op);
@@ -302,9 +316,21 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
 
   if (kind == KQ_KIND_FUSED_MFMA) {
     std::vector<uint16_t> a1(kq_fused_p1op_elems(n1)), a2(kq_fused_p2op_elems(n2));
-    kq_fused_arrange_p1(reinterpret_cast<const uint16_t *>(h1.data()), n1, a1.data());
-    kq_fused_arrange_p2(reinterpret_cast<const uint16_t *>(h2.data()), n2, fv->p2_block,
-                        a2.data());
+    // The factors' element patterns the kernels take: bf16 as given, or, for the variants
+    // that run both contractions on fp16 operands, P * 2^-f as fp16 (round to nearest
+    // even) with f >= 0 the smallest exponent that keeps max |P| 2^-f below 2^15 (fp16
+    // holds up to 65504); f is undone on Y.
+    std::vector<uint16_t> e1((const uint16_t *)h1.data(), (const uint16_t *)h1.data() + (size_t)n1 * n1);
+    std::vector<uint16_t> e2((const uint16_t *)h2.data(), (const uint16_t *)h2.data() + (size_t)n2 * n2);
+    if (fv->f16_ops) {
+      p->p1_exp = to_scaled_f16(e1);
+      p->p2_exp = to_scaled_f16(e2);
+      float cm = 0.f;
+      for (int i = 0; i < n; ++i) cm = fmaxf(cm, fabsf(hc[i]));
+      p->c_absmax = cm;
+    }
+    kq_fused_arrange_p1(e1.data(), n1, a1.data());
+    kq_fused_arrange_p2(e2.data(), n2, fv->p2_block, a2.data());
     if ((st = upload(&p->p1op, a1.data(), a1.size() * 2, s)) != KQ_OK) goto fail;
     if ((st = upload(&p->p2op, a2.data(), a2.size() * 2, s)) != KQ_OK) goto fail;
     if (c && (st = upload(reinterpret_cast<void **>(&p->c), hc.data(), hc.size() * 4, s)) != KQ_OK)
@@ -341,8 +367,8 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
       int small_per_cu = 0;
       if (sv) {
         std::vector<uint16_t> b2(kq_fused_p2op_elems(n2));
-        kq_fused_arrange_p2(reinterpret_cast<const uint16_t *>(h2.data()), n2, sv->p2_block,
-                            b2.data());
+        if (sv->f16_ops != fv->f16_ops) { st = KQ_ERR_UNSUPPORTED; goto fail; }
+        kq_fused_arrange_p2(e2.data(), n2, sv->p2_block, b2.data());
         if ((st = upload(&p->small_p2op, b2.data(), b2.size() * 2, s)) != KQ_OK) goto fail;
         if (hipStreamSynchronize(s) != hipSuccess) { st = KQ_ERR_HIP; goto fail; }
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&small_per_cu, sv->kernel_symbol,

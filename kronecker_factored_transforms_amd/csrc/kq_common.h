@@ -11,6 +11,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
 
 namespace {
 
@@ -160,6 +162,73 @@ __device__ __forceinline__ uint32_t quant8(const float (&y)[8], float inv) {
 // so rint gives |q| <= 7. A zero or overflowed step gives inv = 0 and q = 0.
 __device__ __forceinline__ bool clamp_needed(int clip_allows_no_clamp, float s32) {
   return !(clip_allows_no_clamp && (s32 >= 6.103515625e-05f || s32 == 0.f));
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Largest |x| of 8 bf16 values (bit patterns in raw), as the bit pattern of a
+// non-negative bf16 in the low 16 bits (integer order = magnitude order for |x|)
+__device__ __forceinline__ uint32_t absmax_bf16(const uint4 &raw, uint32_t m) {
+  u16x2_t v = __builtin_bit_cast(u16x2_t, raw.x & 0x7FFF7FFFu);
+  v = __builtin_elementwise_max(v, __builtin_bit_cast(u16x2_t, raw.y & 0x7FFF7FFFu));
+  v = __builtin_elementwise_max(v, __builtin_bit_cast(u16x2_t, raw.z & 0x7FFF7FFFu));
+  v = __builtin_elementwise_max(v, __builtin_bit_cast(u16x2_t, raw.w & 0x7FFF7FFFu));
+  const uint32_t a = v[0] > v[1] ? v[0] : v[1];
+  return a > m ? a : m;
+}
+
+// x (8 bf16) * c (8 fp32) in fp32, scaled by 2^s (exact for normal results), rounded once
+// to fp16 (round to nearest even): the stage-1 operand of the kernels that run both
+// contractions on fp16 operands
+__device__ __forceinline__ f16x8 scale_round_f16(const uint4 &raw, const float *c, int s) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float s0 = __fmul_rn(__uint_as_float(w[e] << 16), c[2 * e]);
+    float s1 = __fmul_rn(__uint_as_float(w[e] & 0xFFFF0000u), c[2 * e + 1]);
+    if (s != 0) {
+      s0 = __builtin_ldexpf(s0, s);
+      s1 = __builtin_ldexpf(s1, s);
+    }
+    r[2 * e] = (_Float16)s0;
+    r[2 * e + 1] = (_Float16)s1;
+  }
+  return r;
+}
+
+// Power-of-two exponent s that brings a token's values into fp16's range before the
+// conversion, from a bound zmax on their magnitudes: 0 when zmax lies in [2^-8, 2^15) (the
+// values convert as they are), else 14 - floor(log2 zmax), which puts zmax * 2^s in
+// [2^14, 2^15) (clamped to [-126, 127]). A function of zmax alone, so every kernel that
+// sees the same values picks the same s.
+__device__ __forceinline__ int f16_scale_exp(float zmax) {
+  const int eb = (int)((__float_as_uint(zmax) >> 23) & 0xFFu);  // biased exponent
+  if (eb >= 127 - 8 && eb < 127 + 15) return 0;
+  const int s = 14 - (eb - 127);
+  return s < -126 ? -126 : (s > 127 ? 127 : s);
+}
+
+// 8 fp32 values (two accumulators) -> fp16 operand, each scaled by 2^s first (exact for
+// normal results) and rounded to nearest even
+__device__ __forceinline__ f16x8 pack8_f16(const f32x4 &a, const f32x4 &b, int s) {
+  f16x8 r;
+  if (s == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (_Float16)a[e];
+      r[4 + e] = (_Float16)b[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (_Float16)__builtin_ldexpf(a[e], s);
+      r[4 + e] = (_Float16)__builtin_ldexpf(b[e], s);
+    }
+  }
+  return r;
 }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {

@@ -337,12 +337,17 @@ __device__ __forceinline__ void store_codes8(uint8_t *codes, int64_t tok,
 // N2R < N2: rows of X (and of Y and the codes) hold N2R values; the tile in LDS keeps the
 // N2 layout, its padding pieces meet P2's zero rows (see dma_tile) and padded columns of
 // Y are zero and not stored
+// With c (HAS_C), both contractions run on fp16 operands: x^ = fp16(fp32(x c) 2^sx), where
+// the token's bound max|x| max|c| picks sx (f16_scale_exp; 0 for ordinary tokens); P2 and
+// P1 come from the plan as fp16 operands scaled by 2^-f2 and 2^-f1 (f_exp = f1 + f2); the
+// token's largest |Z| picks sz for Z's conversion; Y = Y' 2^(f_exp - sx - sz) exactly.
 template <int N1, int N2, bool HAS_C, bool YDBG, int BITS = 4, int N2R = N2>
 __global__ __launch_bounds__(512) void kq_stream_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
-    const float *__restrict__ cvec, float clip, int scale_fp16, int clip_allows_no_clamp,
-    uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
+    const float *__restrict__ cvec, int f_exp, float cmax, float clip, int scale_fp16,
+    int clip_allows_no_clamp, uint8_t *__restrict__ codes, void *__restrict__ scales,
+    float *__restrict__ ydbg) {
   using C = StreamCfg<N1, N2, HAS_C>;
   static_assert(N2R == N2 || (N2 == 128 && N2R == 112 && !HAS_C && BITS == 4), "padded rows");
   constexpr int n = N1 * N2R;
@@ -429,6 +434,97 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
     // quantizer: a higher issue priority for the MFMA phase keeps the matrix core fed
     // while the other wave's VALU work fills the gaps (measured on MI355X: about 2 %).
     __builtin_amdgcn_s_setprio(1);
+    constexpr int NH = C::NT / 2;  // column tiles per half
+    f32x4 yacc[C::NT][C::MT];
+    float pm[C::NT];
+    if constexpr (HAS_C) {
+      // ---- the token's x, its bound max|x| max|c| and the scale of x^ ----
+      uint4 raw[C::KS][C::MT];
+      uint32_t xm = 0;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const unsigned char *arow = slot + lr * C::RB + (((ks * 4 + g) ^ C::swz(lr)) * 16);
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+          raw[ks][mt] = *reinterpret_cast<const uint4 *>(arow + mt * 16 * C::RB);
+          xm = absmax_bf16(raw[ks][mt], xm);
+        }
+      }
+      const float xmax = wave_max_uniform(__uint_as_float(xm << 16));
+      const int sx = __builtin_amdgcn_readfirstlane(f16_scale_exp(__fmul_rn(xmax, cmax)));
+      // ---- stage 1 over all column tiles: Z' = x^ P2' on fp16 operands ----
+      f32x4 zacc[C::MT][C::NT];
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) zacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        f16x8 av[C::MT];
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) {
+          const unsigned char *crow = s_c + (mt * 16 + lr) * (N2 * 4);
+          const int u0 = (ks * 4 + g) * 2;
+          const float4 c0 = *reinterpret_cast<const float4 *>(crow + ((u0 ^ lr) * 16));
+          const float4 c1 = *reinterpret_cast<const float4 *>(crow + (((u0 + 1) ^ lr) * 16));
+          const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          av[mt] = scale_round_f16(raw[ks][mt], cc, sx);
+        }
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+          const f16x8 bv = reinterpret_cast<const f16x8 *>(sp2)[(ks * C::NT + nt) * 64 + lane];
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt) zacc[mt][nt] = mfma_f16(av[mt], bv, zacc[mt][nt]);
+        }
+      }
+      wait_and_fence<kWaitLgkm0>();  // every slot read has returned: the slot is free again
+      if (tok + stride < T) dma_tile(tok + stride);
+      float zm = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) zm = fmaxf(zm, fabsf(zacc[mt][nt][r]));
+      const int zs = __builtin_amdgcn_readfirstlane(f16_scale_exp(wave_max_uniform(zm)));
+      // ---- stage 2 on fp16 operands: Y^T = Z^T P1 ----
+#pragma unroll
+      for (int m2 = 0; m2 < C::NT; ++m2)
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt) yacc[m2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const bool pad = C::KHALF && kk == C::KK - 1;
+        f16x8 za[C::NT];
+#pragma unroll
+        for (int m2 = 0; m2 < C::NT; ++m2)
+          za[m2] = pack8_f16(zacc[2 * kk][m2], pad ? zero : zacc[(2 * kk + 1) % C::MT][m2], zs);
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt) {
+          const f16x8 b = __builtin_bit_cast(f16x8, p1r[kk][nt]);
+#pragma unroll
+          for (int m2 = 0; m2 < C::NT; ++m2) yacc[m2][nt] = mfma_f16(za[m2], b, yacc[m2][nt]);
+        }
+      }
+      const int ty = f_exp - sx - zs;  // Y = Y' 2^(f1 + f2 - sx - sz), exact
+      if (ty != 0) {
+#pragma unroll
+        for (int m2 = 0; m2 < C::NT; ++m2)
+#pragma unroll
+          for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[m2][nt][r] = __builtin_ldexpf(yacc[m2][nt][r], ty);
+      }
+#pragma unroll
+      for (int m2 = 0; m2 < C::NT; ++m2) {
+        pm[m2] = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pm[m2] = fmaxf(pm[m2], fabsf(yacc[m2][nt][r]));
+      }
+    } else {
     // ---- stages 1 and 2 per half of the output columns ----
     // A column tile of Y needs only the same column tile of Z, so each half runs stage 1
     // (Z = V P2 for its columns) and stage 2 (Y^T = Z^T P1) on its own: only half of
@@ -436,9 +532,6 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
     // ahead, and the first half's absmax overlaps the second half's MFMAs.
     // A operand (mt, ks) of lane L: V[16 mt + lr][32 ks + 8 g + v], i.e. piece 4 ks + g
     // of row 16 mt + lr.
-    constexpr int NH = C::NT / 2;  // column tiles per half
-    f32x4 yacc[C::NT][C::MT];
-    float pm[C::NT];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4 zacc[C::MT][NH];
@@ -449,32 +542,16 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const unsigned char *arow = slot + lr * C::RB + (((ks * 4 + g) ^ C::swz(lr)) * 16);
-        bf16x8 av[C::MT], al[HAS_C ? C::MT : 1], bv[NH];
+        bf16x8 av[C::MT], bv[NH];
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {  // swz(16 mt + lr) == swz(lr)
+        for (int mt = 0; mt < C::MT; ++mt)  // swz(16 mt + lr) == swz(lr)
           av[mt] = *reinterpret_cast<const bf16x8 *>(arow + mt * 16 * C::RB);
-          if constexpr (HAS_C) {
-            // x^ = fp32(x c) as bf16 hi + lo words (row 16 mt + lr, channels 32 ks + 8 g + [0, 8))
-            const unsigned char *crow = s_c + (mt * 16 + lr) * (N2 * 4);
-            const int u0 = (ks * 4 + g) * 2;
-            const float4 c0 = *reinterpret_cast<const float4 *>(crow + ((u0 ^ lr) * 16));
-            const float4 c1 = *reinterpret_cast<const float4 *>(crow + (((u0 + 1) ^ lr) * 16));
-            const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            uint4 hi, lo;
-            split_scaled(__builtin_bit_cast(uint4, av[mt]), cc, hi, lo);
-            av[mt] = __builtin_bit_cast(bf16x8, hi);
-            al[mt] = __builtin_bit_cast(bf16x8, lo);
-          }
-        }
 #pragma unroll
         for (int nt = 0; nt < NH; ++nt) bv[nt] = sp2[(ks * C::NT + h * NH + nt) * 64 + lane];
 #pragma unroll
         for (int nt = 0; nt < NH; ++nt)
 #pragma unroll
-          for (int mt = 0; mt < C::MT; ++mt) {
-            zacc[mt][nt] = mfma(av[mt], bv[nt], zacc[mt][nt]);
-            if constexpr (HAS_C) zacc[mt][nt] = mfma(al[mt], bv[nt], zacc[mt][nt]);
-          }
+          for (int mt = 0; mt < C::MT; ++mt) zacc[mt][nt] = mfma(av[mt], bv[nt], zacc[mt][nt]);
       }
       if (h == 1) {
         wait_and_fence<kWaitLgkm0>();  // every slot read has returned: the slot is free again
@@ -510,6 +587,7 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
           for (int r = 0; r < 4; ++r) pm[m2] = fmaxf(pm[m2], fabsf(yacc[m2][nt][r]));
       }
     }
+    }  // !HAS_C
 
     __builtin_amdgcn_s_setprio(0);
     // ---- epilogue: lane holds Y[16 nt + lr][LPL g + 4 m2 + r] ----
@@ -1428,6 +1506,301 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
 }
 
 // ------------------------------------------------------------------------------------
+// column kernel with a per-channel scale: fp16 operands, two barriers per token
+// ------------------------------------------------------------------------------------
+// The same work split as the column kernel (W = n2p / 32 waves per token, each owning 32
+// output columns; whole tokens fill four waves when W < 4), with both contractions on
+// fp16 operands:
+//  * x^ = fp16(fp32(x c) 2^sx), where the token's bound max|x| max|c| picks the
+//    power-of-two sx (f16_scale_exp: 0 for ordinary tokens), stored as the token's plane in
+//    LDS; P2 comes from the plan as fp16 operands (P2 2^-f2), kept per wave in registers;
+//  * stage 1 accumulates Z' = x^ P2' in fp32; the token's largest |Z'| meets in LDS and
+//    picks sz for Z's conversion to fp16; P1 comes from the plan as fp16 (P1 2^-f1);
+//  * stage 2 accumulates Y' in fp32 and Y = Y' 2^(f1 + f2 - sx - sz) exactly.
+// One LDS tile per token slot. Per token two barriers: (A) after stage 1, when every wave
+// has read the tile and published its |Z'| maximum and the next token's |x| maximum (its
+// chunks were loaded into registers a whole token earlier), the next token's tile is
+// stored over this one; (B) after stage 2, when the next tile is complete and every wave
+// has published its |Y| maximum. c is re-read from L2 for every tile.
+template <int N1, int N2>
+struct ColsCCfg {
+  static_assert(N1 >= 16 && N1 <= 128, "n1 in [16, 128]");
+  static_assert(N2 % 8 == 0 && N2 >= 32 && N2 <= 128, "n2 a multiple of 8 in [32, 128]");
+  static constexpr int N2P = cols_n2p(N2);
+  static constexpr bool PADC = N2P != N2;
+  static constexpr int W = N2P / 32;                // waves per token
+  static constexpr int WAVES = cols_waves(N2P);     // waves per workgroup
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int TPI = WAVES / W;             // tokens per workgroup iteration
+  static constexpr bool PADDED = (N1 % 16) != 0;
+  static constexpr int MT = (N1 + 15) / 16;
+  static constexpr int N1P = MT * 16;
+  static constexpr int KS = N2P / 32;
+  static constexpr int KK = (N1P + 31) / 32;
+  static constexpr bool KHALF = (N1P % 32) != 0;
+  static constexpr int CH = N2 / 8;                 // 16-byte chunks per row of X
+  static constexpr int CHP = N2P / 8;               // chunks per row in LDS
+  static constexpr bool POW2 = (CHP & (CHP - 1)) == 0;
+  static constexpr int ROW_CHUNKS = POW2 ? CHP : CHP + 1;
+  static constexpr int TOK_CHUNKS = N1 * CH;
+  static constexpr int CPT = (TPI * TOK_CHUNKS + THREADS - 1) / THREADS;
+  static constexpr bool EVEN = CPT * THREADS == TPI * TOK_CHUNKS;
+  static constexpr int V_BYTES = N1P * ROW_CHUNKS * 16;
+  static constexpr int VBUF = TPI * V_BYTES;
+  static constexpr int P1_BYTES = KK * MT * 1024;
+  // two workgroups per CU when both fit in LDS
+  static constexpr bool TWO = VBUF + P1_BYTES + 1024 <= 80 * 1024;
+};
+
+// workgroups per CU the launch bounds ask for
+template <int N1, int N2>
+constexpr int colsc_blocks = ColsCCfg<N1, N2>::TWO ? 2 : 1;
+
+template <int N1, int N2, bool YDBG = false, int BITS = 4>
+__global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2>)) void kq_colsc_kernel(
+    const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
+    const f16x8 *__restrict__ p2op, const f16x8 *__restrict__ p1op,
+    const float *__restrict__ cvec, int f_exp, float cmax, float clip, int scale_fp16,
+    uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
+  using C = ColsCCfg<N1, N2>;
+  constexpr int n = N1 * N2;
+  __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
+  __shared__ __align__(16) unsigned char s_v[C::VBUF];
+  __shared__ float s_zmax[2][C::WAVES];
+  __shared__ float s_xmax[2][C::WAVES][C::TPI];
+  __shared__ float s_red[2][C::WAVES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int lr = lane & 15;
+  const int ts = wave / C::W;  // token slot within the iteration
+  const int wt = wave % C::W;  // column block of this wave
+  const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
+
+  copy_to_lds(s_p1, p1op, C::P1_BYTES, tid, C::THREADS);
+  if constexpr (C::PADDED) {  // rows n1 .. n1p of every slot stay zero
+    constexpr int PAD_UNITS = (C::N1P - N1) * C::ROW_CHUNKS;
+    for (int q = tid; q < C::TPI * PAD_UNITS; q += C::THREADS)
+      *reinterpret_cast<uint4 *>(s_v + (q / PAD_UNITS) * C::V_BYTES + N1 * C::ROW_CHUNKS * 16 +
+                                 (q % PAD_UNITS) * 16) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if constexpr (C::PADC) {  // chunks ch .. chp of every row stay zero
+    constexpr int PC = C::CHP - C::CH, PER_SLOT = N1 * PC;
+    for (int q = tid; q < C::TPI * PER_SLOT; q += C::THREADS) {
+      const int sl = q / PER_SLOT, r = (q % PER_SLOT) / PC, cc = C::CH + q % PC;
+      *reinterpret_cast<uint4 *>(s_v + sl * C::V_BYTES + vchunk_off<C::CHP>(r, cc)) =
+          make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  // per-thread chunk coordinates (fixed for the whole kernel)
+  int c_ts[C::CPT], c_row[C::CPT], c_cc[C::CPT];
+  bool c_ok[C::CPT];
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int q0 = tid + C::THREADS * i;
+    c_ok[i] = C::EVEN || q0 < C::TPI * C::TOK_CHUNKS;
+    const int q = c_ok[i] ? q0 : 0;
+    c_ts[i] = q / C::TOK_CHUNKS;
+    const int qq = q % C::TOK_CHUNKS;
+    c_row[i] = qq / C::CH;
+    c_cc[i] = qq % C::CH;
+  }
+  uint4 pre[C::CPT];
+  auto issue_loads = [&](int64_t grp) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int64_t t = grp * C::TPI + c_ts[i];
+      if (c_ok[i] && t < T)
+        pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + c_row[i] * N2 + c_cc[i] * 8);
+      else
+        pre[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  // |x| maximum of the loaded chunks per token slot, wave-reduced, into s_xmax[b]
+  auto publish_xmax = [&](int b) {
+    uint32_t m[C::TPI];
+#pragma unroll
+    for (int sl = 0; sl < C::TPI; ++sl) m[sl] = 0;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const uint32_t a = absmax_bf16(pre[i], 0);
+#pragma unroll
+      for (int sl = 0; sl < C::TPI; ++sl)
+        if (c_ts[i] == sl) m[sl] = a > m[sl] ? a : m[sl];
+    }
+#pragma unroll
+    for (int sl = 0; sl < C::TPI; ++sl) {
+      const float v = wave_max_uniform(__uint_as_float(m[sl] << 16));
+      if (lane == 0) s_xmax[b][wave][sl] = v;
+    }
+  };
+  // the scale exponent of x^ for every token slot, from the published maxima
+  auto x_scales = [&](int b, int (&sx)[C::TPI]) {
+#pragma unroll
+    for (int sl = 0; sl < C::TPI; ++sl) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::WAVES; ++w) v = fmaxf(v, s_xmax[b][w][sl]);
+      sx[sl] = __builtin_amdgcn_readfirstlane(f16_scale_exp(__fmul_rn(v, cmax)));
+    }
+  };
+  auto store_lds = [&](const int (&sx)[C::TPI]) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      if (!c_ok[i]) continue;
+      int s = sx[0];
+#pragma unroll
+      for (int sl = 1; sl < C::TPI; ++sl) s = c_ts[i] == sl ? sx[sl] : s;
+      const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
+      const float4 a = cp[0], b = cp[1];
+      const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      *reinterpret_cast<f16x8 *>(s_v + c_ts[i] * C::V_BYTES + vchunk_off<C::CHP>(c_row[i], c_cc[i])) =
+          scale_round_f16(pre[i], cl, s);
+    }
+  };
+  f16x8 p2w[C::KS][2];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    p2w[ks][0] = p2op[((wt * C::KS + ks) * 2 + 0) * 64 + lane];
+    p2w[ks][1] = p2op[((wt * C::KS + ks) * 2 + 1) * 64 + lane];
+  }
+
+  int64_t grp = blockIdx.x;
+  int sx[C::TPI];
+  if (grp < ngroups) issue_loads(grp);
+  publish_xmax(1);
+  lds_barrier();  // P1, the zero padding and the first token's |x| maxima visible
+  x_scales(1, sx);
+  if (grp < ngroups) store_lds(sx);
+  int sx_tok = sx[0];  // the scale of x^ of this wave's token
+#pragma unroll
+  for (int sl = 1; sl < C::TPI; ++sl) sx_tok = ts == sl ? sx[sl] : sx_tok;
+  lds_barrier();  // the first tile visible
+  if (grp + gridDim.x < ngroups) issue_loads(grp + gridDim.x);
+
+  const f16x8 *sp1 = reinterpret_cast<const f16x8 *>(s_p1);
+  const unsigned char *vt = s_v + ts * C::V_BYTES;
+  for (int it = 0; grp < ngroups; grp += gridDim.x, ++it) {
+    const int64_t tok = grp * C::TPI + ts;
+    const int64_t nxt = grp + gridDim.x;
+    // ---- stage 1: Z'[:, block] = x^ P2'[:, block] ----
+    f32x4 zacc[C::MT][2];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) zacc[mt][0] = zacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        const f16x8 a = *reinterpret_cast<const f16x8 *>(vt + vchunk_off<C::CHP>(mt * 16 + lr, ks * 4 + g));
+        zacc[mt][0] = mfma_f16(a, p2w[ks][0], zacc[mt][0]);
+        zacc[mt][1] = mfma_f16(a, p2w[ks][1], zacc[mt][1]);
+      }
+    float zm = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) zm = fmaxf(zm, fmaxf(fabsf(zacc[mt][0][r]), fabsf(zacc[mt][1][r])));
+    zm = wave_max_uniform(zm);
+    if (lane == 0) s_zmax[it & 1][wave] = zm;
+    if (nxt < ngroups) publish_xmax(it & 1);  // the next token's chunks, loaded a token ago
+    lds_barrier();  // (A) the tile is read; the |Z'| and next |x| maxima are published
+    float zmax = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::W; ++w) zmax = fmaxf(zmax, s_zmax[it & 1][ts * C::W + w]);
+    const int zs = __builtin_amdgcn_readfirstlane(f16_scale_exp(zmax));
+    const int ty = f_exp - sx_tok - zs;  // Y = Y' 2^(f1 + f2 - sx - sz), exact
+    // the next group's tile replaces this one
+    if (nxt < ngroups) {
+      x_scales(it & 1, sx);
+      store_lds(sx);
+      if (nxt + gridDim.x < ngroups) issue_loads(nxt + gridDim.x);
+    }
+
+    // ---- stage 2: Y'^T[block, :] = Z'[:, block]^T P1' on fp16 operands ----
+    f16x8 za[C::KK][2];
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const bool pad = C::KHALF && kk == C::KK - 1;
+      za[kk][0] = pack8_f16(zacc[2 * kk][0], pad ? zero : zacc[(2 * kk + 1) % C::MT][0], zs);
+      za[kk][1] = pack8_f16(zacc[2 * kk][1], pad ? zero : zacc[(2 * kk + 1) % C::MT][1], zs);
+    }
+    f32x4 yacc[2][C::MT];
+#pragma unroll
+    for (int nt = 0; nt < C::MT; ++nt) yacc[0][nt] = yacc[1][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) {
+        const f16x8 b = sp1[(kk * C::MT + nt) * 64 + lane];
+        yacc[0][nt] = mfma_f16(za[kk][0], b, yacc[0][nt]);
+        yacc[1][nt] = mfma_f16(za[kk][1], b, yacc[1][nt]);
+      }
+    if (ty != 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yacc[h][nt][r] = __builtin_ldexpf(yacc[h][nt][r], ty);
+    }
+    if (nxt < ngroups) {  // the next token's scale, for the next iteration
+      sx_tok = sx[0];
+#pragma unroll
+      for (int sl = 1; sl < C::TPI; ++sl) sx_tok = ts == sl ? sx[sl] : sx_tok;
+    }
+
+    // ---- epilogue: absmax over the token, then codes ----
+    float m = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[h][nt][r]));
+    m = wave_max_uniform(m);
+    if (lane == 0) s_red[it & 1][wave] = m;
+    lds_barrier();  // (B) the next tile is stored; the |Y| maxima are published
+    float amax = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::W; ++w) amax = fmaxf(amax, s_red[it & 1][ts * C::W + w]);
+    const TokenScale sc = token_scale(amax, clip, scale_fp16, BITS == 4 ? 7.0f : 127.0f);
+
+    if (tok < T) {
+      // lane holds Y[j = nt*16 + lr][wt*32 + 8g + 4h + r]
+      constexpr int RB = N2 * BITS / 8;
+      uint8_t *crow = codes + tok * (int64_t)(n * BITS / 8);
+      const uint32_t loff = (uint32_t)(lr * RB + (wt * 32 + g * 8) * BITS / 8);
+#pragma unroll
+      for (int nt = 0; nt < C::MT; ++nt) {
+        const int j = nt * 16 + lr;
+        if (C::PADDED && j >= N1) continue;
+        if (C::PADC && wt * 32 + g * 8 >= N2) continue;
+        uint8_t *dst = crow + (loff + (uint32_t)(nt * 16 * RB));
+        if constexpr (BITS == 8) {
+          const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], sc.inv),
+                             quant4x8(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3], sc.inv)};
+          *reinterpret_cast<u32x2_t *>(dst) = w;
+        } else {
+          const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
+                               yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
+          *reinterpret_cast<uint32_t *>(dst) = quant8(yv, sc.inv);
+        }
+        if constexpr (YDBG) {
+          float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wt * 32 + g * 8);
+          yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
+          yp[1] = make_float4(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]);
+        }
+      }
+      if (wt == 0 && lane == 0) store_scale(scales, tok, sc, scale_fp16);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // launchers and the variant table
 // ------------------------------------------------------------------------------------
 template <int N1, int N2, int WPT, bool HAS_C, bool DEEP>
@@ -1472,8 +1845,23 @@ hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
-                     p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes,
-                     scales, y_debug);
+                     p->c, p->p1_exp + p->p2_exp, p->c_absmax, p->clip,
+                     p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes, scales,
+                     y_debug);
+  return hipGetLastError();
+}
+
+template <int N1, int N2, int BITS = 4>
+hipError_t launch_colsc(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
+                        void *scales, float *y_debug, void *, hipStream_t stream) {
+  using C = ColsCCfg<N1, N2>;
+  const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
+  const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
+  auto k = y_debug ? &kq_colsc_kernel<N1, N2, true, BITS> : &kq_colsc_kernel<N1, N2, false, BITS>;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream, static_cast<const __bf16 *>(X), T,
+                     ldx, static_cast<const f16x8 *>(p->p2op), static_cast<const f16x8 *>(p->p1op),
+                     p->c, p->p1_exp + p->p2_exp, p->c_absmax, p->clip,
+                     p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
   return hipGetLastError();
 }
 
@@ -1525,7 +1913,7 @@ hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
   kq_fused_variant{A, B, HC, KQ_SPLIT_STREAM, 8, (B), StreamCfg<A, B, HC>::THREADS,       \
                    &launch_stream<A, B, HC, 8>,                                        \
                    reinterpret_cast<const void *>(&kq_stream_kernel<A, B, HC, false, 8>), \
-                   "fused_mfma_bf16_stream_" #A "x" #B SUF "_int8"}
+                   "fused_mfma_bf16_stream_" #A "x" #B SUF "_int8", nullptr, 0, 0, 0, (HC)}
 // rows of 112 values in the 128-column layout (hidden 7168 = 64 x 112)
 #define KQ_STREAM_P(A, B, BR)                                                          \
   kq_fused_variant{A, BR, false, KQ_SPLIT_STREAM, 4, (B), StreamCfg<A, B>::THREADS,         \
@@ -1536,7 +1924,16 @@ hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
   kq_fused_variant{A, B, true, KQ_SPLIT_STREAM, 4, (B), StreamCfg<A, B, true>::THREADS,     \
                    &launch_stream<A, B, true>,                                         \
                    reinterpret_cast<const void *>(&kq_stream_kernel<A, B, true, false>), \
-                   "fused_mfma_bf16_stream_" #A "x" #B "_c"}
+                   "fused_mfma_bf16_stream_" #A "x" #B "_c", nullptr, 0, 0, 0, true}
+// the column split with a per-channel scale (x^ rounded once, Z in fp16)
+#define KQ_COLSC(A, B)                                                                 \
+  kq_fused_variant{A, B, true, KQ_SPLIT_COLS, 4, 32, ColsCCfg<A, B>::THREADS, &launch_colsc<A, B>, \
+                   reinterpret_cast<const void *>(&kq_colsc_kernel<A, B>),            \
+                   "fused_mfma_bf16_cols_" #A "x" #B "_c", nullptr, 0, 0, 0, true}
+#define KQ_COLSC8(A, B)                                                                \
+  kq_fused_variant{A, B, true, KQ_SPLIT_COLS, 8, 32, ColsCCfg<A, B>::THREADS, &launch_colsc<A, B, 8>, \
+                   reinterpret_cast<const void *>(&kq_colsc_kernel<A, B, false, 8>),  \
+                   "fused_mfma_bf16_cols_" #A "x" #B "_c_int8", nullptr, 0, 0, 0, true}
 #define KQ_REG(A, B, WPT, HC, SUF)                                                     \
   kq_fused_variant{A, B, HC, WPT, 4, (B) / (WPT), kThreads, &launch_reg<A, B, WPT, HC, false>, \
                    reinterpret_cast<const void *>(&kq_reg_kernel<A, B, WPT, HC, false>), \
@@ -1555,7 +1952,7 @@ hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
                    "fused_mfma_bf16_cols_" #A "x" #B SUF "_int8"}
 #define KQ_ALL1(A, B)                                                                  \
   KQ_REG(A, B, 1, false, ""), KQ_REG(A, B, 1, true, "_c"), KQ_COLS(A, B, false, ""),    \
-      KQ_COLS(A, B, true, "_c")
+      KQ_COLSC(A, B)
 #define KQ_ALL(A, B)                                                                   \
   KQ_ALL1(A, B), KQ_REG(A, B, 2, false, ""), KQ_REG(A, B, 2, true, "_c")
 
@@ -1582,31 +1979,31 @@ const kq_fused_variant kVariants[] = {
     KQ_STREAM(16, 128),            KQ_REG(16, 128, 1, true, "_c"),
     KQ_STREAM(32, 128),            KQ_REG(32, 128, 1, true, "_c"),
     KQ_STREAM(48, 128),            KQ_REG(48, 128, 1, true, "_c"),
-    KQ_STREAM(64, 128),            KQ_COLS(64, 128, true, "_c"),
-    KQ_COLS(80, 128, false, ""),   KQ_COLS(80, 128, true, "_c"),
-    KQ_COLS(96, 128, false, ""),   KQ_COLS(96, 128, true, "_c"),
-    KQ_COLS(112, 128, false, ""),  KQ_COLS(112, 128, true, "_c"),
-    KQ_COLS(86, 128, false, ""),   KQ_COLS(86, 128, true, "_c"),   // 11008 (padded to 96)
-    KQ_COLS(108, 128, false, ""),  KQ_COLS(108, 128, true, "_c"),  // 13824 (padded to 112)
-    KQ_COLS(128, 128, false, ""),  KQ_COLS(128, 128, true, "_c"),
+    KQ_STREAM(64, 128),            KQ_COLSC(64, 128),
+    KQ_COLS(80, 128, false, ""),   KQ_COLSC(80, 128),
+    KQ_COLS(96, 128, false, ""),   KQ_COLSC(96, 128),
+    KQ_COLS(112, 128, false, ""),  KQ_COLSC(112, 128),
+    KQ_COLS(86, 128, false, ""),   KQ_COLSC(86, 128),   // 11008 (padded to 96)
+    KQ_COLS(108, 128, false, ""),  KQ_COLSC(108, 128),  // 13824 (padded to 112)
+    KQ_COLS(128, 128, false, ""),  KQ_COLSC(128, 128),
     // hidden sizes whose larger factor exceeds 128 (e.g. 28672 -> 128 x 224)
     KQ_COLS(128, 160, false, ""),  KQ_COLS(128, 192, false, ""),
     KQ_COLS(128, 224, false, ""),  KQ_COLS(128, 256, false, ""),
     // n2 not a multiple of 32, padded to one: the factors that minimise n1 + n2 for 1536
     // (32 x 48), 5120 (64 x 80), 7168 (64 x 112), 18432 (128 x 144), 6656 (64 x 104, n2 an
     // odd multiple of 8), and 3584 (56 x 64, n1 padded)
-    KQ_COLS(32, 48, false, ""),    KQ_COLS(32, 48, true, "_c"),
-    KQ_COLS(64, 80, false, ""),    KQ_COLS(64, 80, true, "_c"),
-    KQ_STREAM_P(64, 128, 112),     KQ_COLS(64, 112, false, ""),   KQ_COLS(64, 112, true, "_c"),
+    KQ_COLS(32, 48, false, ""),    KQ_COLSC(32, 48),
+    KQ_COLS(64, 80, false, ""),    KQ_COLSC(64, 80),
+    KQ_STREAM_P(64, 128, 112),     KQ_COLS(64, 112, false, ""),   KQ_COLSC(64, 112),
     KQ_COLS(128, 144, false, ""),
-    KQ_COLS(56, 64, false, ""),    KQ_COLS(56, 64, true, "_c"),
-    KQ_COLS(64, 104, false, ""),   KQ_COLS(64, 104, true, "_c"),
+    KQ_COLS(56, 64, false, ""),    KQ_COLSC(56, 64),
+    KQ_COLS(64, 104, false, ""),   KQ_COLSC(64, 104),
     // 2560 (40 x 64, n1 padded to 48), 5632 (64 x 88, n2 padded to 96), 6144 (64 x 96) and
     // 8960 (80 x 112, n2 padded to 128)
-    KQ_COLS(40, 64, false, ""),    KQ_COLS(40, 64, true, "_c"),
-    KQ_COLS(64, 88, false, ""),    KQ_COLS(64, 88, true, "_c"),
-    KQ_COLS(64, 96, false, ""),    KQ_COLS(64, 96, true, "_c"),
-    KQ_COLS(80, 112, false, ""),   KQ_COLS(80, 112, true, "_c"),
+    KQ_COLS(40, 64, false, ""),    KQ_COLSC(40, 64),
+    KQ_COLS(64, 88, false, ""),    KQ_COLSC(64, 88),
+    KQ_COLS(64, 96, false, ""),    KQ_COLSC(64, 96),
+    KQ_COLS(80, 112, false, ""),   KQ_COLSC(80, 112),
     // the other splits, selectable with KQ_FLAG_SPLIT_*
     KQ_ALL1(16, 32), KQ_ALL1(32, 32), KQ_ALL(16, 64), KQ_ALL(32, 64), KQ_ALL(48, 64),
     KQ_ALL(64, 64), KQ_ALL(16, 128), KQ_ALL(32, 128), KQ_ALL(48, 128), KQ_ALL(64, 128),
@@ -1621,25 +2018,25 @@ const kq_fused_variant kVariants[] = {
     KQ_STREAM8(64, 64, true, "_c"),
     // INT8 codes on the column kernel: the shapes where it is the default (n1 > 64, or
     // 64 x 128 with c), e.g. FFN down-projection inputs kept at 8 bits
-    KQ_COLS8(64, 128, true, "_c"),
-    KQ_COLS8(80, 128, false, ""),  KQ_COLS8(80, 128, true, "_c"),
-    KQ_COLS8(96, 128, false, ""),  KQ_COLS8(96, 128, true, "_c"),
-    KQ_COLS8(112, 128, false, ""), KQ_COLS8(112, 128, true, "_c"),
-    KQ_COLS8(86, 128, false, ""),  KQ_COLS8(86, 128, true, "_c"),
-    KQ_COLS8(108, 128, false, ""), KQ_COLS8(108, 128, true, "_c"),
-    KQ_COLS8(128, 128, false, ""), KQ_COLS8(128, 128, true, "_c"),
+    KQ_COLSC8(64, 128),
+    KQ_COLS8(80, 128, false, ""),  KQ_COLSC8(80, 128),
+    KQ_COLS8(96, 128, false, ""),  KQ_COLSC8(96, 128),
+    KQ_COLS8(112, 128, false, ""), KQ_COLSC8(112, 128),
+    KQ_COLS8(86, 128, false, ""),  KQ_COLSC8(86, 128),
+    KQ_COLS8(108, 128, false, ""), KQ_COLSC8(108, 128),
+    KQ_COLS8(128, 128, false, ""), KQ_COLSC8(128, 128),
     KQ_COLS8(128, 160, false, ""), KQ_COLS8(128, 192, false, ""),
     KQ_COLS8(128, 224, false, ""), KQ_COLS8(128, 256, false, ""),
-    KQ_COLS8(32, 48, false, ""),   KQ_COLS8(32, 48, true, "_c"),
-    KQ_COLS8(64, 80, false, ""),   KQ_COLS8(64, 80, true, "_c"),
-    KQ_COLS8(64, 112, false, ""),  KQ_COLS8(64, 112, true, "_c"),
+    KQ_COLS8(32, 48, false, ""),   KQ_COLSC8(32, 48),
+    KQ_COLS8(64, 80, false, ""),   KQ_COLSC8(64, 80),
+    KQ_COLS8(64, 112, false, ""),  KQ_COLSC8(64, 112),
     KQ_COLS8(128, 144, false, ""),
-    KQ_COLS8(56, 64, false, ""),   KQ_COLS8(56, 64, true, "_c"),
-    KQ_COLS8(64, 104, false, ""),  KQ_COLS8(64, 104, true, "_c"),
-    KQ_COLS8(40, 64, false, ""),   KQ_COLS8(40, 64, true, "_c"),
-    KQ_COLS8(64, 88, false, ""),   KQ_COLS8(64, 88, true, "_c"),
-    KQ_COLS8(64, 96, false, ""),   KQ_COLS8(64, 96, true, "_c"),
-    KQ_COLS8(80, 112, false, ""),  KQ_COLS8(80, 112, true, "_c"),
+    KQ_COLS8(56, 64, false, ""),   KQ_COLSC8(56, 64),
+    KQ_COLS8(64, 104, false, ""),  KQ_COLSC8(64, 104),
+    KQ_COLS8(40, 64, false, ""),   KQ_COLSC8(40, 64),
+    KQ_COLS8(64, 88, false, ""),   KQ_COLSC8(64, 88),
+    KQ_COLS8(64, 96, false, ""),   KQ_COLSC8(64, 96),
+    KQ_COLS8(80, 112, false, ""),  KQ_COLSC8(80, 112),
     KQ_STREAM(16, 128), KQ_STREAM(32, 128), KQ_STREAM(48, 128),
     KQ_PAIR(16, 64), KQ_PAIR(32, 64), KQ_PAIR(48, 64), KQ_PAIR(64, 64),
     KQ_PAIR(16, 128), KQ_PAIR(32, 128), KQ_PAIR(48, 128), KQ_PAIR(64, 128),

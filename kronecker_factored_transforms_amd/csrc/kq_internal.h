@@ -52,6 +52,9 @@ struct kq_plan {
   // 1: identity left factor and one step per row of V (T * n1 scales)
   int per_row;
   int bits;             // code width: 4 or 8
+  int p1_exp;           // fp16 operands (variants with f16_ops): P1 * 2^-p1_exp and
+  int p2_exp;           // P2 * 2^-p2_exp
+  float c_absmax;       // max |c| (the bound of a token's x c, with max |x|)
   // device workspace of the two-kernel designs for large factors: region A holds
   // ws_a_per_token bytes per token, region B (at a 256-byte aligned offset after A) holds
   // ws_b_per_token bytes per token; both 0 for the single-kernel designs
@@ -95,6 +98,9 @@ struct kq_fused_variant {
   int threads2;
   size_t ws_a_per_token;
   size_t ws_b_per_token;
+  // both contractions on fp16 operands: the plan stores P1's and P2's operands as fp16
+  // (scaled by 2^-p1_exp and 2^-p2_exp)
+  bool f16_ops;
 };
 
 // The variant for (n1, n2, has_c) with the given split (0: the default one) and code width,

@@ -45,9 +45,16 @@ def test_exact_factors_reproduce_permuted_input(gpu, name, kind):
     assert np.array_equal(K.np_scales(scales), os_)
 
 
-def test_power_of_two_channel_scale_is_exact(gpu):
-    """c = powers of two: x*c is exact in bf16, the low half of the split is zero, and the
-    identity-factor result is x*c exactly."""
+@pytest.mark.parametrize("flags,kernel", [(B.KQ_FLAG_SPLIT_REG1, "fused_mfma_bf16_reg1_64x64_c"),
+                                          (0, "fused_mfma_bf16_cols_64x64_c")])
+def test_power_of_two_channel_scale_is_exact(gpu, flags, kernel):
+    """c = powers of two with identity factors: x*c has x's 8 significant bits.
+    - The register kernels split x*c into bf16 hi + lo: lo is zero and Y is x*c exactly.
+    - The stream and column kernels run on fp16 operands after a per-token power-of-two
+      scale 2^s (s = 0 unless the bound max|x| max|c| leaves [2^-8, 2^15)): Y is x*c
+      exactly wherever fp16 holds x*c 2^s exactly (at or above 2^-17, where its subnormal
+      grid is still fine enough for 8 bits), and within half of fp16's smallest step 2^-25
+      (times 2^-s) below that."""
     wl = S.WORKLOADS["attn_n4096"]
     inp = S.make(wl, T=70)
     rng = np.random.default_rng(6)
@@ -55,22 +62,43 @@ def test_power_of_two_channel_scale_is_exact(gpu):
     import torch
     dP1 = _factor_tensor(np.eye(wl.n1), "bf16", gpu)
     dP2 = _factor_tensor(np.eye(wl.n2), "bf16", gpu)
-    plan, X = K.make_plan(inp, P1=dP1, P2=dP2, c=torch.from_numpy(c).to(gpu))
+    plan, X = K.make_plan(inp, P1=dP1, P2=dP2, c=torch.from_numpy(c).to(gpu), flags=flags)
+    assert plan.kernel_for(70) == kernel, plan.kernel_for(70)
     codes, scales, y = K.run(plan, X)
-    x = S.bf16_bits_to_f32(inp.X).astype(np.float64) * c.astype(np.float64)
-    assert np.array_equal(y.cpu().numpy(), x.astype(np.float32))
+    xf = S.bf16_bits_to_f32(inp.X).astype(np.float64)
+    x = xf * c.astype(np.float64)
+    yc = y.cpu().numpy().astype(np.float64)
+    if flags:
+        assert np.array_equal(yc, x)
+    else:
+        bound = (np.abs(xf).max(axis=1).astype(np.float32) * np.float32(np.abs(c).max())).astype(np.float64)
+        e = np.floor(np.log2(bound))
+        s = np.where((e >= -8) & (e < 15), 0.0, np.clip(14 - e, -126, 127))[:, None]
+        big = np.abs(x) * 2.0 ** s >= 2.0 ** -17
+        assert big.mean() > 0.999
+        assert np.array_equal(yc[big], x[big])
+        assert np.all(np.abs(yc - x)[~big] <= (2.0 ** (-25 - s) * np.ones_like(x))[~big])
     K.assert_quant_bit_exact(codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(), plan.clip, "fp16")
 
 
-def test_c_of_ones_equals_no_c(gpu):
+@pytest.mark.parametrize("name", ["hidden_n8192", "attn_n4096"])
+def test_c_of_ones_matches_no_c(gpu, name):
+    """c = ones gives x^ = x exactly; the with-c kernels then differ from the plain ones only
+    in carrying Z in fp16 (instead of bf16) to stage 2. Both match the oracle, and their
+    codes agree except for values that sit near a rounding boundary (at most one step)."""
     import torch
-    inp = S.make("hidden_n8192", T=200)
+    inp = S.make(replace(S.WORKLOADS[name], c_kind=None), T=200)
     p0, X = K.make_plan(inp, c=None)
     p1, _ = K.make_plan(inp, c=torch.ones(inp.wl.n, dtype=torch.float32, device=gpu))
     assert p1.kernel.endswith("_c") and not p0.kernel.endswith("_c")
     a = K.run(p0, X)
     b = K.run(p1, X)
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2].abs(), b[2].abs())
+    for codes, scales, y in (a, b):
+        K.check_against_oracle(inp, codes.cpu().numpy(), K.np_scales(scales), y.cpu().numpy(),
+                               p0.clip)
+    qa = O.unpack_int4(a[0].cpu().numpy()).astype(int)
+    qb = O.unpack_int4(b[0].cpu().numpy()).astype(int)
+    assert np.abs(qa - qb).max() <= 1 and np.mean(qa != qb) < 0.02
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 63, 65, 127, 1025])
@@ -338,9 +366,40 @@ def test_fp32_step_with_overflowing_reciprocal_is_an_underflow(gpu, name, T, fla
     assert plan.kernel_for(T) == kernel, plan.kernel_for(T)
     codes, scales, y = K.run(plan, X)
     yc = y.cpu().numpy()
-    assert np.array_equal(yc, x)                   # identity factors: exact
+    special = tiny + [1]                           # powers of two: exact on every kernel
+    assert np.array_equal(yc[special], x[special])
+    # identity factors: the other tokens are exact too, except on the fp16-operand kernels
+    # (the with-c stream and column kernels) for values below fp16's 2^-17, which round to
+    # its subnormal grid (half-step 2^-25)
+    assert np.max(np.abs(yc.astype(np.float64) - x)) <= 2.0 ** -25
     K.assert_quant_bit_exact(codes.cpu().numpy(), K.np_scales(scales), yc, plan.clip, "fp32")
     s = K.np_scales(scales)
     cn = codes.cpu().numpy()
     assert np.all(s[tiny] == 0) and np.all(cn[tiny] == 0)
     assert s[1] > 0 and np.any(cn[1] != 0)
+
+
+# The with-c stream and column kernels carry Z to stage 2 in fp16 after a per-token
+# power-of-two scale chosen from the token's largest |Z|; tokens far outside fp16's range
+# (times 2^40 or 2^-60) take the scaled path, ordinary ones the unscaled one. Every token
+# must still match the oracle, and both kernels of a plan give the same codes.
+@pytest.mark.parametrize("name,T,kernel", [
+    ("attn_n4096", 1100, "fused_mfma_bf16_stream_64x64_c"),
+    ("attn_n4096", 300, "fused_mfma_bf16_cols_64x64_c"),
+    ("down_proj_n14336", 301, "fused_mfma_bf16_cols_112x128_c"),
+    ("ffn_n11008", 203, "fused_mfma_bf16_cols_86x128_c")])
+def test_with_c_kernels_scale_z_into_fp16_range(gpu, name, T, kernel):
+    import torch
+    inp = S.make(name, T=T)
+    x = O.bf16_bits_to_f64(inp.X)
+    for i, k in enumerate((40, -60, 20, -30)):
+        x[i::7] *= 2.0 ** k        # tokens 0, 7, 14, ... times 2^40; 1, 8, ... times 2^-60
+    inp.X = S.to_bf16_bits(x)
+    plan, X = K.make_plan(inp)
+    assert plan.kernel_for(T) == kernel, plan.kernel_for(T)
+    codes, scales, y = K.run(plan, X)
+    K.check_plan_against_oracle(inp, plan, codes, scales, y)
+    if name == "attn_n4096" and T > 1024:   # the small-batch split writes the same codes
+        c2, s2 = K.run(plan, X[:1000], y_debug=False)
+        assert plan.kernel_for(1000) == "fused_mfma_bf16_cols_64x64_c"
+        assert torch.equal(c2, codes[:1000]) and torch.equal(s2, scales[:1000])

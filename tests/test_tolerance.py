@@ -1,15 +1,19 @@
 """Feasibility of the bf16 tolerance, on the CPU.
 
-The bf16 path multiplies bf16 operands with fp32 accumulation in both stages, rounds the
-stage-1 result Z to bf16 to feed stage 2, and with a per-channel scale splits
-x_hat = fp32(x c) into bf16 hi + lo words. This file emulates exactly those roundings in
-numpy (the accumulation order inside an MFMA aside) and compares the result with the
-fp64 oracle on every bf16 workload:
+The bf16 path multiplies bf16 operands with fp32 accumulation in both stages. Without a
+per-channel scale it rounds the stage-1 result Z to bf16 to feed stage 2. With one, the
+stream and column kernels run both stages on fp16 operands: x_hat = fp32(x c) rounded to
+fp16 after a per-token power-of-two scale (from the bound max|x| max|c|), P2 and P1 as
+fp16, and Z rounded to fp16 after a second per-token power-of-two scale (from max|Z|);
+the register and large-factor kernels split x_hat into bf16 hi + lo words and keep Z in
+bf16. This file emulates exactly those roundings in numpy (the accumulation order inside
+an MFMA aside) and compares the result with the fp64 oracle on every bf16 workload:
 
-- the emulated pipeline stays inside the 2e-3 relative-L2 gate with margin, so the gate
+- every emulated pipeline stays inside the 2e-3 relative-L2 gate with margin, so the gate
   is one the design can meet and not one a kernel passes by luck;
-- rounding x_hat once to bf16 instead of splitting it would not meet the gate on the
-  workloads with a per-channel scale, which is why the path splits it.
+- with a per-channel scale, one bf16 rounding of x_hat on top of a bf16 Z would not meet
+  the gate, which is why each with-c design avoids it (the hi/lo split, or fp16 operands,
+  which also keep every single token well inside the gate).
 """
 import numpy as np
 import pytest
@@ -26,7 +30,36 @@ def _bf16(a64):
     return O.bf16_bits_to_f64(S.to_bf16_bits(a64))
 
 
-def _emulate(inp, split_c=True):
+def _fp16(a64):
+    return np.asarray(a64, np.float64).astype(np.float32).astype(np.float16).astype(np.float64)
+
+
+def _f16_scale(bound):
+    """Per-token exponent s: 0 when the bound lies in [2^-8, 2^15), else the one that puts
+    it in [2^14, 2^15) (clamped to [-126, 127])."""
+    e = np.floor(np.log2(np.where(bound > 0, bound, 1.0)))
+    s = np.where((e >= -8) & (e < 15) & (bound > 0), 0.0, np.clip(14 - e, -126, 127))
+    return 2.0 ** s
+
+
+def _emulate_f16(inp):
+    """The stream and column kernels with a per-channel scale: fp16 operands."""
+    wl = inp.wl
+    X = O.bf16_bits_to_f64(inp.X)
+    T = X.shape[0]
+    xh = (X.astype(np.float32) * inp.c.astype(np.float32)).astype(np.float32).astype(np.float64)
+    bound = (np.abs(X).max(axis=1).astype(np.float32) * np.float32(np.abs(inp.c).max())).astype(np.float64)
+    sx = _f16_scale(bound)[:, None]
+    A = _fp16(xh * sx) / sx
+    P1 = O.bf16_bits_to_f64(inp.P1)
+    P2 = O.bf16_bits_to_f64(inp.P2)
+    Z = (A.reshape(T, wl.n1, wl.n2) @ _fp16(P2)).astype(np.float32).astype(np.float64)
+    sz = _f16_scale(np.abs(Z).reshape(T, -1).max(axis=1))[:, None, None]
+    Y = np.einsum("ji,tjk->tik", _fp16(P1), _fp16(Z * sz)) / sz
+    return Y.astype(np.float32).astype(np.float64).reshape(T, -1)
+
+
+def _emulate(inp, split_c=True, z_fp16=False):
     wl = inp.wl
     X = O.bf16_bits_to_f64(inp.X)
     if inp.c is not None:
@@ -41,7 +74,16 @@ def _emulate(inp, split_c=True):
     P1 = O.bf16_bits_to_f64(inp.P1)
     P2 = O.bf16_bits_to_f64(inp.P2)
     Z = (A.reshape(T, wl.n1, wl.n2) @ P2).astype(np.float32).astype(np.float64)
-    Y = np.einsum("ji,tjk->tik", P1, _bf16(Z))  # P1^T Z
+    if z_fp16:
+        # the token's |Z| maximum picks 2^s (s = 0 when it lies in [2^-8, 2^15)); Z * 2^s
+        # and P1 round to fp16, and the scale is undone exactly on Y
+        zmax = np.abs(Z).reshape(T, -1).max(axis=1)
+        e = np.floor(np.log2(np.where(zmax > 0, zmax, 1.0)))
+        s = np.where((e >= -8) & (e < 15), 0.0, np.clip(14 - e, -126, 127))
+        sc = (2.0 ** s)[:, None, None]
+        Y = np.einsum("ji,tjk->tik", _fp16(P1), _fp16(Z * sc)) / sc
+    else:
+        Y = np.einsum("ji,tjk->tik", P1, _bf16(Z))  # P1^T Z
     return Y.astype(np.float32).astype(np.float64).reshape(T, -1)
 
 
@@ -58,11 +100,42 @@ def test_bf16_pipeline_meets_the_gate_with_margin(name):
     assert 1.2e-3 < rel < 0.9 * GATE, f"{name}: {rel:.3e}"
 
 
-@pytest.mark.parametrize("name", ["attn_n4096", "down_proj_n14336"])
-def test_per_channel_scale_needs_the_hi_lo_split(name):
+@pytest.mark.parametrize("name", ["attn_n4096", "down_proj_n14336", "ffn_n11008"])
+def test_per_channel_scale_designs(name):
+    """With c: the hi/lo split (register kernels) and the fp16 operands (stream and column
+    kernels) both meet the gate; one bf16 rounding of x_hat on a bf16 Z would not."""
     inp = S.make(name, T=64)
     assert inp.c is not None
     Y = O.transform(inp.X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
     split = _rel(_emulate(inp, split_c=True), Y)
+    f16 = _rel(_emulate_f16(inp), Y)
     single = _rel(_emulate(inp, split_c=False), Y)
-    assert split < 0.9 * GATE < GATE < single, (split, single)
+    assert split < 0.9 * GATE and f16 < 0.25 * GATE and GATE < single, (split, f16, single)
+
+
+@pytest.mark.parametrize("n1,n2", [(16, 64), (64, 64), (112, 128)])
+def test_fp16_operands_keep_every_token_inside_the_gate(n1, n2):
+    """Tokens dominated by a few outlier channels: their own relative error is a sample of
+    few roundings. With fp16 operands every one of 256 such tokens stays well inside the
+    gate (with bf16 operands about a fifth of the 16 x 64 ones would not)."""
+    from dataclasses import replace
+    wl = replace(S.WORKLOADS["attn_n4096"], n1=n1, n2=n2, n_outliers=4, pivot_channels=0)
+    inp = S.make(wl, T=256)
+    Y = O.transform(inp.X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
+    E = _emulate_f16(inp)
+    per = np.linalg.norm(E - Y, axis=1) / np.linalg.norm(Y, axis=1)
+    assert per.max() < 0.5 * GATE, per.max()
+
+
+@pytest.mark.parametrize("name", ["attn_n4096", "down_proj_n14336"])
+def test_fp16_scales_keep_extreme_tokens_in_range(name):
+    """Tokens far outside fp16's range (x 2^40, x 2^-60) give the same relative error as the
+    unscaled tokens: the power-of-two scales move x_hat and Z into range and back exactly."""
+    inp = S.make(name, T=16)
+    Y = O.transform(inp.X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
+    base = _rel(_emulate_f16(inp), Y)
+    for k in (40, -60):
+        big = S.make(name, T=16)
+        big.X = S.to_bf16_bits(O.bf16_bits_to_f64(inp.X) * 2.0 ** k)
+        Yb = O.transform(big.X, big.P1, big.P2, big.c, big.wl.dtype)
+        assert abs(_rel(_emulate_f16(big), Yb) - base) < 1e-4
