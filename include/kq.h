@@ -94,13 +94,15 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
 /* KQ_FLAG_INT8: INT8 codes instead of INT4 ("FlatQuant" page, How we know: beyond dense
  * W4A4 -- mixed precision, where some layers run at W8A8): step
  * s32 = fp32(fp32(clip * a) / 127), q = clamp(rint(fp32(y * inv)), -128, 127), one
- * two's-complement byte per value, so `codes` holds T x n bytes (row stride n). bf16 plans of the stream kernel's shapes: n2 in {64, 128} with n1 in
- * {16, 32, 48, 64}, without c, or n2 = 64 with c; of the column kernel's shapes: n2 = 128
- * with n1 in {80, 86, 96, 108, 112, 128}, with or without c, 64 x 128 with c, n1 = 128
- * with n2 in {144, 160, 192, 224, 256} without c, and 32 x 48, 56 x 64, 64 x 80, 64 x 104,
- * 64 x 112 with or without c; and per-row plans (KQ_FLAG_PER_ROW, one
- * step per row of n2 values) with n2 in {64, 128} (KQ_ERR_UNSUPPORTED otherwise); not with
- * KQ_FLAG_FORCE_GENERIC. */
+ * two's-complement byte per value, so `codes` holds T x n bytes (row stride n). bf16
+ * plans of the stream kernel's shapes: n2 in {64, 128} with n1 in {16, 32, 48, 64},
+ * without c, or n2 = 64 with c; of the column kernel's shapes: n2 = 128 with n1 in {80,
+ * 86, 96, 108, 112, 128}, with or without c, 64 x 128 with c, n1 = 128 with n2 in {144,
+ * 160, 192, 224, 256} without c, and 32 x 48, 40 x 64, 56 x 64, 64 x 80, 64 x 88,
+ * 64 x 96, 64 x 104, 64 x 112, 80 x 112 with or without c; and per-row plans
+ * (KQ_FLAG_PER_ROW, one step per row of n2 values) with n2 in {64, 128}
+ * (KQ_ERR_UNSUPPORTED otherwise, including the two-kernel designs and the fp32 MFMA
+ * kernel); not with KQ_FLAG_FORCE_GENERIC. */
 #define KQ_FLAG_INT8 0x800u
 
 /*
@@ -134,16 +136,20 @@ kq_status kq_create(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype sc
                     void *stream);
 
 /* Shapes with a kernel (anything else: KQ_ERR_UNSUPPORTED from kq_create):
- *   bf16, bf16 MFMA kernels, with or without c: n2 = 32 with n1 in {16, 32}; n2 = 64
- *     with n1 in {16, 32, 48, 64}; n2 = 128 with n1 in {16, 32, ..., 128}, and with
- *     n1 in {86, 108} (hidden sizes 11008 and 13824; P1 is zero-padded to whole 16-row
- *     tiles inside the plan, results are unchanged). Without c
- *     also n1 = 128 with n2 in {160, 192, 224, 256} (hidden sizes 20480 ... 32768, e.g.
- *     28672 = 128 x 224). n2 not a multiple of 32, padded with zero columns inside the
- *     plan: 32 x 48, 64 x 80, 64 x 104 and 64 x 112 with or without c, 128 x 144 without
- *     c (the factors kq_choose_factors gives for 1536, 5120, 6656, 7168 and 18432); and
- *     56 x 64 with or without c (3584, n1 padded).
- *   fp32 (and bf16 shapes not listed above): the generic fp32 kernel, n <= 16384.
+ *   bf16 on the single-kernel MFMA designs ("FlatQuant" page, Deep Dive: The fused kernel,
+ *     Figure 8(a)), with or without c: n2 = 32 with n1 in {16, 32}; n2 = 64 with n1 in
+ *     {16, 32, 40, 48, 56, 64}; n2 = 128 with n1 in {16, 32, 48, 64, 80, 86, 96, 108, 112,
+ *     128}; and 32 x 48, 64 x 80, 64 x 88, 64 x 96, 64 x 104, 64 x 112, 80 x 112. Factors
+ *     that are not whole MFMA tiles are zero-padded inside the plan (results unchanged).
+ *     Without c also n1 = 128 with n2 in {144, 160, 192, 224, 256}.
+ *   bf16 on the two-kernel designs for factors beyond one CU's on-chip memory (Figure 8(b)
+ *     and 8(c); these need a workspace, see kq_workspace_size): 160 x 160, 144 x 192,
+ *     168 x 176, 208 x 256 and 256 x 256 with or without c, and 128 x n2 with c for n2 in
+ *     {160, 192, 224, 256}.
+ *   fp32 on the MFMA kernel (each value as a bf16 hi + lo pair, three products, Z in
+ *     fp32): n2 = 64 with n1 in {16, 32, 48, 64}, without c.
+ *   Every other fp32 shape, and bf16 shapes not listed above: the generic fp32 kernel,
+ *     n <= 16384.
  */
 
 /* kq_create with flags (KQ_FLAG_*); kq_create(...) == kq_create_ex(..., 0). */

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -181,7 +183,9 @@ __device__ __forceinline__ uint32_t absmax_bf16(const uint4 &raw, uint32_t m) {
 
 // x (8 bf16) * c (8 fp32) in fp32, scaled by 2^s (exact for normal results), rounded once
 // to fp16 (round to nearest even): the stage-1 operand of the kernels that run both
-// contractions on fp16 operands
+// contractions on fp16 operands. SCALE = false is the s = 0 case (no ldexp); callers pick
+// it with a wave-uniform branch, since ordinary tokens need no scaling.
+template <bool SCALE = true>
 __device__ __forceinline__ f16x8 scale_round_f16(const uint4 &raw, const float *c, int s) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   f16x8 r;
@@ -189,7 +193,7 @@ __device__ __forceinline__ f16x8 scale_round_f16(const uint4 &raw, const float *
   for (int e = 0; e < 4; ++e) {
     float s0 = __fmul_rn(__uint_as_float(w[e] << 16), c[2 * e]);
     float s1 = __fmul_rn(__uint_as_float(w[e] & 0xFFFF0000u), c[2 * e + 1]);
-    if (s != 0) {
+    if constexpr (SCALE) {
       s0 = __builtin_ldexpf(s0, s);
       s1 = __builtin_ldexpf(s1, s);
     }
@@ -197,6 +201,34 @@ __device__ __forceinline__ f16x8 scale_round_f16(const uint4 &raw, const float *
     r[2 * e + 1] = (_Float16)s1;
   }
   return r;
+}
+
+// largest |v| over a run of accumulators (and m). Written as one running chain
+// m = max(m, |v|): the compiler then pairs the steps into v_max3_f32 with absolute-value
+// modifiers (two values per instruction). Nested as max(m, max(|a|, |b|)) it first
+// canonicalizes every MFMA result with an extra v_max_f32.
+template <int K>
+__device__ __forceinline__ float absmax_acc(const f32x4 (&v)[K], float m) {
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(v[k][r]));
+  return m;
+}
+
+// The quantizer's reciprocal for Y = Y' 2^ty, applied to Y' directly. With t = 2^ty,
+// fp32(Y' * fp32(inv t)) equals fp32(fp32(Y' t) * inv) whenever both scalings are exact,
+// since both then round the same real product: inv t must be normal (checked by scaling
+// back) or inv = 0, and every nonzero Y' t must be a normal, finite fp32. The latter holds
+// when amax = max|Y'| t is finite and ty >= -78: each nonzero |Y'| is at least 2^-48 (a
+// sum of products of fp16 values, all multiples of 2^-24, accumulated in fp32). Returns
+// false when the kernel has to scale Y itself.
+__device__ __forceinline__ bool fold_scale(float inv, int ty, float amax, float &inv_y) {
+  inv_y = __builtin_ldexpf(inv, ty);
+  if (ty < -78 || !__builtin_isfinite(amax)) return false;
+  if (inv == 0.f) return true;
+  return __builtin_isfinite(inv_y) && inv_y >= 1.17549435e-38f &&
+         __builtin_ldexpf(inv_y, -ty) == inv;
 }
 
 // Power-of-two exponent s that brings a token's values into fp16's range before the

@@ -437,6 +437,7 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
     constexpr int NH = C::NT / 2;  // column tiles per half
     f32x4 yacc[C::NT][C::MT];
     float pm[C::NT];
+    int ty = 0;  // with c: Y = yacc 2^ty
     if constexpr (HAS_C) {
       // ---- the token's x, its bound max|x| max|c| and the scale of x^ ----
       uint4 raw[C::KS][C::MT];
@@ -458,34 +459,36 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) zacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // sx is wave-uniform: tokens that need no scaling (the usual case) take the
+      // branch without the ldexp
+      auto stage1 = [&](auto scale) {
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        f16x8 av[C::MT];
+        for (int ks = 0; ks < C::KS; ++ks) {
+          f16x8 av[C::MT];
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-          const unsigned char *crow = s_c + (mt * 16 + lr) * (N2 * 4);
-          const int u0 = (ks * 4 + g) * 2;
-          const float4 c0 = *reinterpret_cast<const float4 *>(crow + ((u0 ^ lr) * 16));
-          const float4 c1 = *reinterpret_cast<const float4 *>(crow + (((u0 + 1) ^ lr) * 16));
-          const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-          av[mt] = scale_round_f16(raw[ks][mt], cc, sx);
+          for (int mt = 0; mt < C::MT; ++mt) {
+            const unsigned char *crow = s_c + (mt * 16 + lr) * (N2 * 4);
+            const int u0 = (ks * 4 + g) * 2;
+            const float4 c0 = *reinterpret_cast<const float4 *>(crow + ((u0 ^ lr) * 16));
+            const float4 c1 = *reinterpret_cast<const float4 *>(crow + (((u0 + 1) ^ lr) * 16));
+            const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            av[mt] = scale_round_f16<decltype(scale)::value>(raw[ks][mt], cc, sx);
+          }
+#pragma unroll
+          for (int nt = 0; nt < C::NT; ++nt) {
+            const f16x8 bv = reinterpret_cast<const f16x8 *>(sp2)[(ks * C::NT + nt) * 64 + lane];
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt) zacc[mt][nt] = mfma_f16(av[mt], bv, zacc[mt][nt]);
+          }
         }
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) {
-          const f16x8 bv = reinterpret_cast<const f16x8 *>(sp2)[(ks * C::NT + nt) * 64 + lane];
-#pragma unroll
-          for (int mt = 0; mt < C::MT; ++mt) zacc[mt][nt] = mfma_f16(av[mt], bv, zacc[mt][nt]);
-        }
-      }
+      };
+      if (sx == 0) stage1(std::false_type{});
+      else stage1(std::true_type{});
       wait_and_fence<kWaitLgkm0>();  // every slot read has returned: the slot is free again
       if (tok + stride < T) dma_tile(tok + stride);
       float zm = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) zm = fmaxf(zm, fabsf(zacc[mt][nt][r]));
+      for (int mt = 0; mt < C::MT; ++mt) zm = absmax_acc(zacc[mt], zm);
       const int zs = __builtin_amdgcn_readfirstlane(f16_scale_exp(wave_max_uniform(zm)));
       // ---- stage 2 on fp16 operands: Y^T = Z^T P1 ----
 #pragma unroll
@@ -507,23 +510,10 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
           for (int m2 = 0; m2 < C::NT; ++m2) yacc[m2][nt] = mfma_f16(za[m2], b, yacc[m2][nt]);
         }
       }
-      const int ty = f_exp - sx - zs;  // Y = Y' 2^(f1 + f2 - sx - sz), exact
-      if (ty != 0) {
+      ty = f_exp - sx - zs;  // Y = Y' 2^(f1 + f2 - sx - sz), exact
+      // maxima of |Y'|: ldexp is monotone, so max|Y| is the scaled maximum
 #pragma unroll
-        for (int m2 = 0; m2 < C::NT; ++m2)
-#pragma unroll
-          for (int nt = 0; nt < C::MT; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yacc[m2][nt][r] = __builtin_ldexpf(yacc[m2][nt][r], ty);
-      }
-#pragma unroll
-      for (int m2 = 0; m2 < C::NT; ++m2) {
-        pm[m2] = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < C::MT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pm[m2] = fmaxf(pm[m2], fabsf(yacc[m2][nt][r]));
-      }
+      for (int m2 = 0; m2 < C::NT; ++m2) pm[m2] = absmax_acc(yacc[m2], 0.f);
     } else {
     // ---- stages 1 and 2 per half of the output columns ----
     // A column tile of Y needs only the same column tile of Z, so each half runs stage 1
@@ -579,13 +569,7 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
             yacc[h * NH + m2][nt] = mfma(za[kk][m2], p1r[kk][nt], yacc[h * NH + m2][nt]);
       // partial absmax of this half (independent chains, one per column tile)
 #pragma unroll
-      for (int m2 = h * NH; m2 < (h + 1) * NH; ++m2) {
-        pm[m2] = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < C::MT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pm[m2] = fmaxf(pm[m2], fabsf(yacc[m2][nt][r]));
-      }
+      for (int m2 = h * NH; m2 < (h + 1) * NH; ++m2) pm[m2] = absmax_acc(yacc[m2], 0.f);
     }
     }  // !HAS_C
 
@@ -594,18 +578,33 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 #pragma unroll
     for (int w = C::NT / 2; w >= 1; w /= 2)
 #pragma unroll
-      for (int i = 0; i < w; ++i) pm[i] = fmaxf(pm[i], pm[i + w]);
+      for (int i = 0; i < w; ++i) pm[i] = max_nn(pm[i], pm[i + w]);
     const float m = pm[0];
     // the absmax and the clamp decision are wave-uniform: broadcast them so that the
     // choice below is one scalar branch, not a per-lane select
-    const float amax = wave_max_uniform(m);
+    const float amax = HAS_C ? __builtin_ldexpf(wave_max_uniform(m), ty) : wave_max_uniform(m);
     const TokenScale ts = token_scale(amax, clip, scale_fp16, BITS == 4 ? 7.0f : 127.0f);
+    // with c: codes straight from Y' with the reciprocal scaled by 2^ty where that is
+    // exact, else from Y = ldexp(Y', ty) (then ty = 0: yacc holds Y)
+    float inv = ts.inv;
+    if constexpr (HAS_C) {
+      if (!__builtin_amdgcn_readfirstlane(fold_scale(ts.inv, ty, amax, inv) ? 1 : 0)) {
+#pragma unroll
+        for (int m2 = 0; m2 < C::NT; ++m2)
+#pragma unroll
+          for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[m2][nt][r] = __builtin_ldexpf(yacc[m2][nt][r], ty);
+        inv = ts.inv;
+        ty = 0;
+      }
+    }
     if constexpr (BITS == 8) {
-      quant_tile8<C::MT, C::NT>(yacc, ts.inv, pend);
+      quant_tile8<C::MT, C::NT>(yacc, inv, pend);
     } else if (__builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, ts.s32) ? 1 : 0)) {
-      quant_tile<true, C::MT, C::NT>(yacc, ts.inv, pend);
+      quant_tile<true, C::MT, C::NT>(yacc, inv, pend);
     } else {
-      quant_tile<false, C::MT, C::NT>(yacc, ts.inv, pend);
+      quant_tile<false, C::MT, C::NT>(yacc, inv, pend);
     }
     pend_s = ts;
     pend_tok = tok;
@@ -616,7 +615,8 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 #pragma unroll
         for (int m2 = 0; m2 < C::NT; ++m2)
           if (g * C::LPL + 4 * m2 < N2R)  // padded columns are not written
-            yp[m2] = make_float4(yacc[m2][nt][0], yacc[m2][nt][1], yacc[m2][nt][2], yacc[m2][nt][3]);
+            yp[m2] = make_float4(__builtin_ldexpf(yacc[m2][nt][0], ty), __builtin_ldexpf(yacc[m2][nt][1], ty),
+                                 __builtin_ldexpf(yacc[m2][nt][2], ty), __builtin_ldexpf(yacc[m2][nt][3], ty));
       }
     }
   }
@@ -1561,7 +1561,8 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const f16x8 *__restrict__ p2op, const f16x8 *__restrict__ p1op,
     const float *__restrict__ cvec, int f_exp, float cmax, float clip, int scale_fp16,
-    uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
+    int clip_allows_no_clamp, uint8_t *__restrict__ codes, void *__restrict__ scales,
+    float *__restrict__ ydbg) {
   using C = ColsCCfg<N1, N2>;
   constexpr int n = N1 * N2;
   __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
@@ -1647,19 +1648,28 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
       sx[sl] = __builtin_amdgcn_readfirstlane(f16_scale_exp(__fmul_rn(v, cmax)));
     }
   };
+  // x^ of the loaded chunks into the tile. The scales are wave-uniform, so tokens that
+  // need none (the usual case) take the branch without the ldexp.
   auto store_lds = [&](const int (&sx)[C::TPI]) {
+    auto store = [&](auto scale) {
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      if (!c_ok[i]) continue;
-      int s = sx[0];
+      for (int i = 0; i < C::CPT; ++i) {
+        if (!c_ok[i]) continue;
+        int s = sx[0];
 #pragma unroll
-      for (int sl = 1; sl < C::TPI; ++sl) s = c_ts[i] == sl ? sx[sl] : s;
-      const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
-      const float4 a = cp[0], b = cp[1];
-      const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      *reinterpret_cast<f16x8 *>(s_v + c_ts[i] * C::V_BYTES + vchunk_off<C::CHP>(c_row[i], c_cc[i])) =
-          scale_round_f16(pre[i], cl, s);
-    }
+        for (int sl = 1; sl < C::TPI; ++sl) s = c_ts[i] == sl ? sx[sl] : s;
+        const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
+        const float4 a = cp[0], b = cp[1];
+        const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        *reinterpret_cast<f16x8 *>(s_v + c_ts[i] * C::V_BYTES + vchunk_off<C::CHP>(c_row[i], c_cc[i])) =
+            scale_round_f16<decltype(scale)::value>(pre[i], cl, s);
+      }
+    };
+    int any = 0;
+#pragma unroll
+    for (int sl = 0; sl < C::TPI; ++sl) any |= sx[sl];
+    if (any == 0) store(std::false_type{});
+    else store(std::true_type{});
   };
   f16x8 p2w[C::KS][2];
 #pragma unroll
@@ -1700,9 +1710,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
       }
     float zm = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) zm = fmaxf(zm, fmaxf(fabsf(zacc[mt][0][r]), fabsf(zacc[mt][1][r])));
+    for (int mt = 0; mt < C::MT; ++mt) zm = absmax_acc(zacc[mt], zm);
     zm = wave_max_uniform(zm);
     if (lane == 0) s_zmax[it & 1][wave] = zm;
     if (nxt < ngroups) publish_xmax(it & 1);  // the next token's chunks, loaded a token ago
@@ -1739,14 +1747,6 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
         yacc[0][nt] = mfma_f16(za[kk][0], b, yacc[0][nt]);
         yacc[1][nt] = mfma_f16(za[kk][1], b, yacc[1][nt]);
       }
-    if (ty != 0) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int nt = 0; nt < C::MT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) yacc[h][nt][r] = __builtin_ldexpf(yacc[h][nt][r], ty);
-    }
     if (nxt < ngroups) {  // the next token's scale, for the next iteration
       sx_tok = sx[0];
 #pragma unroll
@@ -1754,47 +1754,70 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
     }
 
     // ---- epilogue: absmax over the token, then codes ----
+    // The maxima are those of Y' (Y = Y' 2^ty); ldexp is monotone, so max|Y| is the
+    // scaled maximum.
     float m = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int nt = 0; nt < C::MT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[h][nt][r]));
+    for (int h = 0; h < 2; ++h) m = absmax_acc(yacc[h], m);
     m = wave_max_uniform(m);
     if (lane == 0) s_red[it & 1][wave] = m;
     lds_barrier();  // (B) the next tile is stored; the |Y| maxima are published
-    float amax = 0.f;
+    float amax_y = 0.f;
 #pragma unroll
-    for (int w = 0; w < C::W; ++w) amax = fmaxf(amax, s_red[it & 1][ts * C::W + w]);
+    for (int w = 0; w < C::W; ++w) amax_y = max_nn(amax_y, s_red[it & 1][ts * C::W + w]);
+    const float amax = __builtin_ldexpf(amax_y, ty);
     const TokenScale sc = token_scale(amax, clip, scale_fp16, BITS == 4 ? 7.0f : 127.0f);
+    // codes straight from Y' with the reciprocal scaled by 2^ty where that is exact, else
+    // from Y = ldexp(Y', ty) (then ty_dbg = 0: yacc holds Y)
+    float inv_y;
+    int ty_dbg = ty;
+    if (!__builtin_amdgcn_readfirstlane(fold_scale(sc.inv, ty, amax, inv_y) ? 1 : 0)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nt = 0; nt < C::MT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yacc[h][nt][r] = __builtin_ldexpf(yacc[h][nt][r], ty);
+      inv_y = sc.inv;
+      ty_dbg = 0;
+    }
+    const bool clamp = BITS == 8 || __builtin_amdgcn_readfirstlane(
+                                        clamp_needed(clip_allows_no_clamp, sc.s32) ? 1 : 0);
 
     if (tok < T) {
       // lane holds Y[j = nt*16 + lr][wt*32 + 8g + 4h + r]
       constexpr int RB = N2 * BITS / 8;
       uint8_t *crow = codes + tok * (int64_t)(n * BITS / 8);
       const uint32_t loff = (uint32_t)(lr * RB + (wt * 32 + g * 8) * BITS / 8);
+      // one scalar branch on the clamp for the whole tile
+      auto emit = [&](auto clamp_tag) {
 #pragma unroll
-      for (int nt = 0; nt < C::MT; ++nt) {
-        const int j = nt * 16 + lr;
-        if (C::PADDED && j >= N1) continue;
-        if (C::PADC && wt * 32 + g * 8 >= N2) continue;
-        uint8_t *dst = crow + (loff + (uint32_t)(nt * 16 * RB));
-        if constexpr (BITS == 8) {
-          const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], sc.inv),
-                             quant4x8(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3], sc.inv)};
-          *reinterpret_cast<u32x2_t *>(dst) = w;
-        } else {
-          const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
-                               yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
-          *reinterpret_cast<uint32_t *>(dst) = quant8(yv, sc.inv);
+        for (int nt = 0; nt < C::MT; ++nt) {
+          const int j = nt * 16 + lr;
+          if (C::PADDED && j >= N1) continue;
+          if (C::PADC && wt * 32 + g * 8 >= N2) continue;
+          uint8_t *dst = crow + (loff + (uint32_t)(nt * 16 * RB));
+          if constexpr (BITS == 8) {
+            const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], inv_y),
+                               quant4x8(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3], inv_y)};
+            *reinterpret_cast<u32x2_t *>(dst) = w;
+          } else {
+            const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
+                                 yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
+            *reinterpret_cast<uint32_t *>(dst) = quant8<decltype(clamp_tag)::value>(yv, inv_y);
+          }
+          if constexpr (YDBG) {
+            float yd[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) yd[e] = __builtin_ldexpf(yacc[e / 4][nt][e % 4], ty_dbg);
+            float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wt * 32 + g * 8);
+            yp[0] = make_float4(yd[0], yd[1], yd[2], yd[3]);
+            yp[1] = make_float4(yd[4], yd[5], yd[6], yd[7]);
+          }
         }
-        if constexpr (YDBG) {
-          float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wt * 32 + g * 8);
-          yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
-          yp[1] = make_float4(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]);
-        }
-      }
+      };
+      if (clamp) emit(std::true_type{});
+      else emit(std::false_type{});
       if (wt == 0 && lane == 0) store_scale(scales, tok, sc, scale_fp16);
     }
   }
@@ -1861,7 +1884,8 @@ hipError_t launch_colsc(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream, static_cast<const __bf16 *>(X), T,
                      ldx, static_cast<const f16x8 *>(p->p2op), static_cast<const f16x8 *>(p->p1op),
                      p->c, p->p1_exp + p->p2_exp, p->c_absmax, p->clip,
-                     p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
+                     p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes, scales,
+                     y_debug);
   return hipGetLastError();
 }
 
