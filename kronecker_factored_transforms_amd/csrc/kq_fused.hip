@@ -1521,7 +1521,8 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
 // has read the tile and published its |Z'| maximum and the next token's |x| maximum (its
 // chunks were loaded into registers a whole token earlier), the next token's tile is
 // stored over this one; (B) after stage 2, when the next tile is complete and every wave
-// has published its |Y| maximum. c is re-read from L2 for every tile.
+// has published its |Y| maximum. c is read from LDS where it fits, else re-read from L2
+// for every tile.
 template <int N1, int N2>
 struct ColsCCfg {
   static_assert(N1 >= 16 && N1 <= 128, "n1 in [16, 128]");
@@ -1550,6 +1551,12 @@ struct ColsCCfg {
   static constexpr int P1_BYTES = KK * MT * 1024;
   // two workgroups per CU when both fit in LDS
   static constexpr bool TWO = VBUF + P1_BYTES + 1024 <= 80 * 1024;
+  // With one workgroup per CU, c (fp32) stays in LDS when it fits beside the tiles and P1
+  // (else it is re-read from L2 for every tile): as two planes, the first four channels of
+  // every 8-channel chunk, then the last four, so that a wave's reads of consecutive
+  // chunks are consecutive 16-byte words.
+  static constexpr int C_BYTES = N1 * N2 * 4;
+  static constexpr bool C_LDS = !TWO && VBUF + P1_BYTES + C_BYTES + 2048 <= 160 * 1024;
 };
 
 // workgroups per CU the launch bounds ask for
@@ -1565,8 +1572,20 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
     float *__restrict__ ydbg) {
   using C = ColsCCfg<N1, N2>;
   constexpr int n = N1 * N2;
+  // A lane holds 8 columns of a row (4 bytes of INT4 codes), so direct code stores would
+  // scatter 16-byte pieces over 16 rows per instruction. Where LDS allows (the occupancy
+  // unchanged), a token's codes are staged in LDS in their global layout and written
+  // after the next barrier as whole 16-byte words per lane, consecutive across lanes.
+  constexpr int TOK_CODE = n * BITS / 8;  // code bytes per token
+  constexpr int STAGED_BYTES = C::TPI * TOK_CODE;
+  constexpr int LDS_BASE = C::P1_BYTES + C::VBUF + (C::C_LDS ? C::C_BYTES : 0) + 1024;
+  // (not for 128-row tiles: the staging addresses would make the wave spill)
+  constexpr bool STAGE = TOK_CODE % 16 == 0 && C::N1P < 128 &&
+                         LDS_BASE + STAGED_BYTES <= (C::TWO ? 80 * 1024 : 160 * 1024);
+  __shared__ __align__(16) unsigned char s_code[STAGE ? STAGED_BYTES : 16];
   __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
   __shared__ __align__(16) unsigned char s_v[C::VBUF];
+  __shared__ __align__(16) float4 s_c[C::C_LDS ? C::C_BYTES / 16 : 1];
   __shared__ float s_zmax[2][C::WAVES];
   __shared__ float s_xmax[2][C::WAVES][C::TPI];
   __shared__ float s_red[2][C::WAVES];
@@ -1594,6 +1613,11 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
       *reinterpret_cast<uint4 *>(s_v + sl * C::V_BYTES + vchunk_off<C::CHP>(r, cc)) =
           make_uint4(0u, 0u, 0u, 0u);
     }
+  }
+  if constexpr (C::C_LDS) {  // c in its two planes (chunk q: plane h at h * TOK_CHUNKS + q)
+    const float4 *src = reinterpret_cast<const float4 *>(cvec);
+    for (int u = tid; u < 2 * C::TOK_CHUNKS; u += C::THREADS)
+      s_c[u] = src[(u % C::TOK_CHUNKS) * 2 + u / C::TOK_CHUNKS];
   }
 
   // per-thread chunk coordinates (fixed for the whole kernel)
@@ -1658,8 +1682,16 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
         int s = sx[0];
 #pragma unroll
         for (int sl = 1; sl < C::TPI; ++sl) s = c_ts[i] == sl ? sx[sl] : s;
-        const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
-        const float4 a = cp[0], b = cp[1];
+        float4 a, b;
+        if constexpr (C::C_LDS) {
+          const int q = c_row[i] * C::CH + c_cc[i];
+          a = s_c[q];
+          b = s_c[C::TOK_CHUNKS + q];
+        } else {
+          const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
+          a = cp[0];
+          b = cp[1];
+        }
         const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         *reinterpret_cast<f16x8 *>(s_v + c_ts[i] * C::V_BYTES + vchunk_off<C::CHP>(c_row[i], c_cc[i])) =
             scale_round_f16<decltype(scale)::value>(pre[i], cl, s);
@@ -1690,6 +1722,23 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
   for (int sl = 1; sl < C::TPI; ++sl) sx_tok = ts == sl ? sx[sl] : sx_tok;
   lds_barrier();  // the first tile visible
   if (grp + gridDim.x < ngroups) issue_loads(grp + gridDim.x);
+
+  // the staged codes of group `gq` to global memory: its tokens are consecutive, so the
+  // staged bytes (slot-major) are one contiguous run of codes; 16-byte words, consecutive
+  // threads on consecutive words, the tokens at or beyond T left out
+  auto store_staged = [&](int64_t gq) {
+    constexpr int WPT = TOK_CODE / 16;  // 16-byte words per token
+    const int64_t t0 = gq * C::TPI;
+    const int lim = (int)(T - t0 < C::TPI ? T - t0 : C::TPI) * WPT;
+    uint8_t *dst = codes + t0 * (int64_t)TOK_CODE;
+#pragma unroll
+    for (int u = tid; u < C::TPI * WPT; u += C::THREADS) {
+      if (u < lim)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(s_code + u * 16),
+                                    reinterpret_cast<u32x4_t *>(dst + u * 16));
+    }
+  };
+  int64_t staged_grp = -1;  // group whose codes wait in s_code
 
   const f16x8 *sp1 = reinterpret_cast<const f16x8 *>(s_p1);
   const unsigned char *vt = s_v + ts * C::V_BYTES;
@@ -1725,6 +1774,12 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
       x_scales(it & 1, sx);
       store_lds(sx);
       if (nxt + gridDim.x < ngroups) issue_loads(nxt + gridDim.x);
+    }
+    // The previous group's codes are complete in s_code (written before barrier A); they
+    // are read here, before barrier B, and s_code is rewritten only after it. Issued after
+    // the tile store and the prefetch, so that no wait for those loads covers these stores.
+    if constexpr (STAGE) {
+      if (staged_grp >= 0) store_staged(staged_grp);
     }
 
     // ---- stage 2: Y'^T[block, :] = Z'[:, block]^T P1' on fp16 operands ----
@@ -1787,7 +1842,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
     if (tok < T) {
       // lane holds Y[j = nt*16 + lr][wt*32 + 8g + 4h + r]
       constexpr int RB = N2 * BITS / 8;
-      uint8_t *crow = codes + tok * (int64_t)(n * BITS / 8);
+      uint8_t *crow = STAGE ? s_code + ts * TOK_CODE : codes + tok * (int64_t)TOK_CODE;
       const uint32_t loff = (uint32_t)(lr * RB + (wt * 32 + g * 8) * BITS / 8);
       // one scalar branch on the clamp for the whole tile
       auto emit = [&](auto clamp_tag) {
@@ -1820,6 +1875,11 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
       else emit(std::false_type{});
       if (wt == 0 && lane == 0) store_scale(scales, tok, sc, scale_fp16);
     }
+    staged_grp = grp;
+  }
+  if constexpr (STAGE) {  // the last group's codes
+    lds_barrier();
+    if (staged_grp >= 0) store_staged(staged_grp);
   }
 }
 

@@ -139,3 +139,46 @@ def test_fp16_scales_keep_extreme_tokens_in_range(name):
         big.X = S.to_bf16_bits(O.bf16_bits_to_f64(inp.X) * 2.0 ** k)
         Yb = O.transform(big.X, big.P1, big.P2, big.c, big.wl.dtype)
         assert abs(_rel(_emulate_f16(big), Yb) - base) < 1e-4
+
+
+def _split_bf16(a32):
+    """fp32 values as hi = bf16(a) and lo = bf16(a - hi) (a - hi is exact in fp32)."""
+    a32 = np.asarray(a32, np.float32)
+    hi = _bf16(a32.astype(np.float64))
+    lo = _bf16((a32 - hi.astype(np.float32)).astype(np.float64))
+    return hi, lo
+
+
+def _mm3(A32, B32):
+    """A B from the three products hi*hi + hi*lo + lo*hi of the bf16 pairs, rounded to
+    fp32 (the accumulation order inside an MFMA aside)."""
+    Ah, Al = _split_bf16(A32)
+    Bh, Bl = _split_bf16(B32)
+    return (Ah @ Bh + Ah @ Bl + Al @ Bh).astype(np.float32)
+
+
+def test_fp32_three_product_split_meets_the_fp32_tolerance():
+    """fp32 plans on the matrix cores: every operand as a bf16 hi + lo pair and three
+    products per product, Z kept in fp32 and split again for stage 2. The emulation lands
+    well inside the 1e-5 gate of fp32 plans; the hi words alone (one bf16 product) would
+    miss it by orders of magnitude, and dropping a cross term would too."""
+    inp = S.make("fp32_n4096", T=96)
+    wl = inp.wl
+    X = inp.X.astype(np.float32).reshape(-1, wl.n1, wl.n2)
+    P1, P2 = inp.P1.astype(np.float32), inp.P2.astype(np.float32)
+    Y = O.transform(inp.X, inp.P1, inp.P2, None, "fp32")
+
+    Z = _mm3(X, P2)
+    E = np.swapaxes(_mm3(np.swapaxes(Z, 1, 2), P1), 1, 2).astype(np.float64).reshape(len(X), -1)
+    rel3 = _rel(E, Y)
+
+    def two_terms(A32, B32):
+        Ah, Al = _split_bf16(A32)
+        Bh, _ = _split_bf16(B32)
+        return (Ah @ Bh + Al @ Bh).astype(np.float32)
+    Z2 = two_terms(X, P2)
+    E2 = np.swapaxes(two_terms(np.swapaxes(Z2, 1, 2), P1), 1, 2).astype(np.float64).reshape(len(X), -1)
+    Zh = (_bf16(X.astype(np.float64)) @ _bf16(P2.astype(np.float64))).astype(np.float32)
+    E1 = np.einsum("ji,tjk->tik", _bf16(P1.astype(np.float64)), _bf16(Zh.astype(np.float64))).reshape(len(X), -1)
+    assert rel3 < 0.8e-5, rel3
+    assert _rel(E2, Y) > 1e-4 and _rel(E1, Y) > 1e-3, (_rel(E2, Y), _rel(E1, Y))
