@@ -92,4 +92,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)KQ_LDS_PTR(p);
 }
 
+// s_waitcnt immediate for vmcnt(n), 0 <= n < 64 (gfx9: vmcnt in bits [3:0] and [15:14];
+// expcnt and lgkmcnt at their maxima, so not waited for)
+constexpr int wait_vm_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
+// Copy `bytes` (a multiple of 1 KiB) from global memory to LDS by DMA, the waves of the
+// workgroup taking the 1 KiB instructions in turn (lane i of instruction j moves bytes
+// 1024 j + 16 i). Waiting for it takes this wave's vmcnt; the copy is complete for the
+// workgroup after every wave has waited and passed a barrier.
+__device__ __forceinline__ void dma_copy(const void *src, void *dst, int bytes, int wave,
+                                         int waves, int lane) {
+  for (int j = wave; j < bytes / 1024; j += waves)
+    dma16<false>(src, (uint32_t)(j * 1024 + lane * 16),
+                 lds_addr(static_cast<unsigned char *>(dst) + j * 1024));
+}
+
 }  // namespace

@@ -105,10 +105,18 @@ __global__ __launch_bounds__(512) void kq_f32_kernel(
 
   const int64_t stride = (int64_t)gridDim.x * C::WAVES;
   int64_t tok = (int64_t)blockIdx.x * C::WAVES + wave;
-  if (tok < T) dma_tile(tok);  // first, so that it overlaps the operand loads below
-  for (int i = tid; i < 2 * (C::P2_OPS + C::P1_OPS); i += C::THREADS)
-    s_ops[i] = i < 2 * C::P2_OPS ? p2op[i] : p1op[i - 2 * C::P2_OPS];
-  __syncthreads();  // operands visible (this also waits for every load issued so far)
+  // the factor operands reach LDS by DMA, issued before the first token's DMA: a wave
+  // waits for its share of them, not for its token, before the barrier, so that each wave
+  // starts on its token as soon as that token has landed
+  dma_copy(p2op, s_ops, 2 * C::P2_OPS * 16, wave, C::WAVES, lane);
+  dma_copy(p1op, s_ops + 2 * C::P2_OPS, 2 * C::P1_OPS * 16, wave, C::WAVES, lane);
+  if (tok < T) {
+    dma_tile(tok);
+    wait_and_fence<wait_vm_imm(C::LOADS)>();  // all but the token's own DMAs
+  } else {
+    wait_and_fence<kWaitVm0>();
+  }
+  lds_barrier();  // operands visible to every wave
   const bf16x8 *p2h = s_ops, *p2l = s_ops + C::P2_OPS;
   const bf16x8 *p1h = s_ops + 2 * C::P2_OPS, *p1l = p1h + C::P1_OPS;
 

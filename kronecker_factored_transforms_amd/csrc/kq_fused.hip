@@ -394,27 +394,34 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 
   const int64_t stride = (int64_t)gridDim.x * C::WAVES;
   int64_t tok = (int64_t)blockIdx.x * C::WAVES + wave;
-  if (tok < T) dma_tile(tok);  // first, so that it overlaps the factor loads below
-
-  {
-    const uint4 *src = reinterpret_cast<const uint4 *>(p2op);
-    uint4 *dst = reinterpret_cast<uint4 *>(s_p2);
-    for (int i = tid; i < C::P2_BYTES / 16; i += C::THREADS) dst[i] = src[i];
-  }
-  if constexpr (HAS_C) {
-    constexpr int UPR = N2 / 4;  // 16-byte units per row of c
-    const uint4 *src = reinterpret_cast<const uint4 *>(cvec);
-    for (int q = tid; q < N1 * UPR; q += C::THREADS) {
-      const int R = q / UPR, u = q % UPR;
-      *reinterpret_cast<uint4 *>(s_c + R * (N2 * 4) + ((u ^ (R % 16)) * 16)) = src[q];
-    }
-  }
   bf16x8 p1r[C::KK][C::MT];  // stage-2 B operands, resident
 #pragma unroll
   for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
     for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
-  __syncthreads();  // P2 visible (this also waits for every load issued so far)
+  // P2's operands (and c) reach LDS by DMA, issued before the first token's DMA: a wave
+  // waits for its share of them, not for its token, before the barrier, so that each wave
+  // starts on its token as soon as that token has landed (with one token per wave, as for
+  // a few thousand tokens, the CU no longer waits for all eight)
+  dma_copy(p2op, s_p2, C::P2_BYTES, wave, C::WAVES, lane);
+  if constexpr (HAS_C) {
+    // c in 16-byte units of 4 channels, unit u of row R at R * 4 N2 + ((u ^ (R % 16)) * 16):
+    // lane i of instruction j lands at LDS byte b = 1024 j + 16 i of that layout, i.e. row
+    // b / (4 N2), position p = (b % (4 N2)) / 16, and reads unit p ^ (row % 16)
+    const unsigned char *csrc = reinterpret_cast<const unsigned char *>(cvec);
+    for (int j = wave; j < C::C_BYTES / 1024; j += C::WAVES) {
+      const int b = j * 1024 + lane * 16;
+      const int R = b / (4 * N2), pos = (b % (4 * N2)) / 16;
+      dma16<false>(csrc, (uint32_t)(R * 4 * N2 + ((pos ^ (R % 16)) * 16)), lds_addr(s_c + j * 1024));
+    }
+  }
+  if (tok < T) {
+    dma_tile(tok);
+    wait_and_fence<wait_vm_imm(C::LOADS)>();  // all but the token's own DMAs
+  } else {
+    wait_and_fence<kWaitVm0>();
+  }
+  lds_barrier();  // P2 (and c) visible to every wave
   const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
 
   // codes of the previous token, stored one step late (8 or 4 values per dword)
@@ -1521,8 +1528,8 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
 // has read the tile and published its |Z'| maximum and the next token's |x| maximum (its
 // chunks were loaded into registers a whole token earlier), the next token's tile is
 // stored over this one; (B) after stage 2, when the next tile is complete and every wave
-// has published its |Y| maximum. c is read from LDS where it fits, else re-read from L2
-// for every tile.
+// has published its |Y| maximum. c is re-read from L2 for every tile. A token's codes are
+// staged in LDS and written after the next barrier A.
 template <int N1, int N2>
 struct ColsCCfg {
   static_assert(N1 >= 16 && N1 <= 128, "n1 in [16, 128]");
@@ -1551,12 +1558,6 @@ struct ColsCCfg {
   static constexpr int P1_BYTES = KK * MT * 1024;
   // two workgroups per CU when both fit in LDS
   static constexpr bool TWO = VBUF + P1_BYTES + 1024 <= 80 * 1024;
-  // With one workgroup per CU, c (fp32) stays in LDS when it fits beside the tiles and P1
-  // (else it is re-read from L2 for every tile): as two planes, the first four channels of
-  // every 8-channel chunk, then the last four, so that a wave's reads of consecutive
-  // chunks are consecutive 16-byte words.
-  static constexpr int C_BYTES = N1 * N2 * 4;
-  static constexpr bool C_LDS = !TWO && VBUF + P1_BYTES + C_BYTES + 2048 <= 160 * 1024;
 };
 
 // workgroups per CU the launch bounds ask for
@@ -1578,14 +1579,13 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
   // after the next barrier as whole 16-byte words per lane, consecutive across lanes.
   constexpr int TOK_CODE = n * BITS / 8;  // code bytes per token
   constexpr int STAGED_BYTES = C::TPI * TOK_CODE;
-  constexpr int LDS_BASE = C::P1_BYTES + C::VBUF + (C::C_LDS ? C::C_BYTES : 0) + 1024;
+  constexpr int LDS_BASE = C::P1_BYTES + C::VBUF + 1024;
   // (not for 128-row tiles: the staging addresses would make the wave spill)
   constexpr bool STAGE = TOK_CODE % 16 == 0 && C::N1P < 128 &&
                          LDS_BASE + STAGED_BYTES <= (C::TWO ? 80 * 1024 : 160 * 1024);
   __shared__ __align__(16) unsigned char s_code[STAGE ? STAGED_BYTES : 16];
   __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
   __shared__ __align__(16) unsigned char s_v[C::VBUF];
-  __shared__ __align__(16) float4 s_c[C::C_LDS ? C::C_BYTES / 16 : 1];
   __shared__ float s_zmax[2][C::WAVES];
   __shared__ float s_xmax[2][C::WAVES][C::TPI];
   __shared__ float s_red[2][C::WAVES];
@@ -1613,11 +1613,6 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
       *reinterpret_cast<uint4 *>(s_v + sl * C::V_BYTES + vchunk_off<C::CHP>(r, cc)) =
           make_uint4(0u, 0u, 0u, 0u);
     }
-  }
-  if constexpr (C::C_LDS) {  // c in its two planes (chunk q: plane h at h * TOK_CHUNKS + q)
-    const float4 *src = reinterpret_cast<const float4 *>(cvec);
-    for (int u = tid; u < 2 * C::TOK_CHUNKS; u += C::THREADS)
-      s_c[u] = src[(u % C::TOK_CHUNKS) * 2 + u / C::TOK_CHUNKS];
   }
 
   // per-thread chunk coordinates (fixed for the whole kernel)
@@ -1682,16 +1677,8 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
         int s = sx[0];
 #pragma unroll
         for (int sl = 1; sl < C::TPI; ++sl) s = c_ts[i] == sl ? sx[sl] : s;
-        float4 a, b;
-        if constexpr (C::C_LDS) {
-          const int q = c_row[i] * C::CH + c_cc[i];
-          a = s_c[q];
-          b = s_c[C::TOK_CHUNKS + q];
-        } else {
-          const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
-          a = cp[0];
-          b = cp[1];
-        }
+        const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
+        const float4 a = cp[0], b = cp[1];
         const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         *reinterpret_cast<f16x8 *>(s_v + c_ts[i] * C::V_BYTES + vchunk_off<C::CHP>(c_row[i], c_cc[i])) =
             scale_round_f16<decltype(scale)::value>(pre[i], cl, s);
