@@ -68,6 +68,39 @@ def traffic_from_profile(workload: str, kernel: str):
     return float(m_b.group(1))
 
 
+def hbm_probe(torch, dev, achieved_gbs):
+    """What library kernels reach on this machine's HBM, measured beside the transform: a plain
+    device-to-device copy (1 byte written per byte read), and a 4:1 read:write stream, the
+    transform's own ratio (the sum of four 256 MiB quarters of a bf16 tensor into a fifth:
+    1 GiB in, 256 MiB out). 1 GiB source, beyond the 256 MB Infinity Cache; 3 untimed and
+    10 timed runs each. The transform's achieved rate is reported as a fraction of both."""
+    src = torch.empty(2 ** 29, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
+    dst = torch.empty_like(src)
+    red = torch.empty(2 ** 27, dtype=torch.bfloat16, device=dev)
+    ops = {"copy": (lambda: dst.copy_(src), 2 * src.numel() * 2),
+           "read4_write1": (lambda: torch.sum(src.view(4, -1), dim=0, out=red),
+                            src.numel() * 2 + red.numel() * 2)}
+    res = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_GBps"] = round(nbytes * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    del src, dst, red
+    res["kernel_frac_of_copy"] = round(achieved_gbs / res["copy_GBps"], 3)
+    res["kernel_frac_of_read4_write1"] = round(achieved_gbs / res["read4_write1_GBps"], 3)
+    res["kind"] = "torch copy_ and a sum over the outer dimension of 4 (library kernels), same box"
+    log(f"[bench] HBM probe: copy {res['copy_GBps']:.0f} GB/s, 4:1 stream {res['read4_write1_GBps']:.0f} GB/s; "
+        f"the transform reaches {res['kernel_frac_of_copy']:.2f} and {res['kernel_frac_of_read4_write1']:.2f} of them")
+    return res
+
+
 def cpu_baseline(inp, seconds: float, bits: int = 4):
     """Time the CPU oracle (as it stands) on a bounded sample of the workload's tokens."""
     import numpy as np
@@ -433,6 +466,8 @@ def main():
             extras[name], _ = measure(torch, B, S, dev, name, args, min_warm_ms=20.0,
                                       graph=name.startswith("decode"))
 
+    probe = hbm_probe(torch, dev, head["roofline"]["achieved"]) if run_extra else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds, args.bits)
@@ -457,6 +492,7 @@ def main():
         "config": cfg,
         "inputs_sha256": head["inputs_sha256"],
         "roofline": head["roofline"],
+        "hbm_probe": probe,
         "mfma": head["mfma"],
         "cpu_baseline": cpu,
     }
