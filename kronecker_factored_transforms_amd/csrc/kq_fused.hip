@@ -82,7 +82,7 @@ template <int N1, int N2, int WPT, bool HAS_C, bool DEEP>
 __global__ __launch_bounds__(kThreads, DEEP ? 1 : 2) void kq_reg_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
-    const float *__restrict__ cvec, float clip, int scale_fp16,
+    const float *__restrict__ cvec, float clip, int scale_fp16, int clip_allows_no_clamp,
     uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
   using C = RegCfg<N1, N2, WPT, HAS_C, DEEP>;
   constexpr int n = N1 * N2;
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads, DEEP ? 1 : 2) void kq_reg_kernel(
       for (int nt = 0; nt < C::MT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[m2][nt][r]));
-    m = wave_max(m);
+    m = wave_max_uniform(m);
     if constexpr (WPT > 1) {
       // combine the partial absmax of the waves sharing the token (slots alternate per
       // iteration, so one barrier per token is enough)
@@ -220,6 +220,7 @@ __global__ __launch_bounds__(kThreads, DEEP ? 1 : 2) void kq_reg_kernel(
       for (int w = 0; w < WPT; ++w) m = fmaxf(m, s_red[it & 1][slot * WPT + w]);
     }
     const TokenScale ts = token_scale(m, clip, scale_fp16);
+    const bool clamp = __builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, ts.s32) ? 1 : 0);
 
     if (tok < T) {
       uint8_t *crow = codes + tok * (int64_t)(n / 2);
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kThreads, DEEP ? 1 : 2) void kq_reg_kernel(
                                yacc[2 * q][nt][2],     yacc[2 * q][nt][3],
                                yacc[2 * q + 1][nt][0], yacc[2 * q + 1][nt][1],
                                yacc[2 * q + 1][nt][2], yacc[2 * q + 1][nt][3]};
-          w[q] = quant8(yv, ts.inv);
+          w[q] = clamp ? quant8<true>(yv, ts.inv) : quant8<false>(yv, ts.inv);
         }
         uint8_t *dst = crow + j * (N2 / 2) + wb * (C::CB / 2) + g * (C::LPL / 2);
         if constexpr (C::NT == 8) {
@@ -1241,7 +1242,7 @@ template <int N1, int N2, bool HAS_C, bool YDBG = false, int BITS = 4>
 __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, N2)) void kq_cols_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const bf16x8 *__restrict__ p2op, const bf16x8 *__restrict__ p1op,
-    const float *__restrict__ cvec, float clip, int scale_fp16,
+    const float *__restrict__ cvec, float clip, int scale_fp16, int clip_allows_no_clamp,
     uint8_t *__restrict__ codes, void *__restrict__ scales, float *__restrict__ ydbg) {
   using C = ColsCfg<N1, N2, HAS_C>;
   constexpr int n = N1 * N2;
@@ -1469,7 +1470,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
       for (int nt = 0; nt < C::MT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[h][nt][r]));
-    m = wave_max(m);
+    m = wave_max_uniform(m);
     if (lane == 0) s_red[wave] = m;
     lds_barrier();
     float amax = 0.f;
@@ -1484,27 +1485,34 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
       constexpr int RB = N2 * BITS / 8;  // code bytes per row of Y
       uint8_t *crow = codes + tok * (int64_t)(n * BITS / 8);
       const uint32_t loff = (uint32_t)(lr * RB + (wt * 32 + g * 8) * BITS / 8);
+      // one scalar branch on the clamp (INT4: skipped where the clip ratio rules it out)
+      auto emit = [&](auto clamp_tag) {
 #pragma unroll
-      for (int nt = 0; nt < C::MT; ++nt) {
-        const int j = nt * 16 + lr;
-        if (C::PADDED && j >= N1) continue;  // padded rows of Y are not stored
-        if (C::PADC && wt * 32 + g * 8 >= N2) continue;  // nor its padded columns
-        uint8_t *dst = crow + (loff + (uint32_t)(nt * 16 * RB));
-        if constexpr (BITS == 8) {
-          const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], sc.inv),
-                             quant4x8(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3], sc.inv)};
-          *reinterpret_cast<u32x2_t *>(dst) = w;
-        } else {
-          const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
-                               yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
-          *reinterpret_cast<uint32_t *>(dst) = quant8(yv, sc.inv);
+        for (int nt = 0; nt < C::MT; ++nt) {
+          const int j = nt * 16 + lr;
+          if (C::PADDED && j >= N1) continue;  // padded rows of Y are not stored
+          if (C::PADC && wt * 32 + g * 8 >= N2) continue;  // nor its padded columns
+          uint8_t *dst = crow + (loff + (uint32_t)(nt * 16 * RB));
+          if constexpr (BITS == 8) {
+            const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], sc.inv),
+                               quant4x8(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3], sc.inv)};
+            *reinterpret_cast<u32x2_t *>(dst) = w;
+          } else {
+            const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
+                                 yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
+            *reinterpret_cast<uint32_t *>(dst) = quant8<decltype(clamp_tag)::value>(yv, sc.inv);
+          }
+          if constexpr (YDBG) {
+            float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wt * 32 + g * 8);
+            yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
+            yp[1] = make_float4(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]);
+          }
         }
-        if constexpr (YDBG) {
-          float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + wt * 32 + g * 8);
-          yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
-          yp[1] = make_float4(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]);
-        }
-      }
+      };
+      if (BITS == 8 || __builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, sc.s32) ? 1 : 0))
+        emit(std::true_type{});
+      else
+        emit(std::false_type{});
       if (wt == 0 && lane == 0) store_scale(scales, tok, sc, scale_fp16);
     }
     if constexpr (C::DMA) wait_and_fence<kWaitVm0>();  // the next tile has landed
@@ -1882,7 +1890,8 @@ hipError_t launch_reg(const kq_plan *p, const void *X, int64_t T, int64_t ldx, u
   hipLaunchKernelGGL((kq_reg_kernel<N1, N2, WPT, HAS_C, DEEP>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
-                     p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
+                     p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0,
+                     codes, scales, y_debug);
   return hipGetLastError();
 }
 
@@ -1898,7 +1907,8 @@ hipError_t launch_cols(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx,
                      static_cast<const bf16x8 *>(p->p2op), static_cast<const bf16x8 *>(p->p1op),
-                     p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, codes, scales, y_debug);
+                     p->c, p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0,
+                     codes, scales, y_debug);
   return hipGetLastError();
 }
 

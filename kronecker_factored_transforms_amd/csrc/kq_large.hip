@@ -222,8 +222,8 @@ __global__ __launch_bounds__(large_threads(N2)) void kq_z_kernel(
 template <int N1, int N2, bool YDBG, int BITS>
 __global__ __launch_bounds__(large_threads(N2)) void kq_zq_kernel(
     const bf16x8 *__restrict__ zws, int64_t T, const bf16x8 *__restrict__ p1op, float clip,
-    int scale_fp16, uint8_t *__restrict__ codes, void *__restrict__ scales,
-    float *__restrict__ ydbg) {
+    int scale_fp16, int clip_allows_no_clamp, uint8_t *__restrict__ codes,
+    void *__restrict__ scales, float *__restrict__ ydbg) {
   using C = LargeCfg<N1, N2, false>;
   constexpr int n = N1 * N2;
   __shared__ __align__(16) unsigned char s_p1[C::P1_BYTES];
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(large_threads(N2)) void kq_zq_kernel(
       for (int nt = 0; nt < C::MT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(yacc[h][nt][r]));
-    m = wave_max(m);
+    m = wave_max_uniform(m);
     if (lane == 0) s_red[it & 1][wave] = m;
     lds_barrier();
     float amax = 0.f;
@@ -299,26 +299,33 @@ __global__ __launch_bounds__(large_threads(N2)) void kq_zq_kernel(
     const int col0 = wave * 32 + g * 8;
     if (col0 < N2) {  // padded columns are not stored
       uint8_t *crow = codes + tok * (int64_t)(n * BITS / 8) + col0 * BITS / 8;
+      // one scalar branch on the clamp (INT4: skipped where the clip ratio rules it out)
+      auto emit = [&](auto clamp_tag) {
 #pragma unroll
-      for (int nt = 0; nt < C::MT; ++nt) {
-        const int j = nt * 16 + lr;
-        if (j >= N1) continue;  // nor padded rows
-        uint8_t *dst = crow + j * RB;
-        if constexpr (BITS == 8) {
-          const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], sc.inv),
-                             quant4x8(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3], sc.inv)};
-          *reinterpret_cast<u32x2_t *>(dst) = w;
-        } else {
-          const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
-                               yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
-          *reinterpret_cast<uint32_t *>(dst) = quant8(yv, sc.inv);
+        for (int nt = 0; nt < C::MT; ++nt) {
+          const int j = nt * 16 + lr;
+          if (j >= N1) continue;  // nor padded rows
+          uint8_t *dst = crow + j * RB;
+          if constexpr (BITS == 8) {
+            const u32x2_t w = {quant4x8(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3], sc.inv),
+                               quant4x8(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3], sc.inv)};
+            *reinterpret_cast<u32x2_t *>(dst) = w;
+          } else {
+            const float yv[8] = {yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3],
+                                 yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]};
+            *reinterpret_cast<uint32_t *>(dst) = quant8<decltype(clamp_tag)::value>(yv, sc.inv);
+          }
+          if constexpr (YDBG) {
+            float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + col0);
+            yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
+            yp[1] = make_float4(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]);
+          }
         }
-        if constexpr (YDBG) {
-          float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + j * N2 + col0);
-          yp[0] = make_float4(yacc[0][nt][0], yacc[0][nt][1], yacc[0][nt][2], yacc[0][nt][3]);
-          yp[1] = make_float4(yacc[1][nt][0], yacc[1][nt][1], yacc[1][nt][2], yacc[1][nt][3]);
-        }
-      }
+      };
+      if (BITS == 8 || __builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, sc.s32) ? 1 : 0))
+        emit(std::true_type{});
+      else
+        emit(std::false_type{});
     }
     if (wave == 0 && lane == 0) store_scale(scales, tok, sc, scale_fp16);
     if (KPRE < C::KK && nxt < T) load_z_range(nxt, KPRE, C::KK);
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(large_threads(N2)) void kq_ptile_kernel(
       }
       lds_barrier();  // tile jt + 1 copied; every wave is done with tile jt's buffer
     }
-    m = wave_max(m);
+    m = wave_max_uniform(m);
     if (lane == 0) s_red[wave] = m;
     lds_barrier();
     float amax = 0.f;
@@ -443,7 +450,7 @@ __global__ __launch_bounds__(large_threads(N2)) void kq_ptile_kernel(
 template <int BITS>
 __global__ __launch_bounds__(256) void kq_yquant_kernel(const float *__restrict__ Y, int64_t T,
                                                         int n, const void *__restrict__ scales,
-                                                        int scale_fp16,
+                                                        int scale_fp16, int clip_allows_no_clamp,
                                                         uint8_t *__restrict__ codes) {
   const int64_t per_tok = n / 8;
   const int64_t total = T * per_tok;
@@ -460,7 +467,9 @@ __global__ __launch_bounds__(256) void kq_yquant_kernel(const float *__restrict_
       reinterpret_cast<u32x2_t *>(codes)[e] = w;
     } else {
       const float yv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      reinterpret_cast<uint32_t *>(codes)[e] = quant8(yv, inv);
+      // the clamp bound holds for the stored step as for s32 (normal fp16 or exact fp32)
+      reinterpret_cast<uint32_t *>(codes)[e] =
+          clamp_needed(clip_allows_no_clamp, s) ? quant8<true>(yv, inv) : quant8<false>(yv, inv);
     }
   }
 }
@@ -484,7 +493,7 @@ hipError_t launch_twostage(const kq_plan *p, const void *X, int64_t T, int64_t l
   auto k = y_debug ? &kq_zq_kernel<N1, N2, true, BITS> : &kq_zq_kernel<N1, N2, false, BITS>;
   hipLaunchKernelGGL(k, dim3(g2), dim3(C::THREADS), 0, stream, static_cast<const bf16x8 *>(z), T,
                      static_cast<const bf16x8 *>(p->p1op), p->clip, p->scale_dtype == KQ_FP16 ? 1 : 0,
-                     codes, scales, y_debug);
+                     p->clip >= 0.935f ? 1 : 0, codes, scales, y_debug);
   return hipGetLastError();
 }
 
@@ -512,7 +521,7 @@ hipError_t launch_ptile(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
   const int g2 = (int)(blocks < (int64_t)p->grid_cap2 ? blocks : (int64_t)p->grid_cap2);
   hipLaunchKernelGGL((kq_yquant_kernel<BITS>), dim3(g2), dim3(256), 0, stream,
                      static_cast<const float *>(y), T, N1 * N2, static_cast<const void *>(scales),
-                     p->scale_dtype == KQ_FP16 ? 1 : 0, codes);
+                     p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes);
   return hipGetLastError();
 }
 
