@@ -404,7 +404,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="time only --workload (the default run also times " + ", ".join(EXTRA_WORKLOADS) + ")")
     ap.add_argument("--split", choices=["default", "reg1", "reg2", "cols", "deep", "stream", "pair",
-                                        "generic", "twostage", "ptile"],
+                                        "generic", "twostage", "ptile", "rsplit"],
                     default="default", help="work split of the fused kernel (default: the plan's)")
     ap.add_argument("--per-launch-events", action="store_true",
                     help="also time every launch with its own event pair (diagnostic)")
@@ -442,7 +442,7 @@ def main():
              "cols": B.KQ_FLAG_SPLIT_COLS, "deep": B.KQ_FLAG_SPLIT_DEEP,
              "stream": B.KQ_FLAG_SPLIT_STREAM, "pair": B.KQ_FLAG_SPLIT_PAIR,
              "generic": B.KQ_FLAG_FORCE_GENERIC, "twostage": B.KQ_FLAG_SPLIT_TWOSTAGE,
-             "ptile": B.KQ_FLAG_SPLIT_PTILE}[args.split]
+             "ptile": B.KQ_FLAG_SPLIT_PTILE, "rsplit": B.KQ_FLAG_SPLIT_RSPLIT}[args.split]
 
     if args.copy_probe:
         a = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)

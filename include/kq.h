@@ -64,7 +64,7 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
 #define KQ_FLAG_SPLIT_DEEP 0x80u    /* MFMA: one wave per token and SIMD, next token     */
                                     /* prefetched into registers                          */
 #define KQ_FLAG_SPLIT_STREAM 0x100u /* MFMA: one wave per token, next token prefetched   */
-                                    /* into LDS by DMA (no per-channel scale)             */
+                                    /* into LDS by DMA (per-channel scale: n2 = 64 only)  */
 #define KQ_FLAG_SPLIT_PAIR 0x200u   /* MFMA: two waves per token (one column half each),  */
                                     /* operands in registers, tokens double-buffered in   */
                                     /* LDS by DMA (no per-channel scale)                  */
@@ -80,6 +80,10 @@ typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
                                        /* time, each tile of Y goes to the workspace (fp32) */
                                        /* with the token's absmax, and a second kernel      */
                                        /* quantizes it                                      */
+#define KQ_FLAG_SPLIT_RSPLIT 0x4000u   /* MFMA, with a per-channel scale, n2 = 64, INT4: a   */
+                                       /* token's 16-row blocks on n1/16 waves, Z passed    */
+                                       /* between them through LDS (the small-batch split   */
+                                       /* of those plans)                                   */
 
 /* KQ_FLAG_PER_ROW: the left factor is the identity (pass P1 = NULL) and every row of V
  * (n2 values, e.g. one attention head of a token) gets its own step, so `scales` holds

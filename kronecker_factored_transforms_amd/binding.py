@@ -27,6 +27,7 @@ KQ_FLAG_PER_ROW = 0x400
 KQ_FLAG_INT8 = 0x800
 KQ_FLAG_SPLIT_TWOSTAGE = 0x1000
 KQ_FLAG_SPLIT_PTILE = 0x2000
+KQ_FLAG_SPLIT_RSPLIT = 0x4000
 
 # every symbol declared in include/kq.h
 EXPORTS = (

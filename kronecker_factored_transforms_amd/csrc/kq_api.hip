@@ -226,7 +226,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
   const unsigned split_flags =
       flags & (KQ_FLAG_SPLIT_REG1 | KQ_FLAG_SPLIT_REG2 | KQ_FLAG_SPLIT_COLS | KQ_FLAG_SPLIT_DEEP |
                KQ_FLAG_SPLIT_STREAM | KQ_FLAG_SPLIT_PAIR | KQ_FLAG_SPLIT_TWOSTAGE |
-               KQ_FLAG_SPLIT_PTILE);
+               KQ_FLAG_SPLIT_PTILE | KQ_FLAG_SPLIT_RSPLIT);
   if (flags & ~(KQ_FLAG_FORCE_GENERIC | split_flags)) return KQ_ERR_INVALID_ARG;
   if ((split_flags & (split_flags - 1)) != 0) return KQ_ERR_INVALID_ARG;  // at most one
   if (split_flags && ((flags & KQ_FLAG_FORCE_GENERIC) || x_dtype != KQ_BF16))
@@ -239,6 +239,7 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
                     : split_flags == KQ_FLAG_SPLIT_PAIR ? KQ_SPLIT_PAIR
                     : split_flags == KQ_FLAG_SPLIT_TWOSTAGE ? KQ_SPLIT_TWOSTAGE
                     : split_flags == KQ_FLAG_SPLIT_PTILE ? KQ_SPLIT_PTILE
+                    : split_flags == KQ_FLAG_SPLIT_RSPLIT ? KQ_SPLIT_RSPLIT
                                                         : 0;
   const bool large_split = split == KQ_SPLIT_TWOSTAGE || split == KQ_SPLIT_PTILE;
 
@@ -357,12 +358,16 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
     // about four tokens per CU it leaves most CUs idle, and the pair kernel (two waves
     // per token, 2-wave workgroups) finishes a small batch sooner (measured on MI355X:
     // 64 tokens of 64x128 in 5.4 us vs 9.0 us; break-even near 1024 tokens).
-    // Plans without a pair variant (with c, or rows padded to the stream layout) use the
-    // column kernel for small batches, which also spreads a token over several waves
-    // (measured on MI355X under a HIP graph, 64 tokens: 64x64 with c 4.9 us vs 5.8 us,
-    // 64x112 4.3 us vs 7.4 us).
+    // Plans with c use the row split (a token's 16-row blocks on their own waves, the
+    // stream kernel's arithmetic bit for bit): measured on MI355X under a HIP graph, 64x64
+    // with c, 64 / 256 / 512 / 1024 tokens: 4.17 / 4.44 / 5.74 / 7.52 us against 5.39 /
+    // 5.61 / 6.37 / 8.23 us for the column split and 6.31 / 6.63 / 6.84 / 7.20 us for the
+    // stream split itself. Plans with neither (rows padded to the stream layout) use the
+    // column kernel, which also spreads a token over several waves (64x112, 64 tokens:
+    // 4.3 us vs 7.4 us).
     if (split == 0 && fv->split == KQ_SPLIT_STREAM) {
       const kq_fused_variant *sv = kq_fused_lookup(n1, n2, c != nullptr, KQ_SPLIT_PAIR, bits);
+      if (!sv) sv = kq_fused_lookup(n1, n2, c != nullptr, KQ_SPLIT_RSPLIT, bits);
       if (!sv) sv = kq_fused_lookup(n1, n2, c != nullptr, KQ_SPLIT_COLS, bits);
       int small_per_cu = 0;
       if (sv) {

@@ -632,6 +632,215 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// row-split kernel with c (n2 = 64): a token's rows spread over n1/16 waves
+// ------------------------------------------------------------------------------------
+// For batches of a few thousand tokens the stream kernel has one token per wave, and the
+// token's whole conversion, both contractions and the quantizer run as one serial chain
+// in that wave. Here a workgroup of MT = n1/16 waves takes a token, wave w its rows
+// 16 w .. 16 w + 15:
+//  * stage 1 is row-wise: the wave converts and multiplies only its own rows, with c for
+//    those rows held in registers; the token's bound max|x| max|c| (for x^'s scale 2^sx)
+//    meets at barrier 0;
+//  * Z crosses the waves through LDS, rounded to fp16 after the scale 2^zs from the
+//    token's largest |Z'| (barrier 1); stage 2 starts after barrier 2;
+//  * stage 2 gives wave w rows 16 w .. 16 w + 15 of Y; the absmax meets at barrier 3
+//    and every wave quantizes and stores its rows.
+// The roundings, scales and MFMA order are the stream kernel's, so a token gets the same
+// codes from both (a plan may use either, by batch size). Each wave DMAs its own rows of
+// the next token into its part of the slot as soon as it has read the current ones (no
+// other wave reads them), so the loads overlap the rest of the token.
+template <int N1>
+struct RsplitCfg {
+  static_assert(N1 % 16 == 0 && N1 >= 16 && N1 <= 64, "row-split kernel: n1 in {16, 32, 48, 64}");
+  static constexpr int N2 = 64;
+  static constexpr int MT = N1 / 16;            // waves per token (16-row blocks)
+  static constexpr int THREADS = MT * 64;
+  static constexpr int KS = N2 / 32;            // stage-1 reduction steps
+  static constexpr int NT = N2 / 16;            // column tiles
+  static constexpr int KK = (MT + 1) / 2;       // stage-2 reduction steps (32 rows each)
+  static constexpr int RB = N2 * 2;             // bytes per row of X
+  static constexpr int WROWS = 16 * RB;         // bytes of a wave's rows (2 KiB)
+  static constexpr int ZBYTES = NT * KK * 64 * 16;  // Z exchange: [a][kk][lane] 16 bytes
+};
+
+template <int N1, bool YDBG = false>
+__global__ __launch_bounds__(RsplitCfg<N1>::THREADS) void kq_rsplit_kernel(
+    const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
+    const f16x8 *__restrict__ p2op, const f16x8 *__restrict__ p1op,
+    const float *__restrict__ cvec, int f_exp, float cmax, float clip, int scale_fp16,
+    int clip_allows_no_clamp, uint8_t *__restrict__ codes, void *__restrict__ scales,
+    float *__restrict__ ydbg) {
+  using C = RsplitCfg<N1>;
+  constexpr int N2 = C::N2;
+  constexpr int n = N1 * N2;
+  // the token's rows (each wave DMAs and reads only its own 16), and Z's exchange area:
+  // for stage-2 step kk and column tile a, lane L's 16 bytes are the 4 fp16 values of
+  // lane L of wave 2 kk (rows 32 kk + 4 g + r) then those of wave 2 kk + 1 (rows + 16):
+  // exactly the stage-2 A operand of lane L, in the slot order of P1's operands
+  __shared__ __align__(16) unsigned char s_tile[C::MT * C::WROWS];
+  __shared__ __align__(16) unsigned char s_z[C::ZBYTES];
+  __shared__ float s_xm[2][C::MT];
+  __shared__ float s_zm[2][C::MT];
+  __shared__ float s_ym[2][C::MT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // this wave's 16-row block
+  const int g = lane >> 4;
+  const int lr = lane & 15;
+  unsigned char *rows = s_tile + w * C::WROWS;
+
+  // DMA of the wave's rows of token `tok`: instruction j fills rows 8 j .. 8 j + 7 of the
+  // block; lane i lands at row R = 8 j + i / 8, position i % 8 of that row, so it reads
+  // piece (i % 8) ^ ((R / 2) % 8): the 16 rows of an operand read then fall in 16
+  // different bank groups
+  uint32_t voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int R = 8 * j + lane / 8;
+    voff[j] = (uint32_t)(((16 * w + R) * N2 + (((lane % 8) ^ ((R / 2) % 8)) * 8)) * 2);
+  }
+  auto dma_rows = [&](int64_t tok) {
+    const unsigned char *xt = reinterpret_cast<const unsigned char *>(X + tok * ldx);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16_nt(xt, voff[j], lds_addr(rows + j * 1024));
+  };
+  int64_t tok = blockIdx.x;
+  if (tok < T) dma_rows(tok);
+
+  // operands in registers for the whole kernel: P2 (stage-1 B, all column tiles), P1
+  // (stage-2 B, this wave's output rows), and c for the lane's 16 channels
+  f16x8 p2w[C::KS][C::NT], p1w[C::KK];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int a = 0; a < C::NT; ++a) p2w[ks][a] = p2op[(ks * C::NT + a) * 64 + lane];
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk) p1w[kk] = p1op[(kk * C::MT + w) * 64 + lane];
+  float cl[C::KS][8];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const float4 *cp = reinterpret_cast<const float4 *>(cvec + (16 * w + lr) * N2 + 32 * ks + 8 * g);
+    const float4 u = cp[0], v = cp[1];
+    cl[ks][0] = u.x; cl[ks][1] = u.y; cl[ks][2] = u.z; cl[ks][3] = u.w;
+    cl[ks][4] = v.x; cl[ks][5] = v.y; cl[ks][6] = v.z; cl[ks][7] = v.w;
+  }
+  if constexpr (C::MT % 2 == 1) {  // the absent last block's half of Z stays zero
+    for (int i = tid; i < C::ZBYTES / 16; i += C::THREADS)
+      reinterpret_cast<uint4 *>(s_z)[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  for (int it = 0; tok < T; tok += gridDim.x, ++it) {
+    const int par = it & 1;
+    // this token's rows have landed: at least one store (the codes) was issued after the
+    // last DMA, so waiting for all but one vector-memory operation covers the DMA
+    wait_and_fence<wait_vm_imm(1)>();
+    uint4 raw[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      raw[ks] = *reinterpret_cast<const uint4 *>(rows + lr * C::RB + (((4 * ks + g) ^ ((lr / 2) % 8)) * 16));
+    wait_and_fence<kWaitLgkm0>();  // the rows are read: the next token's may come in
+    if (tok + gridDim.x < T) dma_rows(tok + gridDim.x);
+
+    // ---- stage 1 on the wave's rows: Z' = x^ P2' ----
+    uint32_t xm = 0;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) xm = absmax_bf16(raw[ks], xm);
+    const float xmw = wave_max_uniform(__uint_as_float(xm << 16));
+    if (lane == 0) s_xm[par][w] = xmw;
+    lds_barrier();  // (0) every block's |x| maximum is published
+    float xmax = 0.f;
+#pragma unroll
+    for (int v = 0; v < C::MT; ++v) xmax = max_nn(xmax, s_xm[par][v]);
+    const int sx = __builtin_amdgcn_readfirstlane(f16_scale_exp(__fmul_rn(xmax, cmax)));
+    f16x8 av[C::KS];
+    if (sx == 0) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) av[ks] = scale_round_f16<false>(raw[ks], cl[ks], 0);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) av[ks] = scale_round_f16<true>(raw[ks], cl[ks], sx);
+    }
+    f32x4 zacc[C::NT];
+#pragma unroll
+    for (int a = 0; a < C::NT; ++a) {
+      zacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) zacc[a] = mfma_f16(av[ks], p2w[ks][a], zacc[a]);
+    }
+    const float zm = wave_max_uniform(absmax_acc(zacc, 0.f));
+    if (lane == 0) s_zm[par][w] = zm;
+    lds_barrier();  // (1) every block's |Z'| maximum is published
+    float zmax = 0.f;
+#pragma unroll
+    for (int v = 0; v < C::MT; ++v) zmax = max_nn(zmax, s_zm[par][v]);
+    const int zs = __builtin_amdgcn_readfirstlane(f16_scale_exp(zmax));
+#pragma unroll
+    for (int a = 0; a < C::NT; ++a) {
+      _Float16 h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = (_Float16)(zs == 0 ? zacc[a][r] : __builtin_ldexpf(zacc[a][r], zs));
+      *reinterpret_cast<u32x2_t *>(s_z + ((a * C::KK + w / 2) * 64 + lane) * 16 + (w % 2) * 8) =
+          __builtin_bit_cast(u32x2_t, h);
+    }
+    lds_barrier();  // (2) Z is complete in LDS
+
+    // ---- stage 2: Y'^T[:, rows of block w] = Z^T P1'[:, rows of block w] ----
+    f32x4 yacc[C::NT];
+#pragma unroll
+    for (int a = 0; a < C::NT; ++a) yacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+      for (int a = 0; a < C::NT; ++a) {
+        const f16x8 za = *reinterpret_cast<const f16x8 *>(s_z + ((a * C::KK + kk) * 64 + lane) * 16);
+        yacc[a] = mfma_f16(za, p1w[kk], yacc[a]);
+      }
+    const int ty = f_exp - sx - zs;  // Y = Y' 2^(f1 + f2 - sx - sz), exact
+    const float ym = wave_max_uniform(absmax_acc(yacc, 0.f));
+    if (lane == 0) s_ym[par][w] = ym;
+    lds_barrier();  // (3) every block's |Y'| maximum is published
+    float amax_y = 0.f;
+#pragma unroll
+    for (int v = 0; v < C::MT; ++v) amax_y = max_nn(amax_y, s_ym[par][v]);
+    const float amax = __builtin_ldexpf(amax_y, ty);
+    const TokenScale sc = token_scale(amax, clip, scale_fp16);
+    float inv_y;
+    int ty_dbg = ty;
+    if (!__builtin_amdgcn_readfirstlane(fold_scale(sc.inv, ty, amax, inv_y) ? 1 : 0)) {
+#pragma unroll
+      for (int a = 0; a < C::NT; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[a][r] = __builtin_ldexpf(yacc[a][r], ty);
+      inv_y = sc.inv;
+      ty_dbg = 0;
+    }
+    // lane holds Y[16 w + lr][16 g + 4 a + r]: 16 consecutive codes of its row, 8 bytes
+    const float y0[8] = {yacc[0][0], yacc[0][1], yacc[0][2], yacc[0][3],
+                         yacc[1][0], yacc[1][1], yacc[1][2], yacc[1][3]};
+    const float y1[8] = {yacc[2][0], yacc[2][1], yacc[2][2], yacc[2][3],
+                         yacc[3][0], yacc[3][1], yacc[3][2], yacc[3][3]};
+    u32x2_t cw;
+    if (__builtin_amdgcn_readfirstlane(clamp_needed(clip_allows_no_clamp, sc.s32) ? 1 : 0)) {
+      cw = u32x2_t{quant8<true>(y0, inv_y), quant8<true>(y1, inv_y)};
+    } else {
+      cw = u32x2_t{quant8<false>(y0, inv_y), quant8<false>(y1, inv_y)};
+    }
+    const int row = 16 * w + lr;
+    __builtin_nontemporal_store(
+        cw, reinterpret_cast<u32x2_t *>(codes + tok * (int64_t)(n / 2) + row * (N2 / 2) + g * 8));
+    if (w == 0 && lane == 0) store_scale(scales, tok, sc, scale_fp16);
+    if constexpr (YDBG) {
+      float4 *yp = reinterpret_cast<float4 *>(ydbg + tok * (int64_t)n + row * N2 + 16 * g);
+#pragma unroll
+      for (int a = 0; a < C::NT; ++a)
+        yp[a] = make_float4(__builtin_ldexpf(yacc[a][0], ty_dbg), __builtin_ldexpf(yacc[a][1], ty_dbg),
+                            __builtin_ldexpf(yacc[a][2], ty_dbg), __builtin_ldexpf(yacc[a][3], ty_dbg));
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // pair kernel: a workgroup of two waves per token, each wave one half of the columns
 // ------------------------------------------------------------------------------------
 // A column half of Y needs only the same column half of Z (stage 2 mixes rows, not
@@ -1931,6 +2140,20 @@ hipError_t launch_stream(const kq_plan *p, const void *X, int64_t T, int64_t ldx
   return hipGetLastError();
 }
 
+template <int N1>
+hipError_t launch_rsplit(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
+                         void *scales, float *y_debug, void *, hipStream_t stream) {
+  using C = RsplitCfg<N1>;
+  const int grid = (int)(T < (int64_t)p->grid_cap ? T : (int64_t)p->grid_cap);
+  auto k = y_debug ? &kq_rsplit_kernel<N1, true> : &kq_rsplit_kernel<N1, false>;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream, static_cast<const __bf16 *>(X), T,
+                     ldx, static_cast<const f16x8 *>(p->p2op), static_cast<const f16x8 *>(p->p1op),
+                     p->c, p->p1_exp + p->p2_exp, p->c_absmax, p->clip,
+                     p->scale_dtype == KQ_FP16 ? 1 : 0, p->clip >= 0.935f ? 1 : 0, codes, scales,
+                     y_debug);
+  return hipGetLastError();
+}
+
 template <int N1, int N2, int BITS = 4>
 hipError_t launch_colsc(const kq_plan *p, const void *X, int64_t T, int64_t ldx, uint8_t *codes,
                         void *scales, float *y_debug, void *, hipStream_t stream) {
@@ -2006,6 +2229,11 @@ hipError_t launch_rows(const kq_plan *p, const void *X, int64_t T, int64_t ldx, 
                    &launch_stream<A, B, true>,                                         \
                    reinterpret_cast<const void *>(&kq_stream_kernel<A, B, true, false>), \
                    "fused_mfma_bf16_stream_" #A "x" #B "_c", nullptr, 0, 0, 0, true}
+// the row split with a per-channel scale (n2 = 64): a token's 16-row blocks on their own waves
+#define KQ_RSPLIT(A)                                                                   \
+  kq_fused_variant{A, 64, true, KQ_SPLIT_RSPLIT, 4, 64, RsplitCfg<A>::THREADS, &launch_rsplit<A>, \
+                   reinterpret_cast<const void *>(&kq_rsplit_kernel<A>),              \
+                   "fused_mfma_bf16_rsplit_" #A "x64_c", nullptr, 0, 0, 0, true}
 // the column split with a per-channel scale (x^ rounded once, Z in fp16)
 #define KQ_COLSC(A, B)                                                                 \
   kq_fused_variant{A, B, true, KQ_SPLIT_COLS, 4, 32, ColsCCfg<A, B>::THREADS, &launch_colsc<A, B>, \
@@ -2091,6 +2319,7 @@ const kq_fused_variant kVariants[] = {
     KQ_DEEP(64, 128, false, ""), KQ_DEEP(64, 64, false, ""), KQ_DEEP(64, 64, true, "_c"),
     KQ_STREAM(16, 64), KQ_STREAM(32, 64), KQ_STREAM(48, 64), KQ_STREAM(64, 64),
     KQ_STREAM_C(16, 64), KQ_STREAM_C(32, 64), KQ_STREAM_C(48, 64), KQ_STREAM_C(64, 64),
+    KQ_RSPLIT(16), KQ_RSPLIT(32), KQ_RSPLIT(48), KQ_RSPLIT(64),
     // INT8 codes (stream kernel shapes)
     KQ_STREAM8(16, 64, false, ""), KQ_STREAM8(32, 64, false, ""), KQ_STREAM8(48, 64, false, ""),
     KQ_STREAM8(64, 64, false, ""), KQ_STREAM8(16, 128, false, ""), KQ_STREAM8(32, 128, false, ""),

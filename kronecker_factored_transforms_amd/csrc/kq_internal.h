@@ -81,7 +81,7 @@ inline size_t kq_ws_bytes(const kq_plan *p, int64_t T) {
 // output dimension, Y through the workspace, a second kernel quantizes).
 enum { KQ_SPLIT_REG1 = 1, KQ_SPLIT_REG2 = 2, KQ_SPLIT_COLS = 3, KQ_SPLIT_DEEP = 4,
        KQ_SPLIT_STREAM = 5, KQ_SPLIT_PAIR = 6, KQ_SPLIT_ROWS = 7, KQ_SPLIT_TWOSTAGE = 8,
-       KQ_SPLIT_PTILE = 9 };
+       KQ_SPLIT_PTILE = 9, KQ_SPLIT_RSPLIT = 10 };
 
 struct kq_fused_variant {
   int n1, n2;

@@ -46,11 +46,12 @@ def test_exact_factors_reproduce_permuted_input(gpu, name, kind):
 
 
 @pytest.mark.parametrize("flags,kernel", [(B.KQ_FLAG_SPLIT_REG1, "fused_mfma_bf16_reg1_64x64_c"),
-                                          (0, "fused_mfma_bf16_cols_64x64_c")])
+                                          (B.KQ_FLAG_SPLIT_COLS, "fused_mfma_bf16_cols_64x64_c"),
+                                          (0, "fused_mfma_bf16_rsplit_64x64_c")])
 def test_power_of_two_channel_scale_is_exact(gpu, flags, kernel):
     """c = powers of two with identity factors: x*c has x's 8 significant bits.
     - The register kernels split x*c into bf16 hi + lo: lo is zero and Y is x*c exactly.
-    - The stream and column kernels run on fp16 operands after a per-token power-of-two
+    - The stream, column and row-split kernels run on fp16 operands after a per-token power-of-two
       scale 2^s (s = 0 unless the bound max|x| max|c| leaves [2^-8, 2^15)): Y is x*c
       exactly wherever fp16 holds x*c 2^s exactly (at or above 2^-17, where its subnormal
       grid is still fine enough for 8 bits), and within half of fp16's smallest step 2^-25
@@ -68,9 +69,9 @@ def test_power_of_two_channel_scale_is_exact(gpu, flags, kernel):
     xf = S.bf16_bits_to_f32(inp.X).astype(np.float64)
     x = xf * c.astype(np.float64)
     yc = y.cpu().numpy().astype(np.float64)
-    if flags:
+    if "reg1" in kernel:  # the hi / lo split
         assert np.array_equal(yc, x)
-    else:
+    else:  # fp16 operands
         bound = (np.abs(xf).max(axis=1).astype(np.float32) * np.float32(np.abs(c).max())).astype(np.float64)
         e = np.floor(np.log2(bound))
         s = np.where((e >= -8) & (e < 15), 0.0, np.clip(14 - e, -126, 127))[:, None]
@@ -261,12 +262,12 @@ def test_small_batches_switch_to_the_pair_split(gpu):
                                plan.clip)
 
 
-@pytest.mark.parametrize("name,small", [("attn_n4096", "fused_mfma_bf16_cols_64x64_c"),
+@pytest.mark.parametrize("name,small", [("attn_n4096", "fused_mfma_bf16_rsplit_64x64_c"),
                                         ("hidden_n7168", "fused_mfma_bf16_cols_64x112")])
-def test_small_batches_without_a_pair_split_use_the_column_split(gpu, name, small):
-    """Stream plans with no pair variant (with c, or rows of 112 values) switch to the
-    column split for small batches; both sides of the switch match the oracle, and the
-    same tokens give the same codes on both sides."""
+def test_small_batches_without_a_pair_split_use_the_row_or_column_split(gpu, name, small):
+    """Stream plans with no pair variant switch to another split for small batches: the row
+    split with c, the column split for rows of 112 values; both sides of the switch match
+    the oracle, and the same tokens give the same codes on both sides."""
     import torch
     inp = S.make(name, T=8)
     plan, _ = K.make_plan(inp)
@@ -385,7 +386,7 @@ def test_fp32_step_with_overflowing_reciprocal_is_an_underflow(gpu, name, T, fla
 # must still match the oracle, and both kernels of a plan give the same codes.
 @pytest.mark.parametrize("name,T,kernel", [
     ("attn_n4096", 1100, "fused_mfma_bf16_stream_64x64_c"),
-    ("attn_n4096", 300, "fused_mfma_bf16_cols_64x64_c"),
+    ("attn_n4096", 300, "fused_mfma_bf16_rsplit_64x64_c"),
     ("down_proj_n14336", 301, "fused_mfma_bf16_cols_112x128_c"),
     ("ffn_n11008", 203, "fused_mfma_bf16_cols_86x128_c")])
 def test_with_c_kernels_scale_z_into_fp16_range(gpu, name, T, kernel):
@@ -401,5 +402,5 @@ def test_with_c_kernels_scale_z_into_fp16_range(gpu, name, T, kernel):
     K.check_plan_against_oracle(inp, plan, codes, scales, y)
     if name == "attn_n4096" and T > 1024:   # the small-batch split writes the same codes
         c2, s2 = K.run(plan, X[:1000], y_debug=False)
-        assert plan.kernel_for(1000) == "fused_mfma_bf16_cols_64x64_c"
+        assert plan.kernel_for(1000) == "fused_mfma_bf16_rsplit_64x64_c"
         assert torch.equal(c2, codes[:1000]) and torch.equal(s2, scales[:1000])

@@ -1,6 +1,6 @@
 """Every fused work split (one or two waves per token with the token in registers, the
-column kernel with the token in LDS, the DMA-fed stream and pair kernels) against the
-oracle, on shapes around the workloads:
+column kernel with the token in LDS, the DMA-fed stream and pair kernels, the row split
+with c) against the oracle, on shapes around the workloads:
 square and non-square factors, with and without the per-channel scale, ragged T."""
 from dataclasses import replace
 
@@ -14,9 +14,10 @@ pytestmark = pytest.mark.gpu
 
 SPLITS = {"reg1": B.KQ_FLAG_SPLIT_REG1, "reg2": B.KQ_FLAG_SPLIT_REG2, "cols": B.KQ_FLAG_SPLIT_COLS,
           "deep": B.KQ_FLAG_SPLIT_DEEP, "stream": B.KQ_FLAG_SPLIT_STREAM,
-          "pair": B.KQ_FLAG_SPLIT_PAIR}
+          "pair": B.KQ_FLAG_SPLIT_PAIR, "rsplit": B.KQ_FLAG_SPLIT_RSPLIT}
 DEEP_SHAPES = {(64, 128, False), (64, 64, False), (64, 64, True)}
 SHAPES = [(64, 128, False), (64, 128, True), (64, 64, False), (64, 64, True), (32, 128, False),
+          (32, 64, True), (48, 64, True),
           (48, 128, True), (16, 64, True), (48, 64, False), (32, 32, True), (16, 32, False),
           (112, 128, False), (112, 128, True), (96, 128, False), (128, 128, True), (80, 128, False),
           (128, 160, False), (128, 224, False), (128, 256, False), (128, 224, True),
@@ -37,6 +38,8 @@ def _available(n1, n2, split, with_c=False):
         return split == "cols" or (split == "stream" and (n1, n2, with_c) == (64, 112, False))
     if n2 not in (32, 64, 128):  # e.g. 64 x 96: only the column kernel
         return split == "cols"
+    if split == "rsplit":
+        return with_c and n2 == 64
     if split == "deep":
         return (n1, n2, with_c) in DEEP_SHAPES
     if split == "stream":
