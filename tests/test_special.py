@@ -404,3 +404,23 @@ def test_with_c_kernels_scale_z_into_fp16_range(gpu, name, T, kernel):
         c2, s2 = K.run(plan, X[:1000], y_debug=False)
         assert plan.kernel_for(1000) == "fused_mfma_bf16_rsplit_64x64_c"
         assert torch.equal(c2, codes[:1000]) and torch.equal(s2, scales[:1000])
+
+
+@pytest.mark.parametrize("name", ["hidden_n8192", "attn_n4096", "hidden_n7168", "kv_h8_d128"])
+def test_codes_do_not_depend_on_the_batch_size(gpu, name):
+    """A default plan may run another work split for small batches (include/kq.h,
+    kq_plan_kernel_name_for: both compute the same Y and codes). The same tokens in a
+    small and a large call give bit-identical Y, codes and steps."""
+    import torch
+    small, big = 300, 2200
+    inp = S.make(name, T=big)
+    X, P1, P2, c = K.device_inputs(inp)
+    if inp.wl.per_row:
+        plan = B.Plan(None, P2, None, inp.alpha, inp.wl.scale_dtype, n1=inp.wl.n1)
+    else:
+        plan = B.Plan(P1, P2, c, inp.alpha, inp.wl.scale_dtype)
+    print(f"[batch] {name}: T={small} {plan.kernel_for(small)}, T={big} {plan.kernel_for(big)}", flush=True)
+    a = K.run(plan, X[:small].contiguous(), y_debug=True)
+    b = K.run(plan, X, y_debug=True)
+    assert torch.equal(a[0], b[0][:small]) and torch.equal(a[1], b[1][: a[1].shape[0]])
+    assert torch.equal(a[2], b[2][:small])
