@@ -105,18 +105,23 @@ __global__ __launch_bounds__(512) void kq_f32_kernel(
 
   const int64_t stride = (int64_t)gridDim.x * C::WAVES;
   int64_t tok = (int64_t)blockIdx.x * C::WAVES + wave;
-  // the factor operands reach LDS by DMA, issued before the first token's DMA: a wave
-  // waits for its share of them, not for its token, before the barrier, so that each wave
-  // starts on its token as soon as that token has landed
+  // the factor operands reach LDS by DMA, each wave copying its share, before any token
   dma_copy(p2op, s_ops, 2 * C::P2_OPS * 16, wave, C::WAVES, lane);
   dma_copy(p1op, s_ops + 2 * C::P2_OPS, 2 * C::P1_OPS * 16, wave, C::WAVES, lane);
-  if (tok < T) {
-    dma_tile(tok);
-    wait_and_fence<wait_vm_imm(C::LOADS)>();  // all but the token's own DMAs
+  // The first half of the waves issues its token's DMA at once and waits for it before the
+  // barrier; the second half issues its own only after the barrier, i.e. once the first
+  // half's tokens have landed. The first tokens then arrive sooner and half the CU computes
+  // while the rest load (measured on MI355X: 6 % on 2048 fp32 tokens of 64x64, 0.5 % on
+  // 16384 tokens of 64x128, neutral on 2048 tokens with c).
+  if (wave < C::WAVES / 2) {
+    if (tok < T) dma_tile(tok);
+    wait_and_fence<kWaitVm0>();
+    lds_barrier();  // operands visible to every wave
   } else {
     wait_and_fence<kWaitVm0>();
+    lds_barrier();  // operands visible to every wave
+    if (tok < T) dma_tile(tok);
   }
-  lds_barrier();  // operands visible to every wave
   const bf16x8 *p2h = s_ops, *p2l = s_ops + C::P2_OPS;
   const bf16x8 *p1h = s_ops + 2 * C::P2_OPS, *p1l = p1h + C::P1_OPS;
 

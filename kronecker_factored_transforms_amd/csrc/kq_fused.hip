@@ -400,10 +400,7 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
   for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
     for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
-  // P2's operands (and c) reach LDS by DMA, issued before the first token's DMA: a wave
-  // waits for its share of them, not for its token, before the barrier, so that each wave
-  // starts on its token as soon as that token has landed (with one token per wave, as for
-  // a few thousand tokens, the CU no longer waits for all eight)
+  // P2's operands (and c) reach LDS by DMA, each wave copying its share, before any token
   dma_copy(p2op, s_p2, C::P2_BYTES, wave, C::WAVES, lane);
   if constexpr (HAS_C) {
     // c in 16-byte units of 4 channels, unit u of row R at R * 4 N2 + ((u ^ (R % 16)) * 16):
@@ -416,13 +413,20 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
       dma16<false>(csrc, (uint32_t)(R * 4 * N2 + ((pos ^ (R % 16)) * 16)), lds_addr(s_c + j * 1024));
     }
   }
-  if (tok < T) {
-    dma_tile(tok);
-    wait_and_fence<wait_vm_imm(C::LOADS)>();  // all but the token's own DMAs
+  // The first half of the waves issues its token's DMA at once and waits for it before the
+  // barrier; the second half issues its own only after the barrier, i.e. once the first
+  // half's tokens have landed. The first tokens then arrive sooner and half the CU computes
+  // while the rest load (measured on MI355X: 6 % on 2048 fp32 tokens of 64x64, 0.5 % on
+  // 16384 tokens of 64x128, neutral on 2048 tokens with c).
+  if (wave < C::WAVES / 2) {
+    if (tok < T) dma_tile(tok);
+    wait_and_fence<kWaitVm0>();
+    lds_barrier();  // P2 (and c) visible to every wave
   } else {
     wait_and_fence<kWaitVm0>();
+    lds_barrier();  // P2 (and c) visible to every wave
+    if (tok < T) dma_tile(tok);
   }
-  lds_barrier();  // P2 (and c) visible to every wave
   const bf16x8 *sp2 = reinterpret_cast<const bf16x8 *>(s_p2);
 
   // codes of the previous token, stored one step late (8 or 4 values per dword)
