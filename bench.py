@@ -201,6 +201,10 @@ def bench_int4_gemm(args, torch, B, dev):
     tops = ops / us / 1e6
     log(f"[bench] int4 gemm T={T} N={N} K={K}: {us:.2f} us/launch, {tops:.0f} TOP/s, "
         f"{byts / us / 1e3:.0f} GB/s of operands+output")
+    del sets
+    ref = int8_library_gemm(torch, dev, T, N, K, args.steps, args.warmup)
+    log(f"[bench] library reference: torch._int_mm (int8 x int8 -> int32, one code per byte) "
+        f"{ref['us']:.2f} us, {ref['tops']:.0f} TOP/s; kq_int4_gemm is {ref['us'] / us:.2f}x as fast")
     print(json.dumps({
         "metric": "INT4 x INT4 GEMM (kq_int4_gemm) TOP/s", "value": tops, "unit": "TOP/s",
         "n_gpus": 1, "steps": K_steps, "warmup": args.warmup,
@@ -210,7 +214,34 @@ def bench_int4_gemm(args, torch, B, dev):
                    "buffer_sets": nsets},
         "roofline": {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": tops / PEAK_INT8_TOPS, "traffic": None, "kernel_avg_us": us},
+        "library_reference": {"op": "torch._int_mm (hipBLASLt int8)", "us": ref["us"],
+                              "value": ref["tops"], "unit": "TOP/s",
+                              "frac": ref["tops"] / PEAK_INT8_TOPS},
     }), flush=True)
+
+
+def int8_library_gemm(torch, dev, T, N, K, steps, warmup):
+    """The vendor library's int8 GEMM on the same shape, operands already one int8 per byte
+    (what an INT4 GEMM would multiply after unpacking), timed like kq_int4_gemm."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    a = torch.randint(-128, 128, (T, K), dtype=torch.int8, device=dev, generator=g)
+    w = torch.randint(-128, 128, (N, K), dtype=torch.int8, device=dev, generator=g)
+    wt = w.t()
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, warmup // 4)):
+        c = torch._int_mm(a, wt)
+    n = max(5, steps // 4)
+    e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    e[0].record(stream)
+    for _ in range(n):
+        c = torch._int_mm(a, wt)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    del c
+    us = e[0].elapsed_time(e[1]) / n * 1e3
+    return {"us": us, "tops": 2.0 * T * N * K / us / 1e6}
 
 
 # Workloads timed beside the headline in the default run: the other gated and reported

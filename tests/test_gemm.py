@@ -1,7 +1,8 @@
 """GPU tests of the INT4 x INT4 consumer (kq_int4_gemm, through the C ABI).
 
 Parity: bit-exact against the oracle's integer product with the fp32 epilogue (every
-output dtype, both scale dtypes, ragged T and N around the 256 x 256 workgroup tile).
+output dtype, both scale dtypes, ragged T and N around the 256 x 256 workgroup tile, and
+exact multiples of it).
 End to end ("FlatQuant" page, Learning the affine transformation: (X P)(P^-1 W^T) =
 X W^T): activations through a kq plan with (P1, P2), weight rows through a kq plan with
 (P1^-T, P2^-T), then the INT4 GEMM; the result must equal the oracle GEMM of the same
@@ -32,7 +33,8 @@ def _to_np(out):
 
 
 @pytest.mark.parametrize("T,N,Kc", [(1, 4, 256), (37, 52, 512), (256, 256, 256),
-                                    (300, 520, 1024), (513, 260, 8192)])
+                                    (300, 520, 1024), (512, 512, 512), (513, 260, 8192),
+                                    (769, 772, 1024)])
 @pytest.mark.parametrize("out_dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("scale_dtype", ["fp16", "fp32"])
 def test_int4_gemm_bit_exact(gpu, T, N, Kc, out_dtype, scale_dtype):
