@@ -68,12 +68,14 @@ def traffic_from_profile(workload: str, kernel: str):
     return float(m_b.group(1))
 
 
-def hbm_probe(torch, dev, achieved_gbs):
+def hbm_probe(torch, dev, achieved_gbs, small_kernel_us=None):
     """What library kernels reach on this machine's HBM, measured beside the transform: a plain
     device-to-device copy (1 byte written per byte read), and a 4:1 read:write stream, the
     transform's own ratio (the sum of four 256 MiB quarters of a bf16 tensor into a fifth:
     1 GiB in, 256 MiB out). 1 GiB source, beyond the 256 MB Infinity Cache; 3 untimed and
-    10 timed runs each. The transform's achieved rate is reported as a fraction of both."""
+    10 timed runs each. The transform's achieved rate is reported as a fraction of both.
+    Then the 4:1 stream at the byte volume of the 2048-token attention-input workload, whose
+    time per call is set beside that workload's (small_kernel_us)."""
     src = torch.empty(2 ** 29, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
     dst = torch.empty_like(src)
     red = torch.empty(2 ** 27, dtype=torch.bfloat16, device=dev)
@@ -93,11 +95,31 @@ def hbm_probe(torch, dev, achieved_gbs):
         torch.cuda.synchronize()
         res[name + "_GBps"] = round(nbytes * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
     del src, dst, red
+    # the same 4:1 stream at the volume of 2048 tokens of n = 4096 (16 MiB in, 4 MiB out),
+    # where launch and ramp costs weigh: 80 buffer sets (1.6 GiB) rotated past the Infinity
+    # Cache, 100 untimed and 1000 timed launches, like the workloads' own timing
+    nsets = 80
+    srcs = [torch.empty(2 ** 23, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for _ in range(nsets)]
+    reds = [torch.empty(2 ** 21, dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    for i in range(100):
+        torch.sum(srcs[i % nsets].view(4, -1), dim=0, out=reds[i % nsets])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(1000):
+        torch.sum(srcs[i % nsets].view(4, -1), dim=0, out=reds[i % nsets])
+    e1.record()
+    torch.cuda.synchronize()
+    res["read4_write1_16MiB_us"] = round(e0.elapsed_time(e1), 3)  # ms per 1000 = us per call
+    del srcs, reds
+    if small_kernel_us:
+        res["attn_n4096_us_over_small_stream"] = round(small_kernel_us / res["read4_write1_16MiB_us"], 3)
     res["kernel_frac_of_copy"] = round(achieved_gbs / res["copy_GBps"], 3)
     res["kernel_frac_of_read4_write1"] = round(achieved_gbs / res["read4_write1_GBps"], 3)
     res["kind"] = "torch copy_ and a sum over the outer dimension of 4 (library kernels), same box"
     log(f"[bench] HBM probe: copy {res['copy_GBps']:.0f} GB/s, 4:1 stream {res['read4_write1_GBps']:.0f} GB/s; "
-        f"the transform reaches {res['kernel_frac_of_copy']:.2f} and {res['kernel_frac_of_read4_write1']:.2f} of them")
+        f"the transform reaches {res['kernel_frac_of_copy']:.2f} and {res['kernel_frac_of_read4_write1']:.2f} of them; "
+        f"4:1 stream of 16 MiB in + 4 MiB out: {res['read4_write1_16MiB_us']:.2f} us per call")
     return res
 
 
@@ -497,7 +519,10 @@ def main():
             extras[name], _ = measure(torch, B, S, dev, name, args, min_warm_ms=20.0,
                                       graph=name.startswith("decode"))
 
-    probe = hbm_probe(torch, dev, head["roofline"]["achieved"]) if run_extra else None
+    probe = None
+    if run_extra:
+        small = extras.get("attn_n4096", {}).get("roofline", {}).get("kernel_avg_us")
+        probe = hbm_probe(torch, dev, head["roofline"]["achieved"], small)
 
     cpu = None
     if not args.no_cpu_baseline:
