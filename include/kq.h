@@ -255,6 +255,27 @@ kq_status kq_int4_gemm(const uint8_t *xq, int64_t ldxq, const void *sx, int64_t 
                        kq_dtype scale_dtype, kq_dtype out_dtype, void *out, int64_t ldo,
                        void *stream);
 
+/*
+ * kq_weight_factor -- the weight-side factor (P^-1)^T of one activation factor P, for the
+ * weight rows of a W4A4 layer. The layer computes (X P)(P^-1 W^T) ("FlatQuant" page,
+ * Learning the affine transformation); with P = P1 (x) P2 ("Kronecker Product" page: the
+ * inverse and the transpose of a Kronecker product are the Kronecker products of the
+ * factors' inverses and transposes), row j of W P^-T is w_j ((P1^-1)^T (x) (P2^-1)^T), so
+ * kq_create with the factors kq_weight_factor(P1) and kq_weight_factor(P2), no c and clip
+ * logit +INFINITY, quantizes W's rows for kq_int4_gemm. (A per-channel scale c of the
+ * activations would be divided out of W's columns before that; the pages merge it into the
+ * preceding weight instead.)
+ *   P      device, m x m row-major, dtype KQ_BF16 or KQ_FP32 (aligned to its element).
+ *   out    device, m x m row-major, same dtype; may be P itself.
+ *   m      1 .. 1024.
+ * Computed on the GPU in fp64 (Gauss-Jordan elimination with partial pivoting on
+ * [P^T | I]) and rounded once, to nearest even, to dtype. A plan-time call like kq_create:
+ * it allocates a 16 m^2-byte device workspace and frees it, and it synchronizes `stream`.
+ * Errors: INVALID_ARG (NULL, m out of range, dtype, or P singular: a zero pivot),
+ * ALIGNMENT, OUT_OF_MEMORY, HIP.
+ */
+kq_status kq_weight_factor(const void *P, int m, kq_dtype dtype, void *out, void *stream);
+
 /* Free a plan and its device buffers. NULL is a no-op (returns KQ_OK). The caller must
  * make sure no enqueued kq_transform_quant on this plan is still running. */
 kq_status kq_destroy(kq_plan *plan);

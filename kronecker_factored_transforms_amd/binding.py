@@ -34,7 +34,7 @@ EXPORTS = (
     "kq_choose_factors", "kq_create", "kq_create_ex", "kq_transform_quant", "kq_destroy",
     "kq_plan_clip_ratio", "kq_plan_kernel_name", "kq_plan_kernel_name_for", "kq_status_string",
     "kq_version", "kq_int4_gemm", "kq_workspace_size", "kq_transform_quant_ws",
-    "kq_transform_quant_noalloc",
+    "kq_transform_quant_noalloc", "kq_weight_factor",
 )
 KQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
     L.kq_status_string.restype = ctypes.c_char_p
     L.kq_int4_gemm.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i32, i32, vp, i64, vp]
     L.kq_int4_gemm.restype = i32
+    L.kq_weight_factor.argtypes = [vp, i32, i32, vp, vp]
+    L.kq_weight_factor.restype = i32
     L.kq_version.argtypes = []
     L.kq_version.restype = i32
     _lib = L
@@ -196,6 +198,27 @@ def kq_int4_gemm(xq, ldxq, sx, T, wq, ldwq, sw, N, K, scale_dtype, out_dtype, ou
                             int(N), int(K), _dtype_code(scale_dtype), _dtype_code(out_dtype),
                             _ptr(out), int(ldo), _stream(stream))
     _check(st, "kq_int4_gemm")
+
+
+def kq_weight_factor(P, m, dtype, out, stream=None) -> None:
+    _check(lib().kq_weight_factor(_ptr(P), int(m), _dtype_code(dtype), _ptr(out), _stream(stream)),
+           "kq_weight_factor")
+
+
+def weight_factor(P, out=None, stream=None):
+    """(P^-1)^T of a square bf16 or fp32 factor on the GPU: the factor that the weight rows of
+    a W4A4 layer are transformed with (see kq_weight_factor in include/kq.h)."""
+    import torch
+    if P.dim() != 2 or P.shape[0] != P.shape[1] or not P.is_contiguous():
+        raise ValueError("P must be a contiguous square matrix")
+    if P.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("P must be bf16 or fp32")
+    if out is None:
+        out = torch.empty_like(P)
+    elif out.shape != P.shape or out.dtype != P.dtype or not out.is_contiguous() or out.device != P.device:
+        raise ValueError("out must be a contiguous tensor of P's shape, dtype and device")
+    kq_weight_factor(P, P.shape[0], P.dtype, out, stream)
+    return out
 
 
 def int4_gemm(xq, sx, wq, sw, out_dtype="fp32", out=None, stream=None):

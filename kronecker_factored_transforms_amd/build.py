@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkq.so")
-SOURCES = ["kq_api.hip", "kq_fused.hip", "kq_large.hip", "kq_f32.hip", "kq_generic.hip", "kq_gemm.hip"]
+SOURCES = ["kq_api.hip", "kq_fused.hip", "kq_large.hip", "kq_f32.hip", "kq_generic.hip", "kq_gemm.hip",
+           "kq_weight.hip"]
 ARCH = os.environ.get("KQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -121,7 +121,7 @@ kq_status scratch_address(int dev, void **out) {
 
 extern "C" {
 
-int kq_version(void) { return 10100; }
+int kq_version(void) { return 10200; }
 
 const char *kq_status_string(kq_status s) {
   switch (s) {

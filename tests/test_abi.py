@@ -161,6 +161,17 @@ def test_int4_gemm_rejects_bad_arguments_before_touching_the_gpu(L):
         assert _gemm_raw(L, **kw) == B.KQ_ERR_ALIGNMENT, kw
 
 
+def test_weight_factor_rejects_bad_arguments_before_touching_the_gpu(L):
+    ok = dict(P=0x1000, m=64, dtype=B.KQ_BF16, out=0x2000)
+    for kw in (dict(P=None), dict(out=None), dict(m=0), dict(m=1025), dict(dtype=B.KQ_FP16),
+               dict(dtype=9)):
+        a = {**ok, **kw}
+        assert L.kq_weight_factor(a["P"], a["m"], a["dtype"], a["out"], None) == B.KQ_ERR_INVALID_ARG, kw
+    for kw in (dict(P=0x1001), dict(dtype=B.KQ_FP32, out=0x2002)):
+        a = {**ok, **kw}
+        assert L.kq_weight_factor(a["P"], a["m"], a["dtype"], a["out"], None) == B.KQ_ERR_ALIGNMENT, kw
+
+
 def test_host_tensors_are_refused_before_any_call():
     import torch
     with pytest.raises(ValueError):
@@ -183,6 +194,7 @@ int main(void) {
   if (kq_create(&plan, 3, 3, KQ_BF16, KQ_FP16, (const void *)16, (const void *)16, NULL,
                 1.0f, NULL) != KQ_ERR_INVALID_ARG || plan != NULL) return 4;
   if (kq_destroy(NULL) != KQ_OK) return 5;
+  if (kq_weight_factor(NULL, 4, KQ_BF16, NULL, NULL) != KQ_ERR_INVALID_ARG) return 6;
   printf("ok %d %d\n", n1, n2);
   return 0;
 }

@@ -1,4 +1,5 @@
-"""GPU tests of the INT4 x INT4 consumer (kq_int4_gemm, through the C ABI).
+"""GPU tests of the weight side: the INT4 x INT4 consumer (kq_int4_gemm) and the weight-side
+factors (kq_weight_factor), through the C ABI.
 
 Parity: bit-exact against the oracle's integer product with the fp32 epilogue (every
 output dtype, both scale dtypes, ragged T and N around the 256 x 256 workgroup tile, and
@@ -87,6 +88,63 @@ def test_int4_gemm_strided_rows_and_output(gpu):
     assert np.array_equal(out.cpu().numpy(), got)
 
 
+def _ulp(v, mant_bits):
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - mant_bits), 0.0)
+
+
+@pytest.mark.parametrize("m", [1, 8, 64, 112, 128, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_weight_factor_is_the_inverse_transpose(gpu, m, dtype):
+    """kq_weight_factor(P) against the oracle's inv(P)^T in fp64 (LAPACK's LU inverse, a
+    different algorithm from the library's Gauss-Jordan): every entry within half a unit
+    in the last place of the dtype, plus a margin for the fp64 error of the two
+    eliminations; non-symmetric P, so a missing transpose fails."""
+    import torch
+    rng = np.random.default_rng(m * 3 + (dtype == "bf16"))
+    P = np.eye(m) + 0.3 * rng.standard_normal((m, m)) / np.sqrt(m)
+    dev = "cuda:0"
+    if dtype == "bf16":
+        Pb = S.to_bf16_bits(P)
+        Pd = O.bf16_bits_to_f64(Pb)
+        tP = K.torch_from(Pb, "bf16").to(dev)
+    else:
+        Pf = P.astype(np.float32)
+        Pd = Pf.astype(np.float64)
+        tP = torch.from_numpy(Pf).to(dev)
+    out = B.weight_factor(tP)
+    torch.cuda.synchronize()
+    if dtype == "bf16":
+        got = O.bf16_bits_to_f64(out.cpu().view(torch.int16).numpy().view(np.uint16))
+    else:
+        got = out.cpu().numpy().astype(np.float64)
+    ref = O.weight_factors(Pd, Pd)[0]
+    assert m == 1 or not np.allclose(ref, ref.T)
+    tol = 0.5 * _ulp(ref, 7 if dtype == "bf16" else 23) + 1e-9 * np.abs(ref).max()
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), (float(err.max()), np.unravel_index(np.argmax(err - tol), err.shape))
+    # in place: out may be P itself
+    B.kq_weight_factor(tP, m, tP.dtype, tP)
+    torch.cuda.synchronize()
+    assert torch.equal(tP.cpu(), out.cpu())
+
+
+def test_weight_factor_refuses_singular_factors(gpu):
+    import torch
+    dev = "cuda:0"
+    with pytest.raises(B.KqError) as e:
+        B.weight_factor(torch.zeros((16, 16), dtype=torch.float32, device=dev))
+    assert e.value.status == B.KQ_ERR_INVALID_ARG
+    P = torch.eye(64, dtype=torch.bfloat16) + 0.05 * torch.randn(64, 64).to(torch.bfloat16)
+    P[5] = 0  # a zero row of P: column 5 of P^T stays zero through the elimination
+    with pytest.raises(B.KqError) as e:
+        B.weight_factor(P.to(dev))
+    assert e.value.status == B.KQ_ERR_INVALID_ARG
+    # a regular factor afterwards still works
+    assert torch.isfinite(B.weight_factor(torch.eye(8, device=dev)).float()).all()
+
+
 def test_w4a4_layer_end_to_end(gpu):
     """Activations (hidden 8192, 64 x 128 orthogonal factors) and a synthetic weight matrix
     through their transforms and the INT4 GEMM."""
@@ -95,14 +153,15 @@ def test_w4a4_layer_end_to_end(gpu):
     n, N = inp.wl.n, 512
     rng = np.random.default_rng(21)
     W = S.to_bf16_bits(rng.standard_normal((N, n)) / np.sqrt(n))
-    # weight-side factors from the bf16 activation factors, rounded to bf16 like them
-    Q1, Q2 = O.weight_factors(O.bf16_bits_to_f64(inp.P1), O.bf16_bits_to_f64(inp.P2))
-    Q1b, Q2b = S.to_bf16_bits(Q1), S.to_bf16_bits(Q2)
-
+    # weight-side factors (P^-1)^T from the library, from the bf16 activation factors
     dev = "cuda:0"
     plan_x, X = K.make_plan(inp)
-    plan_w = B.Plan(K.torch_from(Q1b, "bf16").to(dev), K.torch_from(Q2b, "bf16").to(dev), None,
-                    float("inf"), "fp16")
+    tQ1 = B.weight_factor(K.torch_from(inp.P1, "bf16").to(dev))
+    tQ2 = B.weight_factor(K.torch_from(inp.P2, "bf16").to(dev))
+    plan_w = B.Plan(tQ1, tQ2, None, float("inf"), "fp16")
+    # the oracle's own weight-side factors, rounded to bf16, for its reference path
+    Q1, Q2 = O.weight_factors(O.bf16_bits_to_f64(inp.P1), O.bf16_bits_to_f64(inp.P2))
+    Q1b, Q2b = S.to_bf16_bits(Q1), S.to_bf16_bits(Q2)
     xq, sx = plan_x(X)
     wq, sw = plan_w(K.torch_from(W, "bf16").to(dev))
     out = B.int4_gemm(xq, sx, wq, sw, "fp32")
