@@ -323,8 +323,8 @@ kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype
     // holds up to 65504); f is undone on Y.
     std::vector<uint16_t> e1((const uint16_t *)h1.data(), (const uint16_t *)h1.data() + (size_t)n1 * n1);
     std::vector<uint16_t> e2((const uint16_t *)h2.data(), (const uint16_t *)h2.data() + (size_t)n2 * n2);
-    if (fv->f16_ops) {
-      p->p1_exp = to_scaled_f16(e1);
+    if (fv->f16_ops || fv->f16_p2) {
+      if (fv->f16_ops) p->p1_exp = to_scaled_f16(e1);
       p->p2_exp = to_scaled_f16(e2);
       float cm = 0.f;
       for (int i = 0; i < n; ++i) cm = fmaxf(cm, fabsf(hc[i]));

@@ -101,6 +101,9 @@ struct kq_fused_variant {
   // both contractions on fp16 operands: the plan stores P1's and P2's operands as fp16
   // (scaled by 2^-p1_exp and 2^-p2_exp)
   bool f16_ops;
+  // stage 1 only on fp16 operands (the two-kernel design of Figure 8(c) with a per-channel
+  // scale): the plan stores P2's operands as fp16 (scaled by 2^-p2_exp), P1's as bf16
+  bool f16_p2;
 };
 
 // The variant for (n1, n2, has_c) with the given split (0: the default one) and code width,

@@ -36,7 +36,9 @@ namespace {
 // workgroup size of the large-factor kernels: one wave per 32 (padded) columns of n2
 constexpr int large_threads(int n2) { return 64 * ((n2 + 31) / 32); }
 
-template <int N1, int N2, bool HAS_C>
+// HILO: x c staged as bf16 hi / lo planes (Figure 8(b) with c); without it, one plane (bf16 x,
+// or fp16 x c for Figure 8(c) with c)
+template <int N1, int N2, bool HAS_C, bool HILO = HAS_C>
 struct LargeCfg {
   static_assert(N1 >= 16 && N1 <= 256, "n1 in [16, 256]");
   static_assert(N2 % 8 == 0 && N2 >= 32 && N2 <= 256, "n2 a multiple of 8 in [32, 256]");
@@ -49,7 +51,7 @@ struct LargeCfg {
   static constexpr int CH = N2 / 8;                 // 16-byte chunks per row of X
   static constexpr int CHP = N2P / 8;               // chunks per row in LDS
   static constexpr int ROW_CHUNKS = (CHP & (CHP - 1)) == 0 ? CHP : CHP + 1;
-  static constexpr int VPLANES = HAS_C ? 2 : 1;     // hi (+ lo) bf16 planes of x*c
+  static constexpr int VPLANES = HILO ? 2 : 1;      // hi (+ lo) bf16 planes of x*c
   static constexpr int PLANE = 32 * ROW_CHUNKS * 16;  // bytes of a 32-row plane in LDS
   static constexpr int STAGE = PLANE * VPLANES;       // one 32-row staging buffer
   static constexpr int STEP_CHUNKS = 32 * CH;         // 16-byte chunks of X per 32-row step
@@ -87,6 +89,27 @@ struct StepLoader {
         pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + r * N2 + cc[i] * 8);
       else
         pre[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // largest |x| of the loaded chunks (bf16 bit pattern of a non-negative value)
+  __device__ uint32_t absmax() const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) m = absmax_bf16(pre[i], m);
+    return m;
+  }
+  // x c as fp16 scaled by 2^sx (one plane; rows beyond n1 hold zeros), SCALE = (sx != 0)
+  template <bool SCALE>
+  __device__ void store_f16(unsigned char *stage, const float *cvec, int kk, int sx) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      if (!ok[i]) continue;
+      const int r = min(kk * 32 + row[i], N1 - 1);
+      const float4 *cp = reinterpret_cast<const float4 *>(cvec + r * N2 + cc[i] * 8);
+      const float4 a = cp[0], b = cp[1];
+      const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      *reinterpret_cast<f16x8 *>(stage + vchunk_off<C::CHP>(row[i], cc[i])) =
+          scale_round_f16<SCALE>(pre[i], cl, sx);
     }
   }
   __device__ void store(unsigned char *stage, const float *cvec, int kk) {
@@ -158,6 +181,39 @@ __device__ __forceinline__ void stage1_step(const unsigned char *stage, const bf
   z[1] = pack8(acc[0][1], acc[1][1]);
 }
 
+// Stage 1 of one 32-row step on fp16 operands (Figure 8(c) with a per-channel scale): the
+// staged x^ = fp16(x c 2^sx) times P2's fp16 operands (P2 2^-f2), accumulated in fp32, then
+// Z = Z' 2^e with e = f2 - sx (exact for normal results; e is wave-uniform, so the usual
+// e = 0 skips it), rounded once to bf16 for the workspace.
+template <class C>
+__device__ __forceinline__ void stage1_step_f16(const unsigned char *stage, const bf16x8 (&p2w)[C::KS][2],
+                                                int lane, int e, bf16x8 (&z)[2]) {
+  const int g = lane >> 4, lr = lane & 15;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const f16x8 b0 = __builtin_bit_cast(f16x8, p2w[ks][0]), b1 = __builtin_bit_cast(f16x8, p2w[ks][1]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const f16x8 a = *reinterpret_cast<const f16x8 *>(stage + vchunk_off<C::CHP>(mt * 16 + lr, ks * 4 + g));
+      acc[mt][0] = mfma_f16(a, b0, acc[mt][0]);
+      acc[mt][1] = mfma_f16(a, b1, acc[mt][1]);
+    }
+  }
+  if (e != 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][h][r] = __builtin_ldexpf(acc[mt][h][r], e);
+  }
+  z[0] = pack8(acc[0][0], acc[1][0]);
+  z[1] = pack8(acc[0][1], acc[1][1]);
+}
+
 template <class C>
 __device__ __forceinline__ void load_p2_block(const bf16x8 *p2op, int wave, int lane,
                                               bf16x8 (&p2w)[C::KS][2]) {
@@ -176,12 +232,18 @@ __device__ __forceinline__ void load_p2_block(const bf16x8 *p2op, int wave, int 
 // one barrier per item orders the buffers. Each wave keeps its 32-column block of P2 in
 // registers for the whole kernel. The workspace holds, per token, KK x ZT fragments of
 // 1 KiB: fragment (kk, m2) at ((t KK + kk) ZT + m2) KiB, lane L's 16 bytes at L * 16.
+// With a per-channel scale, stage 1 runs on fp16 operands: an item's x c is scaled by the
+// power of two sx that its bound max|x| max|c| picks (f16_scale_exp: 0 for ordinary
+// items). The rows of Z do not depend on each other, so the scale may differ between the
+// items of a token; it is undone exactly on Z. The waves publish the next item's |x|
+// maximum once its loads have landed, and a second barrier per item makes it visible.
 template <int N1, int N2, bool HAS_C>
-__global__ __launch_bounds__(large_threads(N2)) void kq_z_kernel(
+__global__ __launch_bounds__(large_threads(N2), HAS_C && N2 <= 224 ? 4 : 1) void kq_z_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx, const bf16x8 *__restrict__ p2op,
-    const float *__restrict__ cvec, bf16x8 *__restrict__ zws) {
-  using C = LargeCfg<N1, N2, HAS_C>;
+    const float *__restrict__ cvec, int p2_exp, float cmax, bf16x8 *__restrict__ zws) {
+  using C = LargeCfg<N1, N2, HAS_C, false>;
   __shared__ __align__(16) unsigned char s_stage[2 * C::STAGE];
+  __shared__ float s_xmax[2][C::W];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -194,19 +256,43 @@ __global__ __launch_bounds__(large_threads(N2)) void kq_z_kernel(
   const int64_t items = T * C::KK;
   int64_t it = blockIdx.x;
   if (it < items) ld.load(X, T, ldx, it / C::KK, (int)(it % C::KK));
+  // publish the loaded item's |x| maximum into s_xmax[b] (with c)
+  auto publish_xmax = [&](int b) {
+    const float v = wave_max_uniform(__uint_as_float(ld.absmax() << 16));
+    if (lane == 0) s_xmax[b][wave] = v;
+  };
+  if constexpr (HAS_C) {
+    if (it < items) publish_xmax(0);
+    lds_barrier();  // the first item's maxima visible
+  }
   for (int b = 0; it < items; it += gridDim.x, b ^= 1) {
     const int64_t t = it / C::KK;
     const int kk = (int)(it % C::KK);
     unsigned char *stage = s_stage + b * C::STAGE;
-    ld.store(stage, cvec, kk);
+    int sx = 0;
+    if constexpr (HAS_C) {
+      float xm = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::W; ++w) xm = fmaxf(xm, s_xmax[b][w]);
+      sx = __builtin_amdgcn_readfirstlane(f16_scale_exp(__fmul_rn(xm, cmax)));
+      if (sx == 0) ld.template store_f16<false>(stage, cvec, kk, 0);
+      else ld.template store_f16<true>(stage, cvec, kk, sx);
+    } else {
+      ld.store(stage, cvec, kk);
+    }
     lds_barrier();  // this buffer is complete; the other one is free (read an item ago)
     const int64_t nxt = it + gridDim.x;
     if (nxt < items) ld.load(X, T, ldx, nxt / C::KK, (int)(nxt % C::KK));
     bf16x8 z[2];
-    stage1_step<C, HAS_C>(stage, p2w, lane, z);
+    if constexpr (HAS_C) stage1_step_f16<C>(stage, p2w, lane, p2_exp - sx, z);
+    else stage1_step<C, false>(stage, p2w, lane, z);
     bf16x8 *zt = zws + ((t * C::KK + kk) * C::ZT + 2 * wave) * 64 + lane;
     zt[0] = z[0];
     zt[64] = z[1];
+    if constexpr (HAS_C) {
+      if (nxt < items) publish_xmax(b ^ 1);  // the next item's loads have landed
+      lds_barrier();  // its maxima visible (s_xmax[b ^ 1] was last read an item ago)
+    }
   }
 }
 
@@ -486,7 +572,7 @@ hipError_t launch_twostage(const kq_plan *p, const void *X, int64_t T, int64_t l
   const int g1 = (int)(items < (int64_t)p->grid_cap ? items : (int64_t)p->grid_cap);
   hipLaunchKernelGGL((kq_z_kernel<N1, N2, HAS_C>), dim3(g1), dim3(C::THREADS), 0, stream,
                      static_cast<const __bf16 *>(X), T, ldx, static_cast<const bf16x8 *>(p->p2op),
-                     p->c, z);
+                     p->c, p->p2_exp, p->c_absmax, z);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int g2 = (int)(T < (int64_t)p->grid_cap2 ? T : (int64_t)p->grid_cap2);
@@ -536,7 +622,7 @@ constexpr size_t z_bytes(int n1, int n2) {
                    reinterpret_cast<const void *>(&kq_z_kernel<A, B, HC>),                 \
                    "twostage_mfma_bf16_" #A "x" #B SUF,                                    \
                    reinterpret_cast<const void *>(&kq_zq_kernel<A, B, false, 4>),          \
-                   LargeCfg<A, B, HC>::THREADS, z_bytes(A, B), 0}
+                   LargeCfg<A, B, HC>::THREADS, z_bytes(A, B), 0, false, HC}
 #define KQ_PTILE(A, B, HC, SUF)                                                           \
   kq_fused_variant{A, B, HC, KQ_SPLIT_PTILE, 4, 32, LargeCfg<A, B, HC>::THREADS,              \
                    &launch_ptile<A, B, HC, 4>,                                             \

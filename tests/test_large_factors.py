@@ -125,9 +125,12 @@ def test_large_factor_workspace_errors(gpu, split):
     assert torch.equal(codes, ref_c) and torch.equal(scales, ref_s)
 
 
-@pytest.mark.parametrize("case", ["fp32_scales", "clip_zero", "zero_token"])
+@pytest.mark.parametrize("case", ["fp32_scales", "clip_zero", "zero_token", "item_scales"])
 @pytest.mark.parametrize("split", ["twostage", "ptile"])
 def test_large_factor_edge_cases(gpu, case, split):
+    """item_scales: within a token, one 32-row block of X is scaled by 2^60 and another by
+    2^-60 (exact in bf16), so that Figure 8(c)'s per-item fp16 scale of x c takes both
+    signs in one token and is undone on Z; a wrong exponent would be off by 2^120."""
     import math
     wl = _workload(168, 176, True)
     if case == "clip_zero":
@@ -138,7 +141,15 @@ def test_large_factor_edge_cases(gpu, case, split):
         X0 = inp.X.copy()
         X0[[0, 17, T - 1]] = 0
         inp.X = X0
-    sd = "fp32" if case == "fp32_scales" else inp.wl.scale_dtype
+    if case == "item_scales":
+        f = S.bf16_bits_to_f32(inp.X).reshape(T, 168, 176).astype(np.float64)
+        f[::3, 32:64] *= 2.0 ** 60
+        f[1::3, 96:128] *= 2.0 ** -60
+        f[2::3, 0:32] *= 2.0 ** 60
+        f[2::3, 128:160] *= 2.0 ** -60
+        inp.X = S.to_bf16_bits(f.reshape(T, -1))
+    # (the 2^60 blocks take steps beyond fp16's range: fp32 steps keep the codes nonzero)
+    sd = "fp32" if case in ("fp32_scales", "item_scales") else inp.wl.scale_dtype
     plan, X = K.make_plan(inp, scale_dtype=sd, flags=SPLITS[split])
     codes, scales, y = _run_checked(inp, plan, X)
     K.check_plan_against_oracle(inp, plan, codes, scales, y)
@@ -148,3 +159,7 @@ def test_large_factor_edge_cases(gpu, case, split):
         assert np.all(s == 0) and np.all(cn == 0)
     if case == "zero_token":
         assert np.all(s[[0, 17, T - 1]] == 0) and np.all(cn[[0, 17, T - 1]] == 0)
+    if case == "item_scales":
+        # (a 2^60 block sets its token's step; the token's other rows then quantize to 0)
+        assert np.all(np.isfinite(s)) and np.all(cn.any(axis=1))
+        assert np.all(s[0::3] > 1e15) and np.all(s[2::3] > 1e15) and np.all(s[1::3] < 1e3)
