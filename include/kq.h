@@ -28,6 +28,10 @@
  *   - A plan is immutable after kq_create: calls on one plan from several host threads
  *     or streams are safe. It belongs to the device that was current at kq_create, and
  *     kq_transform_quant returns KQ_ERR_INVALID_ARG when another device is current.
+ *   - Debug log: with KQ_LOG set in the environment (to anything but "" or "0"), every
+ *     plan creation (the kernel variant, grid, small-batch variant and workspace it
+ *     chose), every call and every error prints one line on stderr, prefixed "[kq]".
+ *     Host side only; the variable is read once per process.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -41,7 +45,17 @@ extern "C" {
 
 typedef struct kq_plan kq_plan;
 
-typedef enum kq_status {
+/* The enumerations are int-sized in C. Compiled as C++ (the library itself), they get int
+ * as their fixed underlying type, so that any int a C caller passes (say, an unknown
+ * status or dtype) is a valid value there too and is rejected by the checks rather than
+ * being undefined. */
+#ifdef __cplusplus
+#define KQ_ENUM_INT : int
+#else
+#define KQ_ENUM_INT
+#endif
+
+typedef enum kq_status KQ_ENUM_INT {
   KQ_OK = 0,
   KQ_ERR_INVALID_ARG = 1,   /* bad size, NULL pointer, NaN alpha, ...          */
   KQ_ERR_UNSUPPORTED = 2,   /* valid, but this build has no kernel for it     */
@@ -52,7 +66,7 @@ typedef enum kq_status {
                             /* the one given (see kq_workspace_size)           */
 } kq_status;
 
-typedef enum kq_dtype { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
+typedef enum kq_dtype KQ_ENUM_INT { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_dtype;
 
 /* Flags for kq_create_ex. At most one KQ_FLAG_SPLIT_* may be given, only for bf16 plans
  * (KQ_ERR_UNSUPPORTED when that split is not built for the shape). All variants compute

@@ -2,6 +2,8 @@
 // kernel selection and launch. See include/kq.h for the contract of each entry point.
 
 #include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -117,7 +119,28 @@ kq_status scratch_address(int dev, void **out) {
   return KQ_OK;
 }
 
+const char *dtype_name(kq_dtype d) {
+  return d == KQ_BF16 ? "bf16" : d == KQ_FP32 ? "fp32" : d == KQ_FP16 ? "fp16" : "?";
+}
+
 }  // namespace
+
+bool kq_log_on() {
+  static const bool on = [] {
+    const char *e = getenv("KQ_LOG");
+    return e && *e && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void kq_logf(const char *fmt, ...) {
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[kq] %s\n", line);
+}
 
 extern "C" {
 
@@ -200,9 +223,9 @@ fail:
   return st;
 }
 
-kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype scale_dtype,
-                       const void *P1, const void *P2, const float *c, float alpha, void *stream,
-                       unsigned flags) {
+static kq_status create_ex_impl(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
+                                kq_dtype scale_dtype, const void *P1, const void *P2,
+                                const float *c, float alpha, void *stream, unsigned flags) {
   if (!out) return KQ_ERR_INVALID_ARG;
   *out = nullptr;
   if (n1 < 1 || n2 < 1 || (int64_t)n1 * n2 > (1 << 24)) return KQ_ERR_INVALID_ARG;
@@ -456,6 +479,27 @@ fail:
   return st;
 }
 
+kq_status kq_create_ex(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype scale_dtype,
+                       const void *P1, const void *P2, const float *c, float alpha, void *stream,
+                       unsigned flags) {
+  const kq_status st =
+      create_ex_impl(out, n1, n2, x_dtype, scale_dtype, P1, P2, c, alpha, stream, flags);
+  if (kq_log_on()) {
+    if (st == KQ_OK) {
+      const kq_plan *p = *out;
+      kq_logf("create %dx%d x=%s steps=%s c=%s alpha=%g flags=0x%x: kernel %s, grid cap %d, "
+              "small batches (T < %lld) %s, workspace %zu + %zu B per token",
+              n1, n2, dtype_name(x_dtype), dtype_name(scale_dtype), c ? "yes" : "no",
+              (double)alpha, flags, p->kname, p->grid_cap, (long long)p->small_max_T,
+              p->small_launch ? p->small_kname : "-", p->ws_a_per_token, p->ws_b_per_token);
+    } else {
+      kq_logf("create %dx%d x=%s steps=%s c=%s flags=0x%x: %s", n1, n2, dtype_name(x_dtype),
+              dtype_name(scale_dtype), c ? "yes" : "no", flags, kq_status_string(st));
+    }
+  }
+  return st;
+}
+
 kq_status kq_create(kq_plan **out, int n1, int n2, kq_dtype x_dtype, kq_dtype scale_dtype,
                     const void *P1, const void *P2, const float *c, float alpha, void *stream) {
   return kq_create_ex(out, n1, n2, x_dtype, scale_dtype, P1, P2, c, alpha, stream, 0u);
@@ -472,7 +516,7 @@ kq_status kq_transform_quant(const kq_plan *p, const void *X, int64_t T, int64_t
   return kq_transform_quant_ws(p, X, T, ldx, codes, scales, y_debug, nullptr, 0, stream);
 }
 
-kq_status kq_transform_quant_ws(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
+static kq_status transform_impl(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
                                 uint8_t *codes, void *scales, float *y_debug, void *workspace,
                                 size_t workspace_bytes, void *stream) {
   if (!p || T < 0) return KQ_ERR_INVALID_ARG;
@@ -506,6 +550,19 @@ kq_status kq_transform_quant_ws(const kq_plan *p, const void *X, int64_t T, int6
     e = p->launch(p, X, T, ldx, codes, scales, y_debug, workspace, static_cast<hipStream_t>(stream));
   }
   return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
+kq_status kq_transform_quant_ws(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
+                                uint8_t *codes, void *scales, float *y_debug, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  const kq_status st = transform_impl(p, X, T, ldx, codes, scales, y_debug, workspace,
+                                      workspace_bytes, stream);
+  if (kq_log_on())
+    kq_logf("transform T=%lld ldx=%lld on %s%s, workspace %zu B: %s", (long long)T,
+            (long long)ldx, p ? kq_plan_kernel_name_for(p, T) : "(no plan)",
+            y_debug ? " with y_debug" : "", workspace ? workspace_bytes : (size_t)0,
+            kq_status_string(st));
+  return st;
 }
 
 kq_status kq_transform_quant_noalloc(const kq_plan *p, const void *X, int64_t T, int64_t ldx,

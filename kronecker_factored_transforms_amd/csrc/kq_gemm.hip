@@ -192,10 +192,10 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
-extern "C" kq_status kq_int4_gemm(const uint8_t *xq, int64_t ldxq, const void *sx, int64_t T,
-                                  const uint8_t *wq, int64_t ldwq, const void *sw, int64_t N,
-                                  int64_t K, kq_dtype scale_dtype, kq_dtype out_dtype, void *out,
-                                  int64_t ldo, void *stream) {
+static kq_status int4_gemm_impl(const uint8_t *xq, int64_t ldxq, const void *sx, int64_t T,
+                                const uint8_t *wq, int64_t ldwq, const void *sw, int64_t N,
+                                int64_t K, kq_dtype scale_dtype, kq_dtype out_dtype, void *out,
+                                int64_t ldo, void *stream) {
   if (T < 0 || N < 0 || K <= 0) return KQ_ERR_INVALID_ARG;
   if (scale_dtype != KQ_FP16 && scale_dtype != KQ_FP32) return KQ_ERR_INVALID_ARG;
   if (out_dtype != KQ_FP32 && out_dtype != KQ_BF16 && out_dtype != KQ_FP16)
@@ -234,4 +234,16 @@ extern "C" kq_status kq_int4_gemm(const uint8_t *xq, int64_t ldxq, const void *s
       break;
   }
   return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
+extern "C" kq_status kq_int4_gemm(const uint8_t *xq, int64_t ldxq, const void *sx, int64_t T,
+                                  const uint8_t *wq, int64_t ldwq, const void *sw, int64_t N,
+                                  int64_t K, kq_dtype scale_dtype, kq_dtype out_dtype, void *out,
+                                  int64_t ldo, void *stream) {
+  const kq_status st = int4_gemm_impl(xq, ldxq, sx, T, wq, ldwq, sw, N, K, scale_dtype, out_dtype,
+                                      out, ldo, stream);
+  if (kq_log_on())
+    kq_logf("int4_gemm T=%lld N=%lld K=%lld: %s", (long long)T, (long long)N, (long long)K,
+            kq_status_string(st));
+  return st;
 }

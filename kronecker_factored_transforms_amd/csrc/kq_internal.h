@@ -131,3 +131,9 @@ kq_launch_fn kq_generic_launcher(const char **name, const void **kernel_symbol);
 size_t kq_generic_lds_bytes(int n);
 int kq_generic_threads();
 int kq_generic_max_n();
+
+// ---- host-side debug log (kq_api.hip) ----
+// KQ_LOG set to anything but "" or "0" in the environment: one line per plan, call and
+// error on stderr, prefixed "[kq]". Read once; host code only.
+bool kq_log_on();
+void kq_logf(const char *fmt, ...) __attribute__((format(printf, 1, 2)));

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kWThreads) void kq_weight_factor_kernel(
 
 }  // namespace
 
-extern "C" kq_status kq_weight_factor(const void *P, int m, kq_dtype dtype, void *out, void *stream) {
+static kq_status weight_factor_impl(const void *P, int m, kq_dtype dtype, void *out, void *stream) {
   if (!P || !out || m < 1 || m > kMaxM) return KQ_ERR_INVALID_ARG;
   if (dtype != KQ_BF16 && dtype != KQ_FP32) return KQ_ERR_INVALID_ARG;
   const size_t es = dtype == KQ_BF16 ? 2 : 4;
@@ -147,5 +147,11 @@ extern "C" kq_status kq_weight_factor(const void *P, int m, kq_dtype dtype, void
   else if (hstatus != 0)
     st = KQ_ERR_INVALID_ARG;  // singular P
   if (hipFree(ws) != hipSuccess && st == KQ_OK) st = KQ_ERR_HIP;
+  return st;
+}
+
+extern "C" kq_status kq_weight_factor(const void *P, int m, kq_dtype dtype, void *out, void *stream) {
+  const kq_status st = weight_factor_impl(P, m, dtype, out, stream);
+  if (kq_log_on()) kq_logf("weight_factor m=%d: %s", m, kq_status_string(st));
   return st;
 }
