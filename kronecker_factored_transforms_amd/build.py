@@ -34,6 +34,7 @@ CFLAGS = [
     "-ffp-contract=off",          # every fp32 op in the quantizer rounds on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    "-Werror",                    # warnings fail the build
     "-Wno-unused-function",
     "-I", INCLUDE,
     "-I", CSRC,

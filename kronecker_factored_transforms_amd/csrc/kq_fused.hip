@@ -1619,7 +1619,8 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
         vt = s_v + ts * C::V_BYTES;
       }
       // (n2 = 256: a rolled loop, so that only one step's operands are in registers)
-#pragma unroll(C::P2_LDS || C::P2REG ? C::KSH : 1)
+      constexpr int KS_UNROLL = C::P2_LDS || C::P2REG ? C::KSH : 1;
+#pragma unroll KS_UNROLL
       for (int ks = h * C::KSH; ks < (h + 1) * C::KSH; ++ks) {
         bf16x8 b0, b1;
         if constexpr (C::P2_LDS) {
