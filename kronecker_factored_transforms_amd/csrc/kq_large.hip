@@ -4,9 +4,11 @@
 // falls back to tiled or two-stage kernels with extra global-memory traffic).
 //
 // Both designs run two kernels that pass an intermediate through a device workspace the
-// caller provides (kq_transform_quant_ws). They compute the same Y as the fused kernels,
-// with the same roundings: V P2 on bf16 MFMA with fp32 accumulation, Z rounded once to
-// bf16, P1^T Z on bf16 MFMA with fp32 accumulation, then the same quantizer.
+// caller provides (kq_transform_quant_ws). They round like the fused kernels: V P2 on the
+// matrix cores with fp32 accumulation, Z rounded once to bf16, P1^T Z on bf16 MFMA with
+// fp32 accumulation, then the same quantizer. With a per-channel scale, Figure 8(c) feeds
+// stage 1 with fp16 x c scaled by a power of two per 32-row item (and P2 as fp16), and
+// Figure 8(b) with x c split into bf16 hi + lo planes.
 //
 //  * Figure 8(c), "two stages with a trip to global memory" (kq_z_kernel + kq_zq_kernel):
 //    stage 1 computes Z = (x c) P2 for 32 rows of a token at a time and writes it to the
