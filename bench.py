@@ -44,13 +44,21 @@ KERNEL_SOURCES = ("kq_api.hip", "kq_internal.h", "kq_device.h", "kq_common.h", "
                   "kq_generic.hip", "kq_large.hip", "kq_f32.hip")
 
 
+def _code_text(src: str) -> str:
+    """A source without its comments and blank lines: edits to comments leave what a launch
+    reads and writes unchanged, so they do not invalidate a traffic profile."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def kernel_source_sha256() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         path = os.path.join(ROOT, "kronecker_factored_transforms_amd", "csrc", f)
         if os.path.exists(path):
-            with open(path, "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+            with open(path, encoding="utf-8") as fh:
+                h.update(f.encode() + b"\0" + _code_text(fh.read()).encode())
     return h.hexdigest()
 
 

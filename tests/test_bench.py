@@ -51,3 +51,12 @@ def test_traffic_is_reported_only_for_the_current_kernel_sources(tmp_path, monke
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.traffic_from_profile("w", "k") is None
     assert bench.traffic_from_profile("w", "k2") == 123456.0
+
+
+def test_source_hash_ignores_comments_and_blank_lines():
+    import bench
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    same = "/* header\n   text */\nint f(int x) {\n\n  return x + 1;\n}  // end\n"
+    other = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench._code_text(code) == bench._code_text(same)
+    assert bench._code_text(code) != bench._code_text(other)
