@@ -481,7 +481,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}). Tokens are independent, "
               f"so N GPUs would each run the same kernel on T/N tokens with no communication.",
               file=sys.stderr)

@@ -58,7 +58,7 @@ typedef struct kq_plan kq_plan;
 typedef enum kq_status KQ_ENUM_INT {
   KQ_OK = 0,
   KQ_ERR_INVALID_ARG = 1,   /* bad size, NULL pointer, NaN alpha, ...          */
-  KQ_ERR_UNSUPPORTED = 2,   /* valid, but this build has no kernel for it     */
+  KQ_ERR_UNSUPPORTED = 2,   /* valid, but the library has no kernel for it    */
   KQ_ERR_ALIGNMENT = 3,     /* a pointer or leading dimension is misaligned   */
   KQ_ERR_OUT_OF_MEMORY = 4, /* host or device allocation failed (kq_create)   */
   KQ_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed      */
