@@ -310,24 +310,45 @@ __device__ __forceinline__ void quant_tile(const f32x4 (&yacc)[NT][MT], float in
 }
 
 // N2R: the real row length when the tile is laid out for N2 = 128 and rows hold only
-// N2R = 112 values (lane group 3 then holds 16 real and 16 padding columns; rows of codes
-// are 56 bytes, so the stores are split to 8-byte aligned halves)
+// N2R = 112 values (lane group 3 then holds 16 real and 16 padding columns). Rows of codes
+// are then 56 bytes, and the 16 rows of block nt are 896 contiguous bytes: 56 words of 16
+// bytes, seven whole 128-byte lines. Lane k < 56 gathers word k across the wave and writes
+// it, so one store instruction writes each line whole. Dword d of word k is byte b = 16k + 4d
+// of the block, i.e. byte cb = b % 56 of row r = b / 56, held by lane r + 16 (cb / 16) as
+// its dword (cb % 16) / 4 = (d + 2r) % 4. A lane of an odd row swaps its two 8-byte halves
+// first, so that each lane's dword d is the one its reader asks for in slot d.
+// The whole wave must be active (cross-lane reads).
 template <int N1, int N2, int N2R = N2>
 __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t tok, const uint32_t (*w)[N2 / 32],
                                             int lr, int g) {
   static_assert(N2R == N2 || (N2 == 128 && N2R == 112), "padded stream rows: 112 of 128");
   uint8_t *crow = codes + tok * (int64_t)(N1 * N2R / 2);
+  if constexpr (N2R != N2) {
+    constexpr int kBlk = 16 * N2R / 2;  // bytes of codes per 16-row block
+    const int lane = lr + 16 * g;
+    const bool odd = (lr & 1) != 0;
+    int src[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int b = 16 * lane + 4 * d, r = b / (N2R / 2), cb = b - r * (N2R / 2);
+      src[d] = 4 * (lane < kBlk / 16 ? r + 16 * (cb >> 4) : lane);
+    }
+#pragma unroll
+    for (int nt = 0; nt < N1 / 16; ++nt) {
+      const uint32_t s[4] = {odd ? w[nt][2] : w[nt][0], odd ? w[nt][3] : w[nt][1],
+                             odd ? w[nt][0] : w[nt][2], odd ? w[nt][1] : w[nt][3]};
+      u32x4_t v;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) v[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[d], (int)s[d]);
+      if (lane < kBlk / 16)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(crow + nt * kBlk + 16 * lane));
+    }
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < N1 / 16; ++nt) {
     uint8_t *dst = crow + (nt * 16 + lr) * (N2R / 2) + g * (N2 / 8);
-    if constexpr (N2R != N2) {
-      const u32x2_t v0 = {w[nt][0], w[nt][1]};
-      __builtin_nontemporal_store(v0, reinterpret_cast<u32x2_t *>(dst));
-      if (g < 3) {
-        const u32x2_t v1 = {w[nt][2], w[nt][3]};
-        __builtin_nontemporal_store(v1, reinterpret_cast<u32x2_t *>(dst + 8));
-      }
-    } else if constexpr (N2 == 128) {
+    if constexpr (N2 == 128) {
       const u32x4_t v = {w[nt][0], w[nt][1], w[nt][2], w[nt][3]};
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst));
     } else {
