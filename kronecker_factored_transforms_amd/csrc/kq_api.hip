@@ -350,8 +350,14 @@ static kq_status create_ex_impl(kq_plan **out, int n1, int n2, kq_dtype x_dtype,
       if (fv->f16_ops) p->p1_exp = to_scaled_f16(e1);
       p->p2_exp = to_scaled_f16(e2);
       float cm = 0.f;
-      for (int i = 0; i < n; ++i) cm = fmaxf(cm, fabsf(hc[i]));
+      int f16ok = 1;
+      for (size_t i = 0; i < hc.size(); ++i) {
+        const float a = fabsf(hc[i]);
+        cm = fmaxf(cm, a);
+        if (a != 0.f && !(a >= 0x1p-14f && a < 0x1p15f)) f16ok = 0;
+      }
       p->c_absmax = cm;
+      p->c_f16 = c ? f16ok : 0;
     }
     kq_fused_arrange_p1(e1.data(), n1, a1.data());
     kq_fused_arrange_p2(e2.data(), n2, fv->p2_block, a2.data());

@@ -1780,13 +1780,15 @@ struct ColsCCfg {
   static constexpr int P1_BYTES = KK * MT * 1024;
   // two workgroups per CU when both fit in LDS
   static constexpr bool TWO = VBUF + P1_BYTES + 1024 <= 80 * 1024;
+  // a thread's c values fit its registers next to the rest for tiles of up to 112 rows
+  static constexpr bool CREG_OK = MT <= 7;
 };
 
 // workgroups per CU the launch bounds ask for
 template <int N1, int N2>
 constexpr int colsc_blocks = ColsCCfg<N1, N2>::TWO ? 2 : 1;
 
-template <int N1, int N2, bool YDBG = false, int BITS = 4>
+template <int N1, int N2, bool YDBG = false, int BITS = 4, bool CREG = false>
 __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2>)) void kq_colsc_kernel(
     const __bf16 *__restrict__ X, int64_t T, int64_t ldx,
     const f16x8 *__restrict__ p2op, const f16x8 *__restrict__ p1op,
@@ -1837,26 +1839,39 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
     }
   }
 
-  // per-thread chunk coordinates (fixed for the whole kernel)
-  int c_ts[C::CPT], c_row[C::CPT], c_cc[C::CPT];
-  bool c_ok[C::CPT];
-#pragma unroll
-  for (int i = 0; i < C::CPT; ++i) {
-    const int q0 = tid + C::THREADS * i;
-    c_ok[i] = C::EVEN || q0 < C::TPI * C::TOK_CHUNKS;
-    const int q = c_ok[i] ? q0 : 0;
-    c_ts[i] = q / C::TOK_CHUNKS;
-    const int qq = q % C::TOK_CHUNKS;
-    c_row[i] = qq / C::CH;
-    c_cc[i] = qq % C::CH;
-  }
+  // per-thread chunk coordinates (fixed for the whole kernel), as expressions of tid: chunk
+  // i of the thread is chunk q = tid + THREADS i of the group, i.e. chunk qq = q % TOK_CHUNKS
+  // of token slot q / TOK_CHUNKS, whose 8 values start at element 8 qq of the token (rows of
+  // X hold CH chunks)
+  auto c_okf = [&](int i) { return C::EVEN || (unsigned)tid + C::THREADS * i < (unsigned)(C::TPI * C::TOK_CHUNKS); };
+  auto c_q = [&](int i) { return c_okf(i) ? (unsigned)tid + C::THREADS * i : 0u; };
+  auto c_tsf = [&](int i) { return C::TPI == 1 ? 0 : (int)(c_q(i) / C::TOK_CHUNKS); };
+  auto c_qq = [&](int i) { return C::TPI == 1 ? c_q(i) : c_q(i) % C::TOK_CHUNKS; };
+  auto c_rowf = [&](int i) { return (int)(c_qq(i) / C::CH); };
+  auto c_ccf = [&](int i) { return (int)(c_qq(i) % C::CH); };
   uint4 pre[C::CPT];
+  // The channels a thread converts are the same for every token. Where registers allow
+  // (tiles of up to 112 rows) and the plan found every nonzero |c| in fp16's normal range
+  // [2^-14, 2^15) (CREG), the thread's c values stay in registers rounded to fp16, and
+  // x^ = fp16(fp32(x fp16(c)) 2^sx), where x fp16(c) is exact in fp32 (8 + 11 significant
+  // bits). Otherwise c is re-read from L2 (fp32) for every tile and x^ = fp16(fp32(x c) 2^sx).
+  constexpr bool USE_CREG = CREG && C::CREG_OK;
+  f16x8 creg[USE_CREG ? C::CPT : 1];
+  if constexpr (USE_CREG) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const float4 *cp = reinterpret_cast<const float4 *>(cvec + 8 * c_qq(i));
+      const float4 a = cp[0], b = cp[1];
+      creg[i] = f16x8{(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
+                      (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
+    }
+  }
   auto issue_loads = [&](int64_t grp) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int64_t t = grp * C::TPI + c_ts[i];
-      if (c_ok[i] && t < T)
-        pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + c_row[i] * N2 + c_cc[i] * 8);
+      const int64_t t = grp * C::TPI + c_tsf(i);
+      if (c_okf(i) && t < T)
+        pre[i] = *reinterpret_cast<const uint4 *>(X + t * ldx + 8 * c_qq(i));
       else
         pre[i] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -1871,7 +1886,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
       const uint32_t a = absmax_bf16(pre[i], 0);
 #pragma unroll
       for (int sl = 0; sl < C::TPI; ++sl)
-        if (c_ts[i] == sl) m[sl] = a > m[sl] ? a : m[sl];
+        if (c_tsf(i) == sl) m[sl] = a > m[sl] ? a : m[sl];
     }
 #pragma unroll
     for (int sl = 0; sl < C::TPI; ++sl) {
@@ -1895,14 +1910,21 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
     auto store = [&](auto scale) {
 #pragma unroll
       for (int i = 0; i < C::CPT; ++i) {
-        if (!c_ok[i]) continue;
+        if (!c_okf(i)) continue;
         int s = sx[0];
 #pragma unroll
-        for (int sl = 1; sl < C::TPI; ++sl) s = c_ts[i] == sl ? sx[sl] : s;
-        const float4 *cp = reinterpret_cast<const float4 *>(cvec + c_row[i] * N2 + c_cc[i] * 8);
-        const float4 a = cp[0], b = cp[1];
-        const float cl[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        *reinterpret_cast<f16x8 *>(s_v + c_ts[i] * C::V_BYTES + vchunk_off<C::CHP>(c_row[i], c_cc[i])) =
+        for (int sl = 1; sl < C::TPI; ++sl) s = c_tsf(i) == sl ? sx[sl] : s;
+        float cl[8];
+        if constexpr (USE_CREG) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cl[e] = (float)creg[i][e];
+        } else {
+          const float4 *cp = reinterpret_cast<const float4 *>(cvec + 8 * c_qq(i));
+          const float4 a = cp[0], b = cp[1];
+          cl[0] = a.x; cl[1] = a.y; cl[2] = a.z; cl[3] = a.w;
+          cl[4] = b.x; cl[5] = b.y; cl[6] = b.z; cl[7] = b.w;
+        }
+        *reinterpret_cast<f16x8 *>(s_v + c_tsf(i) * C::V_BYTES + vchunk_off<C::CHP>(c_rowf(i), c_ccf(i))) =
             scale_round_f16<decltype(scale)::value>(pre[i], cl, s);
       }
     };
@@ -1978,6 +2000,16 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
     for (int w = 0; w < C::W; ++w) zmax = fmaxf(zmax, s_zmax[it & 1][ts * C::W + w]);
     const int zs = __builtin_amdgcn_readfirstlane(f16_scale_exp(zmax));
     const int ty = f_exp - sx_tok - zs;  // Y = Y' 2^(f1 + f2 - sx - sz), exact
+    // Z' as stage 2's fp16 operands (packed before the next tile's conversion, so that the
+    // stage-1 accumulators are dead while it runs)
+    f16x8 za[C::KK][2];
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const bool pad = C::KHALF && kk == C::KK - 1;
+      za[kk][0] = pack8_f16(zacc[2 * kk][0], pad ? zero : zacc[(2 * kk + 1) % C::MT][0], zs);
+      za[kk][1] = pack8_f16(zacc[2 * kk][1], pad ? zero : zacc[(2 * kk + 1) % C::MT][1], zs);
+    }
     // the next group's tile replaces this one
     if (nxt < ngroups) {
       x_scales(it & 1, sx);
@@ -1992,14 +2024,6 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
     }
 
     // ---- stage 2: Y'^T[block, :] = Z'[:, block]^T P1' on fp16 operands ----
-    f16x8 za[C::KK][2];
-#pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const bool pad = C::KHALF && kk == C::KK - 1;
-      za[kk][0] = pack8_f16(zacc[2 * kk][0], pad ? zero : zacc[(2 * kk + 1) % C::MT][0], zs);
-      za[kk][1] = pack8_f16(zacc[2 * kk][1], pad ? zero : zacc[(2 * kk + 1) % C::MT][1], zs);
-    }
     f32x4 yacc[2][C::MT];
 #pragma unroll
     for (int nt = 0; nt < C::MT; ++nt) yacc[0][nt] = yacc[1][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -2166,6 +2190,10 @@ hipError_t launch_colsc(const kq_plan *p, const void *X, int64_t T, int64_t ldx,
   const int64_t ngroups = (T + C::TPI - 1) / C::TPI;
   const int grid = (int)(ngroups < (int64_t)p->grid_cap ? ngroups : (int64_t)p->grid_cap);
   auto k = y_debug ? &kq_colsc_kernel<N1, N2, true, BITS> : &kq_colsc_kernel<N1, N2, false, BITS>;
+  if constexpr (C::CREG_OK) {
+    if (p->c_f16)
+      k = y_debug ? &kq_colsc_kernel<N1, N2, true, BITS, true> : &kq_colsc_kernel<N1, N2, false, BITS, true>;
+  }
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::THREADS), 0, stream, static_cast<const __bf16 *>(X), T,
                      ldx, static_cast<const f16x8 *>(p->p2op), static_cast<const f16x8 *>(p->p1op),
                      p->c, p->p1_exp + p->p2_exp, p->c_absmax, p->clip,

@@ -55,6 +55,8 @@ struct kq_plan {
   int p1_exp;           // fp16 operands (variants with f16_ops): P1 * 2^-p1_exp and
   int p2_exp;           // P2 * 2^-p2_exp
   float c_absmax;       // max |c| (the bound of a token's x c, with max |x|)
+  int c_f16;            // 1: every nonzero |c| lies in [2^-14, 2^15), so fp16(c) is a normal
+                        // fp16 value (the column kernel with c may hold c in registers as fp16)
   // device workspace of the two-kernel designs for large factors: region A holds
   // ws_a_per_token bytes per token, region B (at a 256-byte aligned offset after A) holds
   // ws_b_per_token bytes per token; both 0 for the single-kernel designs

@@ -424,3 +424,32 @@ def test_codes_do_not_depend_on_the_batch_size(gpu, name):
     b = K.run(plan, X, y_debug=True)
     assert torch.equal(a[0], b[0][:small]) and torch.equal(a[1], b[1][: a[1].shape[0]])
     assert torch.equal(a[2], b[2][:small])
+
+
+# The column kernel with c holds each thread's c values in registers as fp16 when every
+# nonzero |c| lies in fp16's normal range [2^-14, 2^15), and re-reads c (fp32) from L2
+# otherwise. Channel scales far below or above that range (all of c times 2^-20, or times
+# 2^17) must take the second path: as fp16 they would be subnormal (a few significant bits)
+# or infinite. Both paths match the oracle; a c that straddles the edge (one channel at
+# 2^15) does too.
+@pytest.mark.parametrize("name,T,kernel", [
+    ("down_proj_n14336", 301, "fused_mfma_bf16_cols_112x128_c"),
+    ("ffn_n11008", 203, "fused_mfma_bf16_cols_86x128_c")])
+@pytest.mark.parametrize("cscale", ["in_range", "tiny", "huge", "edge"])
+def test_column_kernel_channel_scales_outside_fp16(gpu, name, T, kernel, cscale):
+    import torch
+    inp = S.make(name, T=T)
+    c = inp.c.astype(np.float64)
+    if cscale == "tiny":
+        c = c * 2.0 ** -20
+    elif cscale == "huge":
+        c = c * 2.0 ** 17
+    elif cscale == "edge":
+        c = c.copy()
+        c[5] = 2.0 ** 15
+    inp.c = c.astype(np.float32)
+    plan, X = K.make_plan(inp)
+    assert plan.kernel_for(T) == kernel, plan.kernel_for(T)
+    codes, scales, y = K.run(plan, X)
+    rel = K.check_plan_against_oracle(inp, plan, codes, scales, y)
+    assert rel < 1e-3, rel

@@ -42,12 +42,15 @@ def _f16_scale(bound):
     return 2.0 ** s
 
 
-def _emulate_f16(inp):
-    """The stream and column kernels with a per-channel scale: fp16 operands."""
+def _emulate_f16(inp, c_f16=False):
+    """The stream and column kernels with a per-channel scale: fp16 operands. With c_f16,
+    c itself is rounded to fp16 first (the column kernel holding c in registers), so that
+    x fp16(c) is exact and x_hat has one rounding to fp16."""
     wl = inp.wl
     X = O.bf16_bits_to_f64(inp.X)
     T = X.shape[0]
-    xh = (X.astype(np.float32) * inp.c.astype(np.float32)).astype(np.float32).astype(np.float64)
+    c = _fp16(inp.c) if c_f16 else inp.c.astype(np.float64)
+    xh = (X.astype(np.float32) * c.astype(np.float32)).astype(np.float32).astype(np.float64)
     bound = (np.abs(X).max(axis=1).astype(np.float32) * np.float32(np.abs(inp.c).max())).astype(np.float64)
     sx = _f16_scale(bound)[:, None]
     A = _fp16(xh * sx) / sx
@@ -113,6 +116,17 @@ def test_per_channel_scale_designs(name):
     assert split < 0.9 * GATE and f16 < 0.25 * GATE and GATE < single, (split, f16, single)
 
 
+@pytest.mark.parametrize("name", ["down_proj_n14336", "ffn_n11008"])
+def test_column_kernel_fp16_channel_scales(name):
+    """The column kernel with c in registers rounds c to fp16 (11 significant bits): x_hat
+    then carries two roundings of that size instead of one, still far inside the gate."""
+    inp = S.make(name, T=64)
+    Y = O.transform(inp.X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
+    exact_c = _rel(_emulate_f16(inp), Y)
+    f16_c = _rel(_emulate_f16(inp, c_f16=True), Y)
+    assert exact_c < f16_c < 0.25 * GATE, (exact_c, f16_c)
+
+
 @pytest.mark.parametrize("n1,n2", [(16, 64), (64, 64), (112, 128)])
 def test_fp16_operands_keep_every_token_inside_the_gate(n1, n2):
     """Tokens dominated by a few outlier channels: their own relative error is a sample of
@@ -122,9 +136,10 @@ def test_fp16_operands_keep_every_token_inside_the_gate(n1, n2):
     wl = replace(S.WORKLOADS["attn_n4096"], n1=n1, n2=n2, n_outliers=4, pivot_channels=0)
     inp = S.make(wl, T=256)
     Y = O.transform(inp.X, inp.P1, inp.P2, inp.c, inp.wl.dtype)
-    E = _emulate_f16(inp)
-    per = np.linalg.norm(E - Y, axis=1) / np.linalg.norm(Y, axis=1)
-    assert per.max() < 0.5 * GATE, per.max()
+    for c_f16 in (False, True):
+        E = _emulate_f16(inp, c_f16=c_f16)
+        per = np.linalg.norm(E - Y, axis=1) / np.linalg.norm(Y, axis=1)
+        assert per.max() < 0.5 * GATE, (c_f16, per.max())
 
 
 @pytest.mark.parametrize("name", ["attn_n4096", "down_proj_n14336"])
