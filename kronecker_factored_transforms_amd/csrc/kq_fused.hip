@@ -1750,7 +1750,8 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
 // has read the tile and published its |Z'| maximum and the next token's |x| maximum (its
 // chunks were loaded into registers a whole token earlier), the next token's tile is
 // stored over this one; (B) after stage 2, when the next tile is complete and every wave
-// has published its |Y| maximum. c is re-read from L2 for every tile. A token's codes are
+// has published its |Y| maximum. c stays in registers as fp16 where the plan allows it, else
+// it is re-read from L2 for every tile. A token's codes are
 // staged in LDS and written after the next barrier A.
 template <int N1, int N2>
 struct ColsCCfg {
