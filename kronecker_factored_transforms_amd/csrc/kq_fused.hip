@@ -289,7 +289,10 @@ struct StreamCfg {
   static constexpr int TILE = N1 * N2 * 2;      // bytes of one token
   static constexpr int P2_BYTES = N2 * N2 * 2;
   static constexpr int C_BYTES = HAS_C ? N1 * N2 * 4 : 0;  // c (fp32), swizzled rows
-  static_assert(P2_BYTES + C_BYTES + WAVES * TILE <= 160 * 1024, "LDS budget");
+  // with c, P1's operands live in LDS too (one copy per CU instead of one per wave: with
+  // one token per wave, the per-wave copies would cost as much L2 traffic as the tokens)
+  static constexpr int P1_BYTES = HAS_C ? KK * MT * 1024 : 0;
+  static_assert(P2_BYTES + C_BYTES + P1_BYTES + WAVES * TILE <= 160 * 1024, "LDS budget");
   static constexpr int RB = N2 * 2;             // bytes per row of V
   static constexpr int PPR = RB / 16;           // 16-byte pieces per row
   static constexpr int RPB = 256 / RB;          // rows per 256-byte bank row
@@ -355,8 +358,9 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
   // P2 operands, then (with c) c as 16-byte units of 4 channels: unit u of row R at
   // R * 4 N2 + ((u ^ (R % 16)) * 16), so that the 16 rows of one A-operand read hit 16
   // different bank groups
-  __shared__ __align__(16) unsigned char s_p2[C::P2_BYTES + C::C_BYTES];
+  __shared__ __align__(16) unsigned char s_p2[C::P2_BYTES + C::C_BYTES + C::P1_BYTES];
   unsigned char *const s_c = s_p2 + C::P2_BYTES;
+  unsigned char *const s_p1 = s_c + C::C_BYTES;
   __shared__ __align__(16) unsigned char s_tile[C::WAVES][C::TILE];
 
   const int tid = threadIdx.x;
@@ -395,11 +399,15 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
 
   const int64_t stride = (int64_t)gridDim.x * C::WAVES;
   int64_t tok = (int64_t)blockIdx.x * C::WAVES + wave;
-  bf16x8 p1r[C::KK][C::MT];  // stage-2 B operands, resident
+  bf16x8 p1r[HAS_C ? 1 : C::KK][HAS_C ? 1 : C::MT];  // stage-2 B operands, resident (no c)
+  if constexpr (!HAS_C) {
 #pragma unroll
-  for (int kk = 0; kk < C::KK; ++kk)
+    for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
-    for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
+      for (int nt = 0; nt < C::MT; ++nt) p1r[kk][nt] = p1op[(kk * C::MT + nt) * 64 + lane];
+  } else {
+    dma_copy(p1op, s_p1, C::P1_BYTES, wave, C::WAVES, lane);
+  }
   // P2's operands (and c) reach LDS by DMA, each wave copying its share, before any token
   dma_copy(p2op, s_p2, C::P2_BYTES, wave, C::WAVES, lane);
   if constexpr (HAS_C) {
@@ -517,7 +525,7 @@ __global__ __launch_bounds__(512) void kq_stream_kernel(
           za[m2] = pack8_f16(zacc[2 * kk][m2], pad ? zero : zacc[(2 * kk + 1) % C::MT][m2], zs);
 #pragma unroll
         for (int nt = 0; nt < C::MT; ++nt) {
-          const f16x8 b = __builtin_bit_cast(f16x8, p1r[kk][nt]);
+          const f16x8 b = reinterpret_cast<const f16x8 *>(s_p1)[(kk * C::MT + nt) * 64 + lane];
 #pragma unroll
           for (int m2 = 0; m2 < C::NT; ++m2) yacc[m2][nt] = mfma_f16(za[m2], b, yacc[m2][nt]);
         }
@@ -1958,6 +1966,13 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
   // the staged codes of group `gq` to global memory: its tokens are consecutive, so the
   // staged bytes (slot-major) are one contiguous run of codes; 16-byte words, consecutive
   // threads on consecutive words, the tokens at or beyond T left out
+  // Staged INT4 rows of 128 codes (64 bytes, 4 words): the 16 rows a code store covers
+  // would put 4 lanes on every bank, so word w of row R sits at w ^ ((R / 4) % 4) within
+  // its row (then the 64 lanes' 4-byte pieces hit 64 different banks); code_unit maps a
+  // word's place in the token's codes to its place in the staging buffer (an involution)
+  constexpr bool SWZ_CODE = STAGE && BITS == 4 && N2 == 128;
+  static_assert(!SWZ_CODE || C::TPI == 1 || (TOK_CODE / 16) % 16 == 0, "word swizzle per token");
+  auto code_unit = [](int u) { return SWZ_CODE ? u ^ ((u >> 4) & 3) : u; };
   auto store_staged = [&](int64_t gq) {
     constexpr int WPT = TOK_CODE / 16;  // 16-byte words per token
     const int64_t t0 = gq * C::TPI;
@@ -1966,7 +1981,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
 #pragma unroll
     for (int u = tid; u < C::TPI * WPT; u += C::THREADS) {
       if (u < lim)
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(s_code + u * 16),
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(s_code + code_unit(u) * 16),
                                     reinterpret_cast<u32x4_t *>(dst + u * 16));
     }
   };
@@ -2077,7 +2092,9 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, (colsc_blocks<N1, N2
       // lane holds Y[j = nt*16 + lr][wt*32 + 8g + 4h + r]
       constexpr int RB = N2 * BITS / 8;
       uint8_t *crow = STAGE ? s_code + ts * TOK_CODE : codes + tok * (int64_t)TOK_CODE;
-      const uint32_t loff = (uint32_t)(lr * RB + (wt * 32 + g * 8) * BITS / 8);
+      // (rows 16 nt + lr share lr % 16, so one swizzle serves all of the lane's rows)
+      const uint32_t loff = (uint32_t)(lr * RB + (SWZ_CODE ? ((wt ^ ((lr >> 2) & 3)) * 16 + g * 4)
+                                                           : (wt * 32 + g * 8) * BITS / 8));
       // one scalar branch on the clamp for the whole tile
       auto emit = [&](auto clamp_tag) {
 #pragma unroll
