@@ -70,7 +70,9 @@ typedef enum kq_dtype KQ_ENUM_INT { KQ_BF16 = 0, KQ_FP32 = 1, KQ_FP16 = 2 } kq_d
 
 /* Flags for kq_create_ex. At most one KQ_FLAG_SPLIT_* may be given, only for bf16 plans
  * (KQ_ERR_UNSUPPORTED when that split is not built for the shape). All variants compute
- * the same Y up to fp32 accumulation order and quantize it the same way. */
+ * Y within the plan dtype's tolerance of the exact transform (their operand roundings
+ * differ where a per-channel scale is given, and their fp32 accumulation order always) and
+ * quantize the Y they computed the same way. */
 #define KQ_FLAG_FORCE_GENERIC 0x1u  /* fp32 FMA kernel even where an MFMA one applies   */
 #define KQ_FLAG_SPLIT_REG1 0x10u    /* MFMA: one wave per token, token in registers     */
 #define KQ_FLAG_SPLIT_REG2 0x20u    /* MFMA: two waves per token, token in registers    */
