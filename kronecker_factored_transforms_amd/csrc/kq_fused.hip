@@ -1429,11 +1429,18 @@ struct ColsCfg {
   static constexpr int CHK = CH / KH;               // chunks per row of one column part
   static constexpr int CHL = CHP / KH;              // the same in LDS (with padded columns)
   static constexpr int KSH = KS / KH;               // stage-1 steps per column part
-  // row layout in LDS: an XOR swizzle of the chunks when CHL is a power of two, else rows
-  // padded by one chunk; either way the 16 rows of one A-operand read hit 16 different
-  // bank groups
+  // row layout in LDS: an XOR swizzle of the chunks when CHL is a power of two; for rows
+  // of 20, 24 or 28 chunks an XOR of (R / 2) % 4 within each aligned group of 4 chunks
+  // (rows padded by one chunk read at half speed on MI355X: measured with an LDS access
+  // probe, 8 cycles per 16-byte wave read against 4); else rows padded by one chunk
   static constexpr bool POW2 = (CHL & (CHL - 1)) == 0;
-  static constexpr int ROW_CHUNKS = POW2 ? CHL : CHL + 1;
+  static constexpr bool SWZ4 = !POW2 && CHL % 4 == 0 && CHL >= 20;
+  static constexpr int ROW_CHUNKS = POW2 || SWZ4 ? CHL : CHL + 1;
+  // byte offset of chunk cc of row r in one plane of the tile
+  __device__ static constexpr int voff(int r, int cc) {
+    return POW2 ? (r * CHL + (cc ^ (r & (CHL - 1)))) * 16
+                : SWZ4 ? (r * CHL + (cc ^ ((r >> 1) & 3))) * 16 : (r * (CHL + 1) + cc) * 16;
+  }
   static constexpr int TOK_CHUNKS = N1 * CHK;       // chunks of one column part of a token
   static constexpr int CPT = (TPI * TOK_CHUNKS + THREADS - 1) / THREADS;  // chunks per thread
   static constexpr bool EVEN = CPT * THREADS == TPI * TOK_CHUNKS;        // no idle slots
@@ -1493,7 +1500,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
     constexpr int PC = C::CHP - C::CH, PER_PLANE = N1 * PC;
     for (int q = tid; q < C::TPI * C::VPLANES * PER_PLANE; q += C::THREADS) {
       const int pl = q / PER_PLANE, r = (q % PER_PLANE) / PC, cc = C::CH + q % PC;
-      *reinterpret_cast<uint4 *>(s_v + pl * C::V_BYTES + vchunk_off<C::CHL>(r, cc)) =
+      *reinterpret_cast<uint4 *>(s_v + pl * C::V_BYTES + C::voff(r, cc)) =
           make_uint4(0u, 0u, 0u, 0u);
     }
   }
@@ -1544,7 +1551,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       if (!c_ok[i]) continue;
-      const int off = c_ts[i] * C::V_BYTES + vchunk_off<C::CHL>(c_row[i], c_cc[i]);
+      const int off = c_ts[i] * C::V_BYTES + C::voff(c_row[i], c_cc[i]);
       if constexpr (HAS_C) {
         uint4 hi, lo;
         if constexpr (C::TWO) {
@@ -1567,15 +1574,17 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
   // Large n2: P2 does not fit in LDS next to the tile and P1, but one wave only ever uses
   // its own 32-column block of P2 (n2 x 32 values, KS x 2 operands), which it keeps in
   // registers for the whole kernel. The workgroup loads the next token's tile by DMA into
-  // the other LDS buffer: LDS slot q of the tile (row q / ROW_CHUNKS, chunk q % ROW_CHUNKS;
-  // the padding chunk re-reads chunk 0) is written by lane q % 64 of instruction q / 64.
+  // the other LDS buffer: LDS slot q of the tile (row q / ROW_CHUNKS, position q %
+  // ROW_CHUNKS, which holds the chunk that voff puts there; a padding chunk re-reads chunk
+  // 0) is written by lane q % 64 of instruction q / 64.
   // No other global load sits inside the token loop, so one wait before the end-of-token
   // barrier covers the DMA.
   auto dma_tile = [&](int64_t t, int b) {
     const __bf16 *base = X + t * ldx;
     for (int j = wave; j < C::DMA_INSTR; j += C::WAVES) {
       const int q = j * 64 + lane;
-      const int r = q / C::ROW_CHUNKS, cc = q % C::ROW_CHUNKS;
+      const int r = q / C::ROW_CHUNKS;
+      const int cc = C::SWZ4 ? (q % C::ROW_CHUNKS) ^ ((r >> 1) & 3) : q % C::ROW_CHUNKS;
       const uint32_t voff = (uint32_t)((r * N2 + (cc < C::CH ? cc : 0) * 8) * 2);
       dma16<true>(base, voff, __builtin_amdgcn_readfirstlane(lds_addr(s_v + b * C::VBUF + j * 1024)));
     }
@@ -1643,7 +1652,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
         }
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) {
-          const int off = vchunk_off<C::CHL>(mt * 16 + lr, (ks - h * C::KSH) * 4 + g);
+          const int off = C::voff(mt * 16 + lr, (ks - h * C::KSH) * 4 + g);
           const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vt + off);
           zacc[mt][0] = mfma(a, b0, zacc[mt][0]);
           zacc[mt][1] = mfma(a, b1, zacc[mt][1]);
