@@ -1429,18 +1429,13 @@ struct ColsCfg {
   static constexpr int CHK = CH / KH;               // chunks per row of one column part
   static constexpr int CHL = CHP / KH;              // the same in LDS (with padded columns)
   static constexpr int KSH = KS / KH;               // stage-1 steps per column part
-  // row layout in LDS: an XOR swizzle of the chunks when CHL is a power of two; for rows
-  // of 20, 24 or 28 chunks an XOR of (R / 2) % 4 within each aligned group of 4 chunks
-  // (rows padded by one chunk read at half speed on MI355X: measured with an LDS access
-  // probe, 8 cycles per 16-byte wave read against 4); else rows padded by one chunk
+  // row layout in LDS: vchunk_off's (an XOR swizzle for power-of-two rows, an XOR inside
+  // 4-chunk groups for rows of 20, 24 or 28 chunks, else rows padded by one chunk)
   static constexpr bool POW2 = (CHL & (CHL - 1)) == 0;
-  static constexpr bool SWZ4 = !POW2 && CHL % 4 == 0 && CHL >= 20;
-  static constexpr int ROW_CHUNKS = POW2 || SWZ4 ? CHL : CHL + 1;
+  static constexpr bool SWZ4 = vrow_swz4<CHL>();
+  static constexpr int ROW_CHUNKS = vrow_chunks<CHL>();
   // byte offset of chunk cc of row r in one plane of the tile
-  __device__ static constexpr int voff(int r, int cc) {
-    return POW2 ? (r * CHL + (cc ^ (r & (CHL - 1)))) * 16
-                : SWZ4 ? (r * CHL + (cc ^ ((r >> 1) & 3))) * 16 : (r * (CHL + 1) + cc) * 16;
-  }
+  __device__ static int voff(int r, int cc) { return vchunk_off<CHL>(r, cc); }
   static constexpr int TOK_CHUNKS = N1 * CHK;       // chunks of one column part of a token
   static constexpr int CPT = (TPI * TOK_CHUNKS + THREADS - 1) / THREADS;  // chunks per thread
   static constexpr bool EVEN = CPT * THREADS == TPI * TOK_CHUNKS;        // no idle slots
@@ -1789,7 +1784,7 @@ struct ColsCCfg {
   static constexpr int CH = N2 / 8;                 // 16-byte chunks per row of X
   static constexpr int CHP = N2P / 8;               // chunks per row in LDS
   static constexpr bool POW2 = (CHP & (CHP - 1)) == 0;
-  static constexpr int ROW_CHUNKS = POW2 ? CHP : CHP + 1;
+  static constexpr int ROW_CHUNKS = vrow_chunks<CHP>();
   static constexpr int TOK_CHUNKS = N1 * CH;
   static constexpr int CPT = (TPI * TOK_CHUNKS + THREADS - 1) / THREADS;
   static constexpr bool EVEN = CPT * THREADS == TPI * TOK_CHUNKS;

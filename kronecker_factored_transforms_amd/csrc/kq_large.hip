@@ -52,7 +52,7 @@ struct LargeCfg {
   static constexpr int KS = N2P / 32;               // stage-1 reduction steps
   static constexpr int CH = N2 / 8;                 // 16-byte chunks per row of X
   static constexpr int CHP = N2P / 8;               // chunks per row in LDS
-  static constexpr int ROW_CHUNKS = (CHP & (CHP - 1)) == 0 ? CHP : CHP + 1;
+  static constexpr int ROW_CHUNKS = vrow_chunks<CHP>();
   static constexpr int VPLANES = HILO ? 2 : 1;      // hi (+ lo) bf16 planes of x*c
   static constexpr int PLANE = 32 * ROW_CHUNKS * 16;  // bytes of a 32-row plane in LDS
   static constexpr int STAGE = PLANE * VPLANES;       // one 32-row staging buffer
@@ -65,8 +65,8 @@ struct LargeCfg {
 
 // One 32-row step (rows 32 kk .. 32 kk + 31 of token t) of X: each thread loads CPT chunks
 // of 16 bytes into registers, then stores them (split into hi / lo planes with c) into an
-// LDS staging buffer laid out like the column kernel's tile (XOR-swizzled rows, or rows
-// padded by one chunk). Rows at or beyond n1, and tokens at or beyond T, load zeros.
+// LDS staging buffer laid out like the column kernel's tile (vchunk_off: XOR-swizzled rows,
+// or rows padded by one chunk). Rows at or beyond n1, and tokens at or beyond T, load zeros.
 template <class C, int N1, int N2, bool HAS_C>
 struct StepLoader {
   int row[C::CPT], cc[C::CPT];
