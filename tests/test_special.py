@@ -453,3 +453,23 @@ def test_column_kernel_channel_scales_outside_fp16(gpu, name, T, kernel, cscale)
     codes, scales, y = K.run(plan, X)
     rel = K.check_plan_against_oracle(inp, plan, codes, scales, y)
     assert rel < 1e-3, rel
+
+
+# Tokens whose two halves of rows would need different fp16 scales of x^ (rows 32-63 times
+# 2^20, or rows 0-31 times 2^-30): the stream kernel with c scales by the whole token's
+# bound, and the timed and debug launches agree bit for bit and match the oracle.
+def test_stream_with_c_uneven_token_halves(gpu):
+    import torch
+    name, T = "attn_n4096", 1100
+    inp = S.make(name, T=T)
+    wl = inp.wl
+    x = O.bf16_bits_to_f64(inp.X).reshape(T, wl.n1, wl.n2)
+    x[0::3, 32:, :] *= 2.0 ** 20
+    x[1::3, :32, :] *= 2.0 ** -30
+    inp.X = S.to_bf16_bits(x.reshape(T, -1))
+    plan, X = K.make_plan(inp)
+    assert plan.kernel_for(T) == "fused_mfma_bf16_stream_64x64_c", plan.kernel_for(T)
+    codes, scales, y = K.run(plan, X)
+    K.check_plan_against_oracle(inp, plan, codes, scales, y)
+    c2, s2 = K.run(plan, X, y_debug=False)
+    assert torch.equal(c2, codes) and torch.equal(s2, scales)
