@@ -287,12 +287,15 @@ __device__ __forceinline__ uint32_t quant4x8(float y0, float y1, float y2, float
 
 
 // Row layout of a token tile in LDS with CH 16-byte chunks per row: an XOR swizzle of the
-// chunks when CH is a power of two; for rows of 20, 24 or 28 chunks, an XOR of (R / 2) % 4
-// within each aligned group of 4 chunks (rows padded by one chunk read at half speed on
-// MI355X: an LDS access probe measured 8 cycles per 16-byte wave read against 4); else rows
-// padded by one chunk.
+// chunks when CH is a power of two; for rows of 20, 24 or 28 chunks, an XOR of (R / 2) % 8
+// within each aligned group of 8 chunks (24) or of (R / 2) % 4 within each aligned group of
+// 4 chunks (20, 28) (rows padded by one chunk read at half speed on MI355X: an LDS access
+// probe measured 8 cycles per 16-byte wave read against 4, and (R / 2) % 4 on 24-chunk rows
+// also conflicts); else rows padded by one chunk.
 template <int CH>
 constexpr bool vrow_swz4() { return (CH & (CH - 1)) != 0 && CH % 4 == 0 && CH >= 20; }
+template <int CH>
+constexpr int vrow_xmask() { return CH % 8 == 0 ? 7 : 3; }
 template <int CH>
 constexpr int vrow_chunks() { return (CH & (CH - 1)) == 0 || vrow_swz4<CH>() ? CH : CH + 1; }
 
@@ -300,7 +303,7 @@ constexpr int vrow_chunks() { return (CH & (CH - 1)) == 0 || vrow_swz4<CH>() ? C
 template <int CH>
 __device__ __forceinline__ int vchunk_off(int r, int cc) {
   if constexpr ((CH & (CH - 1)) == 0) return (r * CH + (cc ^ (r & (CH - 1)))) * 16;
-  else if constexpr (vrow_swz4<CH>()) return (r * CH + (cc ^ ((r >> 1) & 3))) * 16;
+  else if constexpr (vrow_swz4<CH>()) return (r * CH + (cc ^ ((r >> 1) & vrow_xmask<CH>()))) * 16;
   else return (r * (CH + 1) + cc) * 16;
 }
 

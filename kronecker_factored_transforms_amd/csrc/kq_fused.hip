@@ -1430,7 +1430,7 @@ struct ColsCfg {
   static constexpr int CHL = CHP / KH;              // the same in LDS (with padded columns)
   static constexpr int KSH = KS / KH;               // stage-1 steps per column part
   // row layout in LDS: vchunk_off's (an XOR swizzle for power-of-two rows, an XOR inside
-  // 4-chunk groups for rows of 20, 24 or 28 chunks, else rows padded by one chunk)
+  // 8- or 4-chunk groups for rows of 24, or 20 and 28, chunks, else rows padded by one chunk)
   static constexpr bool POW2 = (CHL & (CHL - 1)) == 0;
   static constexpr bool SWZ4 = vrow_swz4<CHL>();
   static constexpr int ROW_CHUNKS = vrow_chunks<CHL>();
@@ -1579,7 +1579,7 @@ __global__ __launch_bounds__(cols_waves(cols_n2p(N2)) * 64, cols_min_blocks(N1, 
     for (int j = wave; j < C::DMA_INSTR; j += C::WAVES) {
       const int q = j * 64 + lane;
       const int r = q / C::ROW_CHUNKS;
-      const int cc = C::SWZ4 ? (q % C::ROW_CHUNKS) ^ ((r >> 1) & 3) : q % C::ROW_CHUNKS;
+      const int cc = C::SWZ4 ? (q % C::ROW_CHUNKS) ^ ((r >> 1) & vrow_xmask<C::CHL>()) : q % C::ROW_CHUNKS;
       const uint32_t voff = (uint32_t)((r * N2 + (cc < C::CH ? cc : 0) * 8) * 2);
       dma16<true>(base, voff, __builtin_amdgcn_readfirstlane(lds_addr(s_v + b * C::VBUF + j * 1024)));
     }
